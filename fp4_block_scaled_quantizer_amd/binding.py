@@ -1,0 +1,205 @@
+"""ctypes binding of ``libfp4q.so`` with the C ABI's entry-point names.
+
+Argument marshalling only: every step of the quantizers and GEMMs runs in the
+library's HIP kernels.  PyTorch supplies device memory (``data_ptr()``) and the
+stream (``torch.cuda.current_stream()``).  If the library has not been built
+this module raises -- there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfp4q.so")
+HEADER = os.path.join(os.path.dirname(_HERE), "include", "fp4q.h")
+
+# enums of include/fp4q.h
+OK, EINVAL, ESHAPE, EALIGN, ELAUNCH, EUNSUPPORTED = 0, 1, 2, 3, 4, 5
+ALONG_ROWS, ALONG_COLS = 0, 1
+RNE, SR = 0, 1
+NV_GLOBAL, NV_TILE128 = 0, 1
+LAYOUT_LINEAR = 0
+OUT_F32, OUT_BF16 = 0, 1
+
+_lib = None
+
+
+class Fp4qError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed with status {status}: {status_str(status)}")
+        self.status = status
+
+
+def declared_functions():
+    """Names of the functions include/fp4q.h declares."""
+    with open(HEADER) as f:
+        text = f.read()
+    return re.findall(r"^FP4Q_API\s+[\w\s\*]*?\b(\w+)\s*\(", text, flags=re.MULTILINE)
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise FileNotFoundError(
+            f"{LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'` "
+            "(hipcc, gfx950); libfp4q has no CPU fallback")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i64, u64, u32, i32, f32 = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint64, ctypes.c_uint32,
+                                   ctypes.c_int, ctypes.c_float)
+    L.fp4_quantize_mx.argtypes = [vp, i64, i64, i64, i32, i32, u64, u32, vp, vp, i32, vp]
+    L.fp4_hadamard32_quantize.argtypes = [vp, i64, i64, i64, i32, u32, i32, u64, u32, vp, vp, i32, vp]
+    L.fp4q_nv_workspace_bytes.argtypes = [i64, i64, i32, i32]
+    L.fp4q_nv_workspace_bytes.restype = ctypes.c_size_t
+    L.fp4_quantize_nv.argtypes = [vp, i64, i64, i64, i32, i32, u64, u32, i32, vp, vp, vp, vp, ctypes.c_size_t,
+                                  i32, vp]
+    L.fp4_gemm_mx.argtypes = [vp, vp, vp, vp, i64, i64, i64, f32, i32, vp, i32, i64, vp]
+    L.fp4_gemm_nv.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, i64, i64, f32, i32, vp, i32, i64, vp]
+    for fn in ("fp4_quantize_mx", "fp4_hadamard32_quantize", "fp4_quantize_nv", "fp4_gemm_mx", "fp4_gemm_nv"):
+        getattr(L, fn).restype = i32
+    L.fp4q_status_str.argtypes = [i32]
+    L.fp4q_status_str.restype = ctypes.c_char_p
+    L.fp4q_abi_version.argtypes = []
+    L.fp4q_abi_version.restype = i32
+    _lib = L
+    return L
+
+
+def status_str(status: int) -> str:
+    return lib().fp4q_status_str(status).decode()
+
+
+def abi_version() -> int:
+    return lib().fp4q_abi_version()
+
+
+def _check(fn: str, status: int):
+    if status != OK:
+        raise Fp4qError(fn, status)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> int:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _input(x: torch.Tensor, cols: Optional[int]):
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be a 2-D bf16 tensor with unit column stride")
+    rows = x.shape[0]
+    cols = x.shape[1] if cols is None else cols
+    ld = x.stride(0) if rows > 1 else x.shape[1]
+    return rows, cols, ld
+
+
+def _logical(rows: int, cols: int, axis: int):
+    return (rows, cols) if axis == ALONG_ROWS else (cols, rows)
+
+
+def fp4_quantize_mx(x: torch.Tensor, *, cols: Optional[int] = None, axis: int = ALONG_ROWS, round: int = RNE,
+                    seed: int = 0, stream_id: int = 0, codes: Optional[torch.Tensor] = None,
+                    scales: Optional[torch.Tensor] = None, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    rows, cols, ld = _input(x, cols)
+    R, K = _logical(rows, cols, axis)
+    if codes is None:
+        codes = torch.empty((R, K // 2), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((R, K // 32), dtype=torch.uint8, device=x.device)
+    _check("fp4_quantize_mx", lib().fp4_quantize_mx(x.data_ptr(), rows, cols, ld, axis, round, seed, stream_id,
+                                                    codes.data_ptr(), scales.data_ptr(), LAYOUT_LINEAR,
+                                                    _stream(stream)))
+    return codes, scales
+
+
+def fp4_hadamard32_quantize(x: torch.Tensor, sign_mask: int, *, cols: Optional[int] = None, axis: int = ALONG_COLS,
+                            round: int = RNE, seed: int = 0, stream_id: int = 0,
+                            codes: Optional[torch.Tensor] = None, scales: Optional[torch.Tensor] = None,
+                            stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    rows, cols, ld = _input(x, cols)
+    R, K = _logical(rows, cols, axis)
+    if codes is None:
+        codes = torch.empty((R, K // 2), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((R, K // 32), dtype=torch.uint8, device=x.device)
+    _check("fp4_hadamard32_quantize",
+           lib().fp4_hadamard32_quantize(x.data_ptr(), rows, cols, ld, axis, sign_mask & 0xFFFFFFFF, round, seed,
+                                         stream_id, codes.data_ptr(), scales.data_ptr(), LAYOUT_LINEAR,
+                                         _stream(stream)))
+    return codes, scales
+
+
+def fp4q_nv_workspace_bytes(rows: int, cols: int, axis: int, domain: int) -> int:
+    return lib().fp4q_nv_workspace_bytes(rows, cols, axis, domain)
+
+
+def nv_tensor_scale_shape(R: int, K: int, domain: int):
+    return (1,) if domain == NV_GLOBAL else ((R + 127) // 128, (K + 127) // 128)
+
+
+def fp4_quantize_nv(x: torch.Tensor, domain: int = NV_GLOBAL, *, cols: Optional[int] = None, axis: int = ALONG_ROWS,
+                    round: int = RNE, seed: int = 0, stream_id: int = 0, codes: Optional[torch.Tensor] = None,
+                    scales: Optional[torch.Tensor] = None, tensor_scale: Optional[torch.Tensor] = None,
+                    workspace: Optional[torch.Tensor] = None, stream=None):
+    rows, cols, ld = _input(x, cols)
+    R, K = _logical(rows, cols, axis)
+    if codes is None:
+        codes = torch.empty((R, K // 2), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((R, K // 16), dtype=torch.uint8, device=x.device)
+    if tensor_scale is None:
+        tensor_scale = torch.empty(nv_tensor_scale_shape(R, K, domain), dtype=torch.float32, device=x.device)
+    need = fp4q_nv_workspace_bytes(rows, cols, axis, domain)
+    if workspace is None and need > 0:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=x.device)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("fp4_quantize_nv",
+           lib().fp4_quantize_nv(x.data_ptr(), rows, cols, ld, axis, round, seed, stream_id, domain,
+                                 codes.data_ptr(), scales.data_ptr(), tensor_scale.data_ptr(), _ptr(workspace),
+                                 wbytes, LAYOUT_LINEAR, _stream(stream)))
+    return codes, scales, tensor_scale
+
+
+def _gemm_out(M: int, N: int, out_dtype, device, c: Optional[torch.Tensor]):
+    if c is None:
+        c = torch.empty((M, N), dtype=out_dtype, device=device)
+    if c.dtype not in (torch.float32, torch.bfloat16) or c.dim() != 2 or c.stride(1) != 1:
+        raise ValueError("c must be a 2-D fp32 or bf16 tensor with unit column stride")
+    ldc = c.stride(0) if M > 1 else N
+    return c, (OUT_F32 if c.dtype == torch.float32 else OUT_BF16), ldc
+
+
+def fp4_gemm_mx(a_codes: torch.Tensor, a_scales: torch.Tensor, b_codes: torch.Tensor, b_scales: torch.Tensor, *,
+                alpha: float = 1.0, out_dtype=torch.float32, c: Optional[torch.Tensor] = None,
+                stream=None) -> torch.Tensor:
+    M, N, K = a_codes.shape[0], b_codes.shape[0], a_codes.shape[1] * 2
+    if b_codes.shape[1] * 2 != K:
+        raise ValueError("A and B must have the same K")
+    c, ctype, ldc = _gemm_out(M, N, out_dtype, a_codes.device, c)
+    _check("fp4_gemm_mx", lib().fp4_gemm_mx(a_codes.data_ptr(), a_scales.data_ptr(), b_codes.data_ptr(),
+                                            b_scales.data_ptr(), M, N, K, float(alpha), LAYOUT_LINEAR,
+                                            c.data_ptr(), ctype, ldc, _stream(stream)))
+    return c
+
+
+def fp4_gemm_nv(a_codes: torch.Tensor, a_scales: torch.Tensor, a_tensor_scale: torch.Tensor, b_codes: torch.Tensor,
+                b_scales: torch.Tensor, b_tensor_scale: torch.Tensor, domain: int = NV_GLOBAL, *, alpha: float = 1.0,
+                out_dtype=torch.float32, c: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    M, N, K = a_codes.shape[0], b_codes.shape[0], a_codes.shape[1] * 2
+    if b_codes.shape[1] * 2 != K:
+        raise ValueError("A and B must have the same K")
+    c, ctype, ldc = _gemm_out(M, N, out_dtype, a_codes.device, c)
+    _check("fp4_gemm_nv", lib().fp4_gemm_nv(a_codes.data_ptr(), a_scales.data_ptr(), a_tensor_scale.data_ptr(),
+                                            b_codes.data_ptr(), b_scales.data_ptr(), b_tensor_scale.data_ptr(),
+                                            domain, M, N, K, float(alpha), LAYOUT_LINEAR, c.data_ptr(), ctype, ldc,
+                                            _stream(stream)))
+    return c

@@ -1,0 +1,261 @@
+// fp4q_api.hip -- the extern "C" entry points declared in include/fp4q.h:
+// argument checks (all before any HIP call, so they run without a GPU), then
+// one call into the kernel launchers.  The library allocates nothing.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/fp4q.h"
+#include "fp4q_internal.h"
+
+namespace {
+
+constexpr int64_t kMaxDim = INT32_MAX;
+
+struct Range {
+    uintptr_t lo, hi;  // [lo, hi)
+};
+
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+Range bytes(const void *p, uint64_t n) { return Range{(uintptr_t)p, (uintptr_t)p + (uintptr_t)n}; }
+
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+// bytes spanned by a row-major bf16 [rows x ld] input whose rows hold `cols` used elements
+uint64_t input_span(int64_t rows, int64_t cols, int64_t ld)
+{
+    return rows == 0 || cols == 0 ? 0 : ((uint64_t)(rows - 1) * (uint64_t)ld + (uint64_t)cols) * 2u;
+}
+
+hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
+
+fp4q_status launched(int rc) { return rc == 0 ? FP4Q_OK : FP4Q_ELAUNCH; }
+
+// Shared checks of the two MX producers.
+fp4q_status check_mx_producer(const void *x, int64_t rows, int64_t cols, int64_t ld_x, int axis, int round,
+                              const void *codes, const void *scales, int layout, bool *empty)
+{
+    if ((axis != FP4Q_ALONG_ROWS && axis != FP4Q_ALONG_COLS) || (round != FP4Q_RNE && round != FP4Q_SR) ||
+        layout != FP4Q_LAYOUT_LINEAR)
+        return FP4Q_EINVAL;
+    if (rows < 0 || cols < 0 || ld_x < cols || rows > kMaxDim || cols > kMaxDim || ld_x > kMaxDim)
+        return FP4Q_ESHAPE;
+    const int64_t R = axis == FP4Q_ALONG_ROWS ? rows : cols;
+    const int64_t K = axis == FP4Q_ALONG_ROWS ? cols : rows;
+    if (K % 32 != 0) return FP4Q_ESHAPE;
+    if (axis == FP4Q_ALONG_COLS && cols % 4 != 0) return FP4Q_ESHAPE;
+    if ((uint64_t)R * (uint64_t)(K / 8) >= (1ull << 32)) return FP4Q_ESHAPE;
+    *empty = (R == 0 || K == 0);
+    if (*empty) return FP4Q_OK;
+    if (!x || !codes || !scales) return FP4Q_EINVAL;
+    if (!aligned(x, 16) || !aligned(codes, 16) || ld_x % 8 != 0) return FP4Q_EALIGN;
+    const Range rx = bytes(x, input_span(rows, cols, ld_x));
+    const Range rc = bytes(codes, (uint64_t)R * (uint64_t)K / 2);
+    const Range rs = bytes(scales, (uint64_t)R * (uint64_t)K / 32);
+    if (overlap(rx, rc) || overlap(rx, rs) || overlap(rc, rs)) return FP4Q_EINVAL;
+    return FP4Q_OK;
+}
+
+fp4q_status run_mx_producer(const void *x, int64_t rows, int64_t cols, int64_t ld_x, int axis, bool hadamard,
+                            uint32_t sign_mask, int round, uint64_t seed, uint32_t stream_id, void *codes,
+                            void *scales, int layout, void *stream)
+{
+    bool empty = false;
+    const fp4q_status st = check_mx_producer(x, rows, cols, ld_x, axis, round, codes, scales, layout, &empty);
+    if (st != FP4Q_OK || empty) return st;
+    fp4q::QuantArgs a{};
+    a.x = x;
+    a.rows = rows;
+    a.cols = cols;
+    a.ld = ld_x;
+    a.axis = axis;
+    a.sr = round == FP4Q_SR;
+    a.hadamard = hadamard;
+    a.seed = seed;
+    a.stream_id = stream_id;
+    a.sign_mask = sign_mask;
+    a.codes = codes;
+    a.scales = scales;
+    (void)hipGetLastError();  // report only this call's launch status
+    return launched(fp4q::launch_quant_mx(a, as_stream(stream)));
+}
+
+fp4q_status check_gemm_common(const void *a_codes, const void *a_scales, const void *b_codes, const void *b_scales,
+                              int64_t M, int64_t N, int64_t K, int layout, const void *c, int c_type, int64_t ldc,
+                              int scale_div, bool *empty)
+{
+    if (layout != FP4Q_LAYOUT_LINEAR || (c_type != FP4Q_OUT_F32 && c_type != FP4Q_OUT_BF16)) return FP4Q_EINVAL;
+    if (M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim || ldc < N || ldc > kMaxDim)
+        return FP4Q_ESHAPE;
+    if (K % 128 != 0) return FP4Q_ESHAPE;
+    if ((uint64_t)M * (uint64_t)K / 2 >= (1ull << 32) || (uint64_t)N * (uint64_t)K / 2 >= (1ull << 32))
+        return FP4Q_ESHAPE;
+    *empty = (M == 0 || N == 0);
+    if (*empty) return FP4Q_OK;
+    if (!c) return FP4Q_EINVAL;
+    const uint64_t esize = c_type == FP4Q_OUT_F32 ? 4 : 2;
+    if (!aligned(c, esize)) return FP4Q_EALIGN;
+    if (K == 0) return FP4Q_OK;
+    if (!a_codes || !a_scales || !b_codes || !b_scales) return FP4Q_EINVAL;
+    if (!aligned(a_codes, 16) || !aligned(b_codes, 16) || !aligned(a_scales, 4) || !aligned(b_scales, 4))
+        return FP4Q_EALIGN;
+    const Range rc = bytes(c, ((uint64_t)(M - 1) * (uint64_t)ldc + (uint64_t)N) * esize);
+    const Range ins[4] = {bytes(a_codes, (uint64_t)M * K / 2), bytes(a_scales, (uint64_t)M * K / scale_div),
+                          bytes(b_codes, (uint64_t)N * K / 2), bytes(b_scales, (uint64_t)N * K / scale_div)};
+    for (const Range &r : ins)
+        if (overlap(rc, r)) return FP4Q_EINVAL;
+    return FP4Q_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+fp4q_status fp4_quantize_mx(const void *x, int64_t rows, int64_t cols, int64_t ld_x, int axis, int round,
+                            uint64_t seed, uint32_t stream_id, void *codes, void *scales, int layout, void *stream)
+{
+    return run_mx_producer(x, rows, cols, ld_x, axis, false, 0u, round, seed, stream_id, codes, scales, layout,
+                           stream);
+}
+
+fp4q_status fp4_hadamard32_quantize(const void *x, int64_t rows, int64_t cols, int64_t ld_x, int axis,
+                                    uint32_t sign_mask, int round, uint64_t seed, uint32_t stream_id, void *codes,
+                                    void *scales, int layout, void *stream)
+{
+    return run_mx_producer(x, rows, cols, ld_x, axis, true, sign_mask, round, seed, stream_id, codes, scales, layout,
+                           stream);
+}
+
+size_t fp4q_nv_workspace_bytes(int64_t rows, int64_t cols, int axis, int domain)
+{
+    (void)rows;
+    (void)cols;
+    (void)axis;
+    return domain == FP4Q_NV_GLOBAL ? fp4q::nv_workspace_bytes(0) : 0;
+}
+
+fp4q_status fp4_quantize_nv(const void *x, int64_t rows, int64_t cols, int64_t ld_x, int axis, int round,
+                            uint64_t seed, uint32_t stream_id, int domain, void *codes, void *scales,
+                            float *tensor_scale, void *workspace, size_t workspace_bytes, int layout, void *stream)
+{
+    if ((axis != FP4Q_ALONG_ROWS && axis != FP4Q_ALONG_COLS) || (round != FP4Q_RNE && round != FP4Q_SR) ||
+        (domain != FP4Q_NV_GLOBAL && domain != FP4Q_NV_TILE128) || layout != FP4Q_LAYOUT_LINEAR)
+        return FP4Q_EINVAL;
+    if (rows < 0 || cols < 0 || ld_x < cols || rows > kMaxDim || cols > kMaxDim || ld_x > kMaxDim)
+        return FP4Q_ESHAPE;
+    if (axis == FP4Q_ALONG_COLS) return FP4Q_EUNSUPPORTED;
+    const int64_t R = rows, K = cols;
+    if (K % 16 != 0) return FP4Q_ESHAPE;
+    if ((uint64_t)R * (uint64_t)(K / 8) >= (1ull << 32)) return FP4Q_ESHAPE;
+    const bool empty = R == 0 || K == 0;
+    if (empty && domain == FP4Q_NV_TILE128) return FP4Q_OK;  // no tiles, no tensor scales
+    if (!tensor_scale) return FP4Q_EINVAL;
+    if (!empty && (!x || !codes || !scales)) return FP4Q_EINVAL;
+    if (!empty && (!aligned(x, 16) || !aligned(codes, 16) || ld_x % 8 != 0)) return FP4Q_EALIGN;
+    if (!aligned(tensor_scale, 4)) return FP4Q_EALIGN;
+    const size_t need = fp4q_nv_workspace_bytes(rows, cols, axis, domain);
+    if (need > 0 && (!workspace || workspace_bytes < need)) return FP4Q_EINVAL;
+    if (need > 0 && !aligned(workspace, 4)) return FP4Q_EALIGN;
+    const uint64_t nts = domain == FP4Q_NV_GLOBAL ? 1 : (uint64_t)((R + 127) / 128) * (uint64_t)((K + 127) / 128);
+    const Range rx = bytes(x, input_span(rows, cols, ld_x));
+    const Range outs[4] = {bytes(codes, (uint64_t)R * K / 2), bytes(scales, (uint64_t)R * K / 16),
+                           bytes(tensor_scale, nts * 4), bytes(workspace, need)};
+    for (int i = 0; i < 4; ++i) {
+        if (overlap(rx, outs[i])) return FP4Q_EINVAL;
+        for (int j = i + 1; j < 4; ++j)
+            if (overlap(outs[i], outs[j])) return FP4Q_EINVAL;
+    }
+    fp4q::QuantArgs a{};
+    a.x = x;
+    a.rows = rows;
+    a.cols = cols;
+    a.ld = ld_x;
+    a.axis = axis;
+    a.sr = round == FP4Q_SR;
+    a.seed = seed;
+    a.stream_id = stream_id;
+    a.codes = codes;
+    a.scales = scales;
+    (void)hipGetLastError();
+    return launched(fp4q::launch_quant_nv(a, domain, tensor_scale, workspace, as_stream(stream)));
+}
+
+fp4q_status fp4_gemm_mx(const void *a_codes, const void *a_scales, const void *b_codes, const void *b_scales,
+                        int64_t M, int64_t N, int64_t K, float alpha, int layout, void *c, int c_type, int64_t ldc,
+                        void *stream)
+{
+    bool empty = false;
+    const fp4q_status st =
+        check_gemm_common(a_codes, a_scales, b_codes, b_scales, M, N, K, layout, c, c_type, ldc, 32, &empty);
+    if (st != FP4Q_OK || empty) return st;
+    fp4q::GemmArgs g{};
+    g.a_codes = a_codes;
+    g.a_scales = a_scales;
+    g.b_codes = b_codes;
+    g.b_scales = b_scales;
+    g.M = M;
+    g.N = N;
+    g.K = K;
+    g.alpha = alpha;
+    g.c = c;
+    g.c_bf16 = c_type == FP4Q_OUT_BF16;
+    g.ldc = ldc;
+    (void)hipGetLastError();
+    return launched(fp4q::launch_gemm_mx(g, as_stream(stream)));
+}
+
+fp4q_status fp4_gemm_nv(const void *a_codes, const void *a_scales, const float *a_tensor_scale, const void *b_codes,
+                        const void *b_scales, const float *b_tensor_scale, int domain, int64_t M, int64_t N,
+                        int64_t K, float alpha, int layout, void *c, int c_type, int64_t ldc, void *stream)
+{
+    if (domain != FP4Q_NV_GLOBAL && domain != FP4Q_NV_TILE128) return FP4Q_EINVAL;
+    bool empty = false;
+    const fp4q_status st =
+        check_gemm_common(a_codes, a_scales, b_codes, b_scales, M, N, K, layout, c, c_type, ldc, 16, &empty);
+    if (st != FP4Q_OK || empty) return st;
+    if (K > 0) {
+        if (!a_tensor_scale || !b_tensor_scale) return FP4Q_EINVAL;
+        if (!aligned(a_tensor_scale, 4) || !aligned(b_tensor_scale, 4)) return FP4Q_EALIGN;
+        const uint64_t TK = (uint64_t)(K + 127) / 128;
+        const uint64_t na = domain == FP4Q_NV_GLOBAL ? 1 : (uint64_t)((M + 127) / 128) * TK;
+        const uint64_t nb = domain == FP4Q_NV_GLOBAL ? 1 : (uint64_t)((N + 127) / 128) * TK;
+        const uint64_t esize = c_type == FP4Q_OUT_F32 ? 4 : 2;
+        const Range rc = bytes(c, ((uint64_t)(M - 1) * (uint64_t)ldc + (uint64_t)N) * esize);
+        if (overlap(rc, bytes(a_tensor_scale, na * 4)) || overlap(rc, bytes(b_tensor_scale, nb * 4)))
+            return FP4Q_EINVAL;
+    }
+    fp4q::GemmArgs g{};
+    g.a_codes = a_codes;
+    g.a_scales = a_scales;
+    g.b_codes = b_codes;
+    g.b_scales = b_scales;
+    g.a_ts = a_tensor_scale;
+    g.b_ts = b_tensor_scale;
+    g.nv_domain = domain;
+    g.M = M;
+    g.N = N;
+    g.K = K;
+    g.alpha = alpha;
+    g.c = c;
+    g.c_bf16 = c_type == FP4Q_OUT_BF16;
+    g.ldc = ldc;
+    (void)hipGetLastError();
+    return launched(fp4q::launch_gemm_nv(g, as_stream(stream)));
+}
+
+const char *fp4q_status_str(int status)
+{
+    switch (status) {
+    case FP4Q_OK: return "ok";
+    case FP4Q_EINVAL: return "invalid argument (null pointer, unknown enum, overlapping buffers or small workspace)";
+    case FP4Q_ESHAPE: return "unsupported shape (block multiple, leading dimension or size limit)";
+    case FP4Q_EALIGN: return "misaligned pointer or leading dimension";
+    case FP4Q_ELAUNCH: return "kernel launch failed";
+    case FP4Q_EUNSUPPORTED: return "valid combination not implemented by this build";
+    default: return "unknown status";
+    }
+}
+
+int fp4q_abi_version(void) { return FP4Q_ABI_VERSION; }
+
+}  // extern "C"

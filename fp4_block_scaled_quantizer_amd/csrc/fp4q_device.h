@@ -1,0 +1,138 @@
+// fp4q_device.h -- scalar building blocks of the libfp4q kernels (gfx950).
+//
+// Every function here is __host__ __device__ so that a CPU test can run the
+// very same code over all relevant inputs; the kernels inline them.
+//
+// Pages cited (titles as printed):
+//   [Fusion] "Format-Aware Fusion: The Engineering Practice That Doubles FP4
+//            Pretraining Throughput"
+//   [Stack]  "FP4 Is No Longer Just a Hardware Feature -- The NVFP4 Software
+//            Stack Is Taking Shape"
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define FP4Q_HD __host__ __device__ __forceinline__
+
+namespace fp4q {
+
+FP4Q_HD float u2f(uint32_t u) { return __builtin_bit_cast(float, u); }
+FP4Q_HD uint32_t f2u(float f) { return __builtin_bit_cast(uint32_t, f); }
+
+// Two bf16 values packed in a u32 (element 0 in the low half); widening to
+// binary32 is exact.
+FP4Q_HD float bf16_lo(uint32_t u) { return u2f(u << 16); }
+FP4Q_HD float bf16_hi(uint32_t u) { return u2f(u & 0xFFFF0000u); }
+
+// binary32 -> bf16 bits, round to nearest even (finite values).
+FP4Q_HD uint32_t f32_to_bf16_rne(float f)
+{
+    uint32_t u = f2u(f);
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// E2M1 stochastic rounding ([Fusion] section "Two Key Numerical Techniques":
+// up or down with probability proportional to the distance).  The grid step
+// is g = 0.5 below 2, 1 in [2, 4), 2 in [4, 6); t = |y| / g is exact, its
+// fractional part f is the distance to the lower neighbour in steps, and the
+// value rounds up iff r16 < f * 2^16 (all exact in binary32).  |y| >= 6
+// saturates.  r16 is uniform on [0, 65535].
+FP4Q_HD uint32_t e2m1_sr(float y, uint32_t r16)
+{
+    const uint32_t b = f2u(y);
+    const float m = u2f(b & 0x7FFFFFFFu);
+    const uint32_t s = (b >> 28) & 8u;
+    if (m >= 6.0f) return s | 7u;
+    const float ginv = m < 2.0f ? 2.0f : (m < 4.0f ? 1.0f : 0.5f);
+    const float t = m * ginv;
+    const float fl = floorf(t);
+    const float frac = t - fl;
+    const uint32_t up = (float)r16 < frac * 65536.0f ? 1u : 0u;
+    const uint32_t k0 = m < 2.0f ? (uint32_t)fl : (m < 4.0f ? (uint32_t)fl + 2u : 6u);
+    return s | (k0 + up);
+}
+
+// OCP MX shared exponent byte (E8M0) of a block whose amax has binary32 bits
+// amax_bits: E = floor(log2 amax) - 2 clamped at -127 (zero and tiny blocks),
+// byte = E + 127 = max(biased exponent field - 2, 0).
+FP4Q_HD uint32_t mx_scale_byte(uint32_t amax_bits) { return (amax_bits >> 23) > 2u ? (amax_bits >> 23) - 2u : 0u; }
+
+// 2^-E for scale byte E + 127: a normal binary32 for every byte the rule
+// above produces (biased exponent 254 - byte in [2, 254]).
+FP4Q_HD float mx_inv_scale(uint32_t byte) { return u2f((254u - byte) << 23); }
+
+// OCP FP8 E4M3 value of a code 0x00..0x7E (bias 7, 3 mantissa bits,
+// subnormal step 2^-9).
+FP4Q_HD float e4m3_value(uint32_t c)
+{
+    const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+    if (e == 0) return (float)m * 0x1p-9f;
+    return u2f(((e + 120u) << 23) | (m << 20));
+}
+
+// E4M3 round-to-nearest-even with saturation to 448 (0x7E), z >= 0 finite.
+// Below 2^-6 the E4M3 step is 2^-9, so the code is rint(z * 512) (this also
+// yields 0x08 when z rounds up to 2^-6); above, the 23-bit mantissa is
+// rounded to 3 bits at bit 20 with the carry flowing into the exponent.
+FP4Q_HD uint32_t e4m3_rne_satfinite(float z)
+{
+    if (z >= 448.0f) return 0x7Eu;
+    const uint32_t b = f2u(z);
+    if (b < 0x3C800000u) {  // z < 2^-6
+        return (uint32_t)rintf(z * 512.0f);
+    }
+    const uint32_t r = b + 0x7FFFFu + ((b >> 20) & 1u);
+    const uint32_t eb = (r >> 23) - 120u;  // E4M3 biased exponent (fp32 bias 127, E4M3 bias 7)
+    const uint32_t code = (eb << 3) | ((r >> 20) & 7u);
+    return code < 0x7Eu ? code : 0x7Eu;
+}
+
+// NVFP4 block scale byte and its reciprocal decode scale for block amax b in
+// a domain with tensor scale S ([Stack] section "NVFP4 is more than a 4-bit
+// value"; the clamp of section "The third change": the block scale never
+// becomes zero).  Two correctly rounded divisions in this order, then
+// d = e4m3(sb) * S and one reciprocal.
+FP4Q_HD uint32_t nv_block_scale(float b, float S)
+{
+    const float sbf = (b / 6.0f) / S;
+    const uint32_t sb = e4m3_rne_satfinite(sbf);
+    return sb == 0u ? 1u : sb;
+}
+FP4Q_HD float nv_inv_decode(uint32_t sb, float S) { return 1.0f / (e4m3_value(sb) * S); }
+
+// FP32 tensor-level scale of a domain with amax A (A = 0 gives 1): the
+// domain's largest block then maps onto E4M3 448 x E2M1 6 = 2688.
+FP4Q_HD float nv_tensor_scale(float A) { return A == 0.0f ? 1.0f : A / 2688.0f; }
+
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): ten rounds of two 32x32
+// -> 64-bit multiplies with the published multipliers and Weyl key increments.
+FP4Q_HD void philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3, uint32_t k0, uint32_t k1,
+                           uint32_t out[4])
+{
+#pragma unroll
+    for (int round = 0; round < 10; ++round) {
+        if (round > 0) {
+            k0 += 0x9E3779B9u;
+            k1 += 0xBB67AE85u;
+        }
+        const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+        const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+        const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+        const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+        c1 = (uint32_t)p1;
+        c3 = (uint32_t)p0;
+        c0 = n0;
+        c2 = n2;
+    }
+    out[0] = c0;
+    out[1] = c1;
+    out[2] = c2;
+    out[3] = c3;
+}
+
+// 16 random bits of element j (0..7) of the 8-element group whose Philox
+// words are w[4]: word j/2, high half for odd j.
+FP4Q_HD uint32_t r16_of(const uint32_t w[4], int j) { return (j & 1) ? (w[j >> 1] >> 16) : (w[j >> 1] & 0xFFFFu); }
+
+}  // namespace fp4q

@@ -1,0 +1,41 @@
+// fp4q_internal.h -- argument bundles shared by the C-ABI layer and the
+// kernel launchers of libfp4q.  Not installed; not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fp4q {
+
+struct QuantArgs {
+    const void *x;   // bf16 [rows x ld]
+    int64_t rows, cols, ld;
+    int axis;        // 0: along rows, 1: along columns (x^T)
+    bool sr;
+    bool hadamard;
+    uint64_t seed;
+    uint32_t stream_id;
+    uint32_t sign_mask;
+    void *codes;
+    void *scales;
+};
+
+struct GemmArgs {
+    const void *a_codes, *a_scales, *b_codes, *b_scales;
+    const float *a_ts, *b_ts;  // NV tensor scales (null for MX)
+    int nv_domain;             // NV only: 0 global, 1 tile128
+    int64_t M, N, K;
+    float alpha;
+    void *c;
+    bool c_bf16;
+    int64_t ldc;
+};
+
+int launch_quant_mx(const QuantArgs &a, hipStream_t st);
+int launch_quant_nv(const QuantArgs &a, int domain, float *tensor_scale, void *workspace, hipStream_t st);
+size_t nv_workspace_bytes(int domain);
+int launch_gemm_mx(const GemmArgs &g, hipStream_t st);
+int launch_gemm_nv(const GemmArgs &g, hipStream_t st);
+
+}  // namespace fp4q

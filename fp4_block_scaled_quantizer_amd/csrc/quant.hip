@@ -1,0 +1,541 @@
+// quant.hip -- FP4 quantization producers for gfx950 (MXFP4, MXFP4 with the
+// fixed-sign Hadamard-32, NVFP4 global and per-128x128-tile domains).
+//
+// Pages cited (titles as printed):
+//   [Fusion] "Format-Aware Fusion: The Engineering Practice That Doubles FP4
+//            Pretraining Throughput"
+//   [Stack]  "FP4 Is No Longer Just a Hardware Feature -- The NVFP4 Software
+//            Stack Is Taking Shape"
+//
+// Each producer is one pass over the bf16 input: block amax -> scale ->
+// divide -> E2M1 -> pack -> store, with nothing materialised in between
+// ([Stack] section "The first change: PyTorch is bringing FP4 packing into
+// compiler fusion" describes the unfused chain this avoids).  The kernels are
+// HBM-bound: 2 bytes read and 0.53 (MX) / 0.56 (NV) bytes written per element.
+//
+// Work split (along rows): a lane owns 8 consecutive elements (one 16-byte
+// load of bf16, one 4-byte store of codes).  Four lanes make an MX block of 32
+// and two lanes an NV block of 16; block maxima are combined with cross-lane
+// exchanges inside the wavefront.  Consecutive lanes read consecutive 16-byte
+// chunks, so every wavefront load is a contiguous 1 KiB.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fp4q_device.h"
+#include "fp4q_internal.h"
+
+namespace fp4q {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kChunksPerThread = 4;  // 16-byte chunks per lane per launch slot
+
+// Cross-lane exchange inside a quad of lanes (DPP quad_perm): mask 1 swaps
+// lanes 0<->1 and 2<->3, mask 2 swaps 0<->2 and 1<->3.
+template <int kMask>
+__device__ __forceinline__ uint32_t quad_xor(uint32_t v)
+{
+    static_assert(kMask == 1 || kMask == 2, "quad exchange");
+    constexpr int ctrl = kMask == 1 ? 0xB1 : 0x4E;  // quad_perm [1,0,3,2] / [2,3,0,1]
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, ctrl, 0xF, 0xF, false);
+}
+template <int kMask>
+__device__ __forceinline__ uint32_t xor_max(uint32_t v)
+{
+    return max(v, quad_xor<kMask>(v));
+}
+template <int kMask>
+__device__ __forceinline__ float xor_get(float v)
+{
+    return u2f(quad_xor<kMask>(f2u(v)));
+}
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+// Streaming loads of the bf16 input: each byte is read once, so the loads
+// carry the non-temporal hint.
+__device__ __forceinline__ uint4 load_nt16(const uint16_t *p)
+{
+    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint2 load_nt8(const uint16_t *p)
+{
+    const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t *>(p));
+    return make_uint2(v.x, v.y);
+}
+
+// E2M1 round-to-nearest-even of x / scale for 8 values, by gfx950's scaled
+// FP4 convert (2 values per instruction, element 2j in the low nibble of byte
+// j).  scale must be an exact power of two 2^E.  For such scales the
+// instruction equals the E2M1 RNE rule of this library (ties to even,
+// saturation at 6, sign kept on zero) bit for bit for every finite input:
+// all 65536 bf16 patterns, and binary32 values with random low mantissa
+// bits, were compared with the CPU reference for every E in [-127, 127].
+__device__ __forceinline__ uint32_t cvt8_bf16(const uint4 &q, float scale)
+{
+    uint32_t r = 0;
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, __builtin_bit_cast(bf16x2_t, q.x), scale, 0);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, __builtin_bit_cast(bf16x2_t, q.y), scale, 1);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, __builtin_bit_cast(bf16x2_t, q.z), scale, 2);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, __builtin_bit_cast(bf16x2_t, q.w), scale, 3);
+    return r;
+}
+__device__ __forceinline__ uint32_t cvt8_f32(const float f[8], float scale)
+{
+    uint32_t r = 0;
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, f[0], f[1], scale, 0);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, f[2], f[3], scale, 1);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, f[4], f[5], scale, 2);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, f[6], f[7], scale, 3);
+    return r;
+}
+
+// 2^E as binary32 for E8M0 byte E + 127 (byte 0 -> the subnormal 2^-127).
+__device__ __forceinline__ float mx_scale_f32(uint32_t byte) { return byte ? u2f(byte << 23) : u2f(0x00400000u); }
+
+// Largest |bf16| bit pattern (15 bits) among the 8 values of a chunk.
+__device__ __forceinline__ uint32_t amax8_bf16(const uint4 &q)
+{
+    uint32_t m = max(max(q.x & 0x7FFFu, (q.x >> 16) & 0x7FFFu), max(q.y & 0x7FFFu, (q.y >> 16) & 0x7FFFu));
+    m = max(m, max(max(q.z & 0x7FFFu, (q.z >> 16) & 0x7FFFu), max(q.w & 0x7FFFu, (q.w >> 16) & 0x7FFFu)));
+    return m;
+}
+
+// The 8 bf16 of a chunk as binary32.
+__device__ __forceinline__ void unpack8(const uint4 &q, float f[8])
+{
+    f[0] = bf16_lo(q.x); f[1] = bf16_hi(q.x);
+    f[2] = bf16_lo(q.y); f[3] = bf16_hi(q.y);
+    f[4] = bf16_lo(q.z); f[5] = bf16_hi(q.z);
+    f[6] = bf16_lo(q.w); f[7] = bf16_hi(q.w);
+}
+
+// Butterfly stages of span 1, 2, 4 inside the lane's 8 elements, then 8 and
+// 16 across the lanes of the quad (lane bit 0 and bit 1), in the fixed
+// order of the fixed-sign Hadamard-32 ([Fusion] section "Two Key Numerical
+// Techniques"): (a, b) -> (a + b, a - b) with a the lower index.
+__device__ __forceinline__ void hadamard32_quad(float f[8], uint32_t sign_bits8, int quad_lane)
+{
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        if ((sign_bits8 >> i) & 1u) f[i] = -f[i];
+#pragma unroll
+    for (int h = 1; h < 8; h <<= 1) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            if (i & h) continue;
+            const float a = f[i], b = f[i + h];
+            f[i] = a + b;
+            f[i + h] = a - b;
+        }
+    }
+#pragma unroll
+    for (int bit = 0; bit < 2; ++bit) {
+        const bool upper = (quad_lane >> bit) & 1;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float p = bit == 0 ? xor_get<1>(f[i]) : xor_get<2>(f[i]);
+            f[i] = upper ? (p - f[i]) : (f[i] + p);
+        }
+    }
+}
+
+// ------------------------------------------------------------------
+// MXFP4 along rows (optionally Hadamard-32 first, optionally SR)
+// ------------------------------------------------------------------
+template <bool kSR, bool kHad, bool kContig>
+__global__ __launch_bounds__(kThreads) void quant_mx_rows_kernel(const uint16_t *__restrict__ x, uint32_t K,
+                                                                 uint32_t ld, uint32_t nchunks,
+                                                                 uint32_t *__restrict__ codes,
+                                                                 uint8_t *__restrict__ scales, uint32_t seed_lo,
+                                                                 uint32_t seed_hi, uint32_t stream_id,
+                                                                 uint32_t sign_mask)
+{
+    const uint32_t cpr = K >> 3;  // 16-byte chunks per row
+    const uint32_t base = blockIdx.x * (kThreads * kChunksPerThread) + threadIdx.x;
+    const int quad_lane = threadIdx.x & 3;
+    uint4 q[kChunksPerThread];
+#pragma unroll
+    for (int i = 0; i < kChunksPerThread; ++i) {
+        const uint32_t c = base + i * kThreads;
+        q[i] = make_uint4(0u, 0u, 0u, 0u);
+        if (c < nchunks) {
+            size_t off;
+            if (kContig) {
+                off = (size_t)c * 8;
+            } else {
+                const uint32_t r = c / cpr;
+                off = (size_t)r * ld + (size_t)(c - r * cpr) * 8;
+            }
+            q[i] = load_nt16(x + off);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < kChunksPerThread; ++i) {
+        const uint32_t c = base + i * kThreads;
+        uint32_t packed = 0, sbyte;
+        if (!kHad && !kSR) {
+            // bf16 straight into the scaled convert: no binary32 unpack
+            uint32_t amax = amax8_bf16(q[i]);
+            amax = xor_max<1>(amax);
+            amax = xor_max<2>(amax);
+            sbyte = mx_scale_byte(amax << 16);
+            packed = cvt8_bf16(q[i], mx_scale_f32(sbyte));
+        } else {
+            float f[8];
+            unpack8(q[i], f);
+            if (kHad) hadamard32_quad(f, (sign_mask >> (8 * quad_lane)) & 0xFFu, quad_lane);
+            uint32_t amax = 0;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) amax = max(amax, f2u(f[j]) & 0x7FFFFFFFu);
+            amax = xor_max<1>(amax);
+            amax = xor_max<2>(amax);
+            sbyte = mx_scale_byte(amax);
+            if (kSR) {
+                const float inv = mx_inv_scale(sbyte);
+                const uint32_t r = c / cpr;
+                const uint32_t c8 = c - r * cpr;
+                uint32_t w[4];
+                philox4x32_10(c8, r, stream_id, 0u, seed_lo, seed_hi, w);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) packed |= e2m1_sr(f[j] * inv, r16_of(w, j)) << (4 * j);
+            } else {
+                packed = cvt8_f32(f, mx_scale_f32(sbyte));
+            }
+        }
+        if (c < nchunks) {
+            __builtin_nontemporal_store(packed, codes + c);
+            if (quad_lane == 0) scales[c >> 2] = (uint8_t)sbyte;
+        }
+    }
+}
+
+// ------------------------------------------------------------------
+// MXFP4 along columns: the logical operand is x^T, blocks run down 32 rows of
+// one column of x.  A lane owns 4 adjacent columns (8-byte loads, so a
+// wavefront reads 512 contiguous bytes of each row) and walks kBlocks
+// consecutive 32-row blocks, so its 16-byte code stores for one output row
+// land next to each other.
+// ------------------------------------------------------------------
+constexpr int kColBlocks = 4;
+
+template <bool kSR, bool kHad>
+__global__ __launch_bounds__(64) void quant_mx_cols_kernel(const uint16_t *__restrict__ x, uint32_t rows,
+                                                           uint32_t cols, uint32_t ld, uint8_t *__restrict__ codes,
+                                                           uint8_t *__restrict__ scales, uint32_t seed_lo,
+                                                           uint32_t seed_hi, uint32_t stream_id, uint32_t sign_mask)
+{
+    const uint32_t col0 = (blockIdx.x * 64 + threadIdx.x) * 4;  // first of this lane's 4 columns
+    const uint32_t Kb = rows >> 5;                               // blocks per output row
+    const uint32_t j0 = blockIdx.y * kColBlocks;
+    if (col0 >= cols) return;  // whole lane idle; no cross-lane work below
+    const uint32_t K2 = rows >> 1;  // bytes of codes per output row
+    for (int jb = 0; jb < kColBlocks; ++jb) {
+        const uint32_t j = j0 + jb;
+        if (j >= Kb) break;
+        uint2 raw[32];
+#pragma unroll
+        for (int i = 0; i < 32; ++i)
+            raw[i] = load_nt8(x + (size_t)(32 * j + i) * ld + col0);
+#pragma unroll
+        for (int cq = 0; cq < 4; ++cq) {
+            const uint32_t col = col0 + cq;
+            float v[32];
+#pragma unroll
+            for (int i = 0; i < 32; ++i) {
+                const uint32_t word = (cq < 2) ? raw[i].x : raw[i].y;
+                v[i] = (cq & 1) ? bf16_hi(word) : bf16_lo(word);
+            }
+            if (kHad) {
+#pragma unroll
+                for (int i = 0; i < 32; ++i)
+                    if ((sign_mask >> i) & 1u) v[i] = -v[i];
+#pragma unroll
+                for (int h = 1; h < 32; h <<= 1) {
+#pragma unroll
+                    for (int i = 0; i < 32; ++i) {
+                        if (i & h) continue;
+                        const float a = v[i], b = v[i + h];
+                        v[i] = a + b;
+                        v[i + h] = a - b;
+                    }
+                }
+            }
+            uint32_t amax = 0;
+#pragma unroll
+            for (int i = 0; i < 32; ++i) amax = max(amax, f2u(v[i]) & 0x7FFFFFFFu);
+            const uint32_t sbyte = mx_scale_byte(amax);
+            const float inv = mx_inv_scale(sbyte);
+            const float scale = mx_scale_f32(sbyte);
+            uint32_t out[4];
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                uint32_t packed = 0;
+                if (kSR) {
+                    uint32_t w[4];
+                    philox4x32_10(4 * j + g, col, stream_id, 0u, seed_lo, seed_hi, w);
+#pragma unroll
+                    for (int t = 0; t < 8; ++t) packed |= e2m1_sr(v[8 * g + t] * inv, r16_of(w, t)) << (4 * t);
+                } else {
+                    packed = cvt8_f32(v + 8 * g, scale);
+                }
+                out[g] = packed;
+            }
+            if (col < cols) {
+                uint4 o = make_uint4(out[0], out[1], out[2], out[3]);
+                *reinterpret_cast<uint4 *>(codes + (size_t)col * K2 + (size_t)j * 16) = o;
+                scales[(size_t)col * Kb + j] = (uint8_t)sbyte;
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------------
+// NVFP4, global domain: pass 1 writes one partial maximum per workgroup,
+// pass 2 folds them into the domain amax A, derives S and quantizes.
+// ------------------------------------------------------------------
+constexpr int kAmaxBlocks = 1024;
+
+__device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t *sh)
+{
+    for (int m = 32; m >= 1; m >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, m, 64));
+    const int wave = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) sh[wave] = v;
+    __syncthreads();
+    uint32_t r = sh[0];
+    for (int w = 1; w < (int)(blockDim.x >> 6); ++w) r = max(r, sh[w]);
+    __syncthreads();
+    return r;
+}
+
+__global__ __launch_bounds__(kThreads) void nv_amax_partial_kernel(const uint16_t *__restrict__ x, uint32_t K,
+                                                                   uint32_t ld, uint32_t nchunks,
+                                                                   uint32_t *__restrict__ partial)
+{
+    __shared__ uint32_t sh[kThreads / 64];
+    const uint32_t cpr = K >> 3;
+    uint32_t m = 0;
+    for (uint32_t c = blockIdx.x * kThreads + threadIdx.x; c < nchunks; c += gridDim.x * kThreads) {
+        const uint32_t r = c / cpr;
+        const uint4 q = load_nt16(x + (size_t)r * ld + (size_t)(c - r * cpr) * 8);
+        m = max(m, max(max(q.x & 0x7FFFu, (q.x >> 16) & 0x7FFFu), max(q.y & 0x7FFFu, (q.y >> 16) & 0x7FFFu)));
+        m = max(m, max(max(q.z & 0x7FFFu, (q.z >> 16) & 0x7FFFu), max(q.w & 0x7FFFu, (q.w >> 16) & 0x7FFFu)));
+    }
+    m = block_max_u32(m, sh);
+    if (threadIdx.x == 0) partial[blockIdx.x] = m << 16;  // binary32 bits of the partial amax
+}
+
+template <bool kSR>
+__device__ __forceinline__ uint32_t nv_encode8(const float f[8], float S, uint32_t *sb_out, uint32_t r,
+                                               uint32_t c8, uint32_t stream_id, uint32_t seed_lo,
+                                               uint32_t seed_hi)
+{
+    uint32_t bmax = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) bmax = max(bmax, f2u(f[j]) & 0x7FFFFFFFu);
+    bmax = xor_max<1>(bmax);  // the two lanes of a 16-element block
+    const uint32_t sb = nv_block_scale(u2f(bmax), S);
+    const float inv = nv_inv_decode(sb, S);
+    float y[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) y[j] = f[j] * inv;
+    uint32_t packed = 0;
+    if (kSR) {
+        uint32_t w[4];
+        philox4x32_10(c8, r, stream_id, 0u, seed_lo, seed_hi, w);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) packed |= e2m1_sr(y[j], r16_of(w, j)) << (4 * j);
+    } else {
+        packed = cvt8_f32(y, 1.0f);  // scale 2^0: plain RNE of y, saturating
+    }
+    *sb_out = sb;
+    return packed;
+}
+
+template <bool kSR>
+__global__ __launch_bounds__(kThreads) void nv_quant_global_kernel(const uint16_t *__restrict__ x, uint32_t K,
+                                                                   uint32_t ld, uint32_t nchunks,
+                                                                   const uint32_t *__restrict__ partial,
+                                                                   uint32_t npartial, uint32_t *__restrict__ codes,
+                                                                   uint8_t *__restrict__ scales,
+                                                                   float *__restrict__ tensor_scale,
+                                                                   uint32_t seed_lo, uint32_t seed_hi,
+                                                                   uint32_t stream_id)
+{
+    __shared__ uint32_t sh[kThreads / 64];
+    uint32_t a = 0;
+    for (uint32_t i = threadIdx.x; i < npartial; i += kThreads) a = max(a, partial[i]);
+    a = block_max_u32(a, sh);
+    const float S = nv_tensor_scale(u2f(a));
+    if (blockIdx.x == 0 && threadIdx.x == 0) *tensor_scale = S;
+
+    const uint32_t cpr = K >> 3;
+    const uint32_t base = blockIdx.x * (kThreads * kChunksPerThread) + threadIdx.x;
+    uint4 q[kChunksPerThread];
+#pragma unroll
+    for (int i = 0; i < kChunksPerThread; ++i) {
+        const uint32_t c = base + i * kThreads;
+        q[i] = make_uint4(0u, 0u, 0u, 0u);
+        if (c < nchunks) {
+            const uint32_t r = c / cpr;
+            q[i] = load_nt16(x + (size_t)r * ld + (size_t)(c - r * cpr) * 8);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < kChunksPerThread; ++i) {
+        const uint32_t c = base + i * kThreads;
+        const uint32_t r = c / cpr;
+        float f[8];
+        unpack8(q[i], f);
+        uint32_t sb;
+        const uint32_t packed = nv_encode8<kSR>(f, S, &sb, r, c - r * cpr, stream_id, seed_lo, seed_hi);
+        if (c < nchunks) {
+            __builtin_nontemporal_store(packed, codes + c);
+            if ((threadIdx.x & 1) == 0) scales[c >> 1] = (uint8_t)sb;
+        }
+    }
+}
+
+// ------------------------------------------------------------------
+// NVFP4, per-128x128-tile domain ("CTA-local"): one workgroup owns one tile,
+// takes its amax, writes its S, then quantizes it from registers.  No
+// grid-wide dependency.  Lane t handles chunks t + 256 i (i < 8) of the
+// tile's 128 rows x 16 chunks.
+// ------------------------------------------------------------------
+template <bool kSR>
+__global__ __launch_bounds__(kThreads) void nv_quant_tile_kernel(const uint16_t *__restrict__ x, uint32_t R,
+                                                                 uint32_t K, uint32_t ld,
+                                                                 uint32_t *__restrict__ codes,
+                                                                 uint8_t *__restrict__ scales,
+                                                                 float *__restrict__ tensor_scale,
+                                                                 uint32_t seed_lo, uint32_t seed_hi,
+                                                                 uint32_t stream_id)
+{
+    __shared__ uint32_t sh[kThreads / 64];
+    const uint32_t TK = (K + 127) >> 7;
+    const uint32_t tr = blockIdx.y, tk = blockIdx.x;
+    const uint32_t cpr = K >> 3;
+    uint4 q[8];
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint32_t t = threadIdx.x + kThreads * i;
+        const uint32_t r = tr * 128 + (t >> 4);
+        const uint32_t c8 = tk * 16 + (t & 15);
+        q[i] = make_uint4(0u, 0u, 0u, 0u);
+        if (r < R && c8 < cpr)
+            q[i] = load_nt16(x + (size_t)r * ld + (size_t)c8 * 8);
+        m = max(m, max(max(q[i].x & 0x7FFFu, (q[i].x >> 16) & 0x7FFFu), max(q[i].y & 0x7FFFu, (q[i].y >> 16) & 0x7FFFu)));
+        m = max(m, max(max(q[i].z & 0x7FFFu, (q[i].z >> 16) & 0x7FFFu), max(q[i].w & 0x7FFFu, (q[i].w >> 16) & 0x7FFFu)));
+    }
+    m = block_max_u32(m, sh);
+    const float S = nv_tensor_scale(u2f(m << 16));
+    if (threadIdx.x == 0) tensor_scale[tr * TK + tk] = S;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint32_t t = threadIdx.x + kThreads * i;
+        const uint32_t r = tr * 128 + (t >> 4);
+        const uint32_t c8 = tk * 16 + (t & 15);
+        float f[8];
+        unpack8(q[i], f);
+        uint32_t sb;
+        const uint32_t packed = nv_encode8<kSR>(f, S, &sb, r, c8, stream_id, seed_lo, seed_hi);
+        if (r < R && c8 < cpr) {
+            const size_t c = (size_t)r * cpr + c8;
+            __builtin_nontemporal_store(packed, codes + c);
+            if ((threadIdx.x & 1) == 0) scales[c >> 1] = (uint8_t)sb;
+        }
+    }
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------ launchers
+
+int launch_quant_mx(const QuantArgs &a, hipStream_t st)
+{
+    const uint32_t seed_lo = (uint32_t)a.seed, seed_hi = (uint32_t)(a.seed >> 32);
+    if (a.axis == 0) {
+        const uint32_t R = (uint32_t)a.rows, K = (uint32_t)a.cols;
+        const uint64_t nchunks = (uint64_t)R * (K >> 3);
+        if (nchunks == 0) return 0;
+        const uint32_t grid = (uint32_t)((nchunks + kThreads * kChunksPerThread - 1) / (kThreads * kChunksPerThread));
+        const bool contig = a.ld == a.cols;
+        auto *codes = reinterpret_cast<uint32_t *>(a.codes);
+        auto *scales = reinterpret_cast<uint8_t *>(a.scales);
+        auto *x = reinterpret_cast<const uint16_t *>(a.x);
+#define FP4Q_LAUNCH_ROWS(SR, HAD, CONTIG)                                                                   \
+    hipLaunchKernelGGL((quant_mx_rows_kernel<SR, HAD, CONTIG>), dim3(grid), dim3(kThreads), 0, st, x, K,       \
+                       (uint32_t)a.ld, (uint32_t)nchunks, codes, scales, seed_lo, seed_hi, a.stream_id, a.sign_mask)
+        if (a.sr) {
+            if (a.hadamard) { if (contig) FP4Q_LAUNCH_ROWS(true, true, true); else FP4Q_LAUNCH_ROWS(true, true, false); }
+            else { if (contig) FP4Q_LAUNCH_ROWS(true, false, true); else FP4Q_LAUNCH_ROWS(true, false, false); }
+        } else {
+            if (a.hadamard) { if (contig) FP4Q_LAUNCH_ROWS(false, true, true); else FP4Q_LAUNCH_ROWS(false, true, false); }
+            else { if (contig) FP4Q_LAUNCH_ROWS(false, false, true); else FP4Q_LAUNCH_ROWS(false, false, false); }
+        }
+#undef FP4Q_LAUNCH_ROWS
+    } else {
+        const uint32_t rows = (uint32_t)a.rows, cols = (uint32_t)a.cols;
+        if (rows == 0 || cols == 0) return 0;
+        const uint32_t Kb = rows >> 5;
+        dim3 grid((cols + 255) / 256, (Kb + kColBlocks - 1) / kColBlocks);
+        auto *x = reinterpret_cast<const uint16_t *>(a.x);
+        auto *codes = reinterpret_cast<uint8_t *>(a.codes);
+        auto *scales = reinterpret_cast<uint8_t *>(a.scales);
+#define FP4Q_LAUNCH_COLS(SR, HAD)                                                                         \
+    hipLaunchKernelGGL((quant_mx_cols_kernel<SR, HAD>), grid, dim3(64), 0, st, x, rows, cols, (uint32_t)a.ld, \
+                       codes, scales, seed_lo, seed_hi, a.stream_id, a.sign_mask)
+        if (a.sr) { if (a.hadamard) FP4Q_LAUNCH_COLS(true, true); else FP4Q_LAUNCH_COLS(true, false); }
+        else { if (a.hadamard) FP4Q_LAUNCH_COLS(false, true); else FP4Q_LAUNCH_COLS(false, false); }
+#undef FP4Q_LAUNCH_COLS
+    }
+    return hipGetLastError() == hipSuccess ? 0 : 1;
+}
+
+size_t nv_workspace_bytes(int domain) { return domain == 0 ? (size_t)kAmaxBlocks * sizeof(uint32_t) : 0; }
+
+int launch_quant_nv(const QuantArgs &a, int domain, float *tensor_scale, void *workspace, hipStream_t st)
+{
+    const uint32_t seed_lo = (uint32_t)a.seed, seed_hi = (uint32_t)(a.seed >> 32);
+    const uint32_t R = (uint32_t)a.rows, K = (uint32_t)a.cols;
+    auto *x = reinterpret_cast<const uint16_t *>(a.x);
+    auto *codes = reinterpret_cast<uint32_t *>(a.codes);
+    auto *scales = reinterpret_cast<uint8_t *>(a.scales);
+    if (domain == 0) {
+        const uint64_t nchunks = (uint64_t)R * (K >> 3);
+        auto *partial = reinterpret_cast<uint32_t *>(workspace);
+        uint32_t np = (uint32_t)((nchunks + kThreads - 1) / kThreads);
+        if (np > (uint32_t)kAmaxBlocks) np = kAmaxBlocks;
+        if (np == 0) np = 1;
+        // pass 1 (also runs for an empty operand so that S = 1 is written)
+        hipLaunchKernelGGL(nv_amax_partial_kernel, dim3(np), dim3(kThreads), 0, st, x, K, (uint32_t)a.ld,
+                           (uint32_t)nchunks, partial);
+        const uint32_t grid = (uint32_t)((nchunks + kThreads * kChunksPerThread - 1) / (kThreads * kChunksPerThread));
+        const uint32_t g = grid == 0 ? 1 : grid;
+        if (a.sr)
+            hipLaunchKernelGGL(nv_quant_global_kernel<true>, dim3(g), dim3(kThreads), 0, st, x, K, (uint32_t)a.ld,
+                               (uint32_t)nchunks, partial, np, codes, scales, tensor_scale, seed_lo, seed_hi,
+                               a.stream_id);
+        else
+            hipLaunchKernelGGL(nv_quant_global_kernel<false>, dim3(g), dim3(kThreads), 0, st, x, K,
+                               (uint32_t)a.ld, (uint32_t)nchunks, partial, np, codes, scales, tensor_scale, seed_lo,
+                               seed_hi, a.stream_id);
+    } else {
+        if (R == 0 || K == 0) return 0;
+        dim3 grid((K + 127) / 128, (R + 127) / 128);
+        if (a.sr)
+            hipLaunchKernelGGL(nv_quant_tile_kernel<true>, grid, dim3(kThreads), 0, st, x, R, K, (uint32_t)a.ld,
+                               codes, scales, tensor_scale, seed_lo, seed_hi, a.stream_id);
+        else
+            hipLaunchKernelGGL(nv_quant_tile_kernel<false>, grid, dim3(kThreads), 0, st, x, R, K, (uint32_t)a.ld,
+                               codes, scales, tensor_scale, seed_lo, seed_hi, a.stream_id);
+    }
+    return hipGetLastError() == hipSuccess ? 0 : 1;
+}
+
+}  // namespace fp4q

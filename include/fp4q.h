@@ -1,0 +1,187 @@
+/*
+ * fp4q.h -- C ABI of libfp4q: FP4 block-scaled quantization producers and the
+ * block-scaled FP4 GEMM that consumes them, for AMD Instinct MI355X (gfx950).
+ *
+ * Pages cited (titles as printed):
+ *   [Fusion] "Format-Aware Fusion: The Engineering Practice That Doubles FP4
+ *            Pretraining Throughput"
+ *   [Stack]  "FP4 Is No Longer Just a Hardware Feature -- The NVFP4 Software
+ *            Stack Is Taking Shape"
+ *   [OnGPUs] "4-Bit Floating Point (FP4) on GPUs: How It Works and When It Pays Off"
+ *
+ * What the library computes.  A quantization producer turns a bf16 matrix
+ * into a two-part FP4 operand ([OnGPUs], section "How Does 4-Bit Floating
+ * Point Work in Practice?": packed 4-bit payload plus per-block scales) in one
+ * pass: block amax -> scale -> divide by the scale -> E2M1 -> pack two codes
+ * per byte ([Stack], section "The first change: PyTorch is bringing FP4
+ * packing into compiler fusion").  Each producer is bound to its scale domain
+ * and to the layout its GEMM loads ([Fusion], section "The Design Philosophy
+ * of Format-Aware Fusion": native mxfp, global nvfp, CTA-local nvfp).
+ *
+ * Numerical contract (bit-exact; every output byte is a pure function of the
+ * inputs):
+ *   E2M1 code  = sign<<3 | k, magnitudes {0, .5, 1, 1.5, 2, 3, 4, 6}[k];
+ *                the sign bit is kept for negative values that round to zero.
+ *   RNE        round to nearest, ties to even k; |y| >= 6 saturates to k = 7.
+ *   SR         with lo <= |y| < hi the neighbouring magnitudes, round up iff
+ *              r16 < 65536 * (|y| - lo) / (hi - lo); r16 = 16 bits of
+ *              Philox4x32-10 (Salmon et al., SC'11) with counter
+ *              {k/8, r, stream_id, 0} and key {seed low, seed high}, word
+ *              (k/2) mod 4, high half for odd k; (r, k) are coordinates in the
+ *              logical operand, so results do not depend on the launch shape.
+ *   MX         32-element blocks along K; shared exponent
+ *              E = clamp(floor(log2 amax) - 2, -127, 127) (OCP MX v1.0; an
+ *              all-zero block gets -127); scale byte = E + 127 (E8M0);
+ *              y = x * 2^-E in binary32.
+ *   NV         16-element blocks along K; tensor scale S = A / 2688 (A = amax
+ *              of the domain; S = 1 when A = 0); block scale
+ *              sb = E4M3_RNE_satfinite((b / 6) / S) clamped to >= 0x01
+ *              ([Stack], section "The third change: oneDNN is defining a safe
+ *              numerical range for FP4 scales"); d = e4m3(sb) * S;
+ *              y = x * (1 / d) in binary32.
+ *   Hadamard   before MX: x <- H32 * diag(d) * x per 32-block along K, d_i = -1
+ *              where bit i of sign_mask is set, H32 the unnormalised Sylvester
+ *              matrix, evaluated as butterflies of span 1, 2, 4, 8, 16 in
+ *              binary32 ([Fusion], section "Two Key Numerical Techniques").
+ *              H32 * H32^T = 32 I, so a GEMM of two such operands takes
+ *              alpha = 1/32.
+ *
+ * Operands.  The input x is a row-major bf16 [rows x cols] matrix with leading
+ * dimension ld_x >= cols (elements).  The logical quantized operand [R x K] is
+ * x itself for FP4Q_ALONG_ROWS (R = rows, K = cols) and x^T for
+ * FP4Q_ALONG_COLS (R = cols, K = rows): blocks then run down the columns of x
+ * (the transpose-quantize a wgrad/dgrad operand needs).
+ * Linear layout (FP4Q_LAYOUT_LINEAR):
+ *   codes   [R x K/2] bytes, row-major; element 2j in the low nibble of byte j,
+ *           element 2j+1 in the high nibble ([Stack] pairs even and odd
+ *           elements into one byte);
+ *   scales  MX: [R x K/32] E8M0 bytes; NV: [R x K/16] E4M3 bytes, row-major;
+ *   tensor_scale  NV global: 1 float; NV tile128: [ceil(R/128) x ceil(K/128)]
+ *           floats, row-major, one per 128 x 128 tile of the logical operand.
+ *
+ * GEMM.  C[M x N] = alpha * A * B^T, A the logical [M x K] operand and B the
+ * logical [N x K] operand, both quantized along K; fp32 accumulation; C is
+ * row-major with leading dimension ldc >= N, fp32 or bf16 (round to nearest
+ * even from the fp32 result).  For Y = X * W^T pass X as A and W as B.
+ *
+ * Ownership and execution.  Every pointer is device memory owned by the
+ * caller (for example PyTorch tensors).  The library never allocates, frees
+ * or synchronizes; every call enqueues its kernels on `stream` (a hipStream_t;
+ * NULL = the default stream) and returns once they are enqueued.  Outputs are
+ * valid after the stream is synchronized.  Inputs must not overlap outputs.
+ *
+ * Errors.  Arguments are checked on the host before any launch; a failing
+ * check returns a status and enqueues nothing:
+ *   FP4Q_EINVAL       null pointer, unknown enum value, overlapping buffers,
+ *                     workspace too small;
+ *   FP4Q_ESHAPE       negative size, K not a multiple of the block (32 MX,
+ *                     16 NV), GEMM K not a multiple of 128, ld_x < cols,
+ *                     ldc < N, a dimension above 2^31 - 1;
+ *   FP4Q_EALIGN       x, codes or GEMM operand pointers not 16-byte aligned,
+ *                     ld_x not a multiple of 8 elements;
+ *   FP4Q_EUNSUPPORTED a valid combination this build does not implement
+ *                     (listed at each call);
+ *   FP4Q_ELAUNCH      the kernel launch failed (hipGetLastError).
+ * Inputs outside the numerical contract (NaN or Inf anywhere in x, an NV
+ * domain with 0 < amax < 2^-100) are not detected and give unspecified codes.
+ * Empty operands (R == 0 or K == 0, or M, N or K == 0) are valid and enqueue
+ * nothing, except that a GEMM with K == 0 writes C = 0.
+ */
+#ifndef FP4Q_H
+#define FP4Q_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FP4Q_ABI_VERSION 1
+
+/* Symbols of the C ABI are the only ones the shared library exports. */
+#if defined(__GNUC__) || defined(__clang__)
+#define FP4Q_API __attribute__((visibility("default")))
+#else
+#define FP4Q_API
+#endif
+
+typedef enum {
+    FP4Q_OK = 0,
+    FP4Q_EINVAL = 1,
+    FP4Q_ESHAPE = 2,
+    FP4Q_EALIGN = 3,
+    FP4Q_ELAUNCH = 4,
+    FP4Q_EUNSUPPORTED = 5
+} fp4q_status;
+
+typedef enum { FP4Q_ALONG_ROWS = 0, FP4Q_ALONG_COLS = 1 } fp4q_axis;
+typedef enum { FP4Q_RNE = 0, FP4Q_SR = 1 } fp4q_round;
+typedef enum { FP4Q_NV_GLOBAL = 0, FP4Q_NV_TILE128 = 1 } fp4q_nv_domain;
+typedef enum { FP4Q_LAYOUT_LINEAR = 0 } fp4q_layout;
+typedef enum { FP4Q_OUT_F32 = 0, FP4Q_OUT_BF16 = 1 } fp4q_out;
+
+/* MXFP4 producer ("native mxfp", [Fusion] section "The Design Philosophy of
+ * Format-Aware Fusion"; steps of [Stack] section "The first change").
+ * x: bf16 [rows x ld_x]; writes codes [R x K/2] and E8M0 scales [R x K/32].
+ * round = FP4Q_SR uses (seed, stream_id) as stated above ("row-gradient
+ * stochastic rounding", [Fusion] section "Two Key Numerical Techniques").
+ * Requires K % 32 == 0.  Both axes, both rounding modes. */
+FP4Q_API fp4q_status fp4_quantize_mx(const void *x, int64_t rows, int64_t cols, int64_t ld_x, int axis,
+                            int round, uint64_t seed, uint32_t stream_id, void *codes, void *scales,
+                            int layout, void *stream);
+
+/* Fixed-sign 32-point Hadamard, then MXFP4 ("fixed-sign 32-value Hadamard
+ * weight-gradient preconditioning", [Fusion] section "Two Key Numerical
+ * Techniques").  Same outputs and requirements as fp4_quantize_mx; the
+ * transform runs along K in the same 32-blocks as the scales. */
+FP4Q_API fp4q_status fp4_hadamard32_quantize(const void *x, int64_t rows, int64_t cols, int64_t ld_x, int axis,
+                                    uint32_t sign_mask, int round, uint64_t seed, uint32_t stream_id,
+                                    void *codes, void *scales, int layout, void *stream);
+
+/* Bytes of device workspace fp4_quantize_nv needs (the global domain's
+ * partial maxima; 0 for the tile domain). */
+FP4Q_API size_t fp4q_nv_workspace_bytes(int64_t rows, int64_t cols, int axis, int domain);
+
+/* NVFP4 producer: "global nvfp" (domain FP4Q_NV_GLOBAL, one FP32 tensor scale
+ * from the whole operand's amax; two kernels: partial maxima into `workspace`,
+ * then quantize) or "CTA-local nvfp" (FP4Q_NV_TILE128, one tensor scale per
+ * 128 x 128 tile, one kernel) ([Fusion] section "The Design Philosophy of
+ * Format-Aware Fusion"; the two-level scale of [Stack] section "NVFP4 is more
+ * than a 4-bit value").  Writes codes [R x K/2], E4M3 scales [R x K/16] and
+ * tensor_scale.  Requires K % 16 == 0.  FP4Q_EUNSUPPORTED: axis
+ * FP4Q_ALONG_COLS. */
+FP4Q_API fp4q_status fp4_quantize_nv(const void *x, int64_t rows, int64_t cols, int64_t ld_x, int axis, int round,
+                            uint64_t seed, uint32_t stream_id, int domain, void *codes, void *scales,
+                            float *tensor_scale, void *workspace, size_t workspace_bytes, int layout,
+                            void *stream);
+
+/* MXFP4 GEMM on gfx950's scaled FP4 MFMA (E8M0 scales applied by the matrix
+ * core): C = alpha * A * B^T.  a_codes [M x K/2], a_scales [M x K/32],
+ * b_codes [N x K/2], b_scales [N x K/32] as written by the MX producers.
+ * Requires K % 128 == 0; M and N are arbitrary. */
+FP4Q_API fp4q_status fp4_gemm_mx(const void *a_codes, const void *a_scales, const void *b_codes, const void *b_scales,
+                        int64_t M, int64_t N, int64_t K, float alpha, int layout, void *c, int c_type,
+                        int64_t ldc, void *stream);
+
+/* NVFP4 GEMM: E2M1 x E4M3 is dequantized exactly to bf16 and multiplied on
+ * bf16 MFMA; the FP32 tensor scales multiply the fp32 partial sums (once in
+ * the epilogue for the global domain, per 128-wide K slice for tile128).
+ * a_tensor_scale / b_tensor_scale as written by fp4_quantize_nv with the same
+ * domain.  Requires K % 128 == 0. */
+FP4Q_API fp4q_status fp4_gemm_nv(const void *a_codes, const void *a_scales, const float *a_tensor_scale,
+                        const void *b_codes, const void *b_scales, const float *b_tensor_scale, int domain,
+                        int64_t M, int64_t N, int64_t K, float alpha, int layout, void *c, int c_type,
+                        int64_t ldc, void *stream);
+
+/* Human-readable text for a status code (static storage). */
+FP4Q_API const char *fp4q_status_str(int status);
+
+/* FP4Q_ABI_VERSION of the built library. */
+FP4Q_API int fp4q_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP4Q_H */

@@ -1,0 +1,128 @@
+"""The C-ABI library loads, exports every function include/fp4q.h declares,
+and rejects bad arguments with the documented status before any HIP call
+(so these run without a GPU; the pointers below are never dereferenced)."""
+import ctypes
+
+import pytest
+
+from fp4_block_scaled_quantizer_amd import binding as B
+
+L = None
+X = 0x7F0000000000  # fake, 16-byte aligned device addresses far apart
+CODES = 0x7F1000000000
+SCALES = 0x7F2000000000
+TS = 0x7F3000000000
+WS = 0x7F4000000000
+C = 0x7F5000000000
+
+
+@pytest.fixture(scope="module", autouse=True)
+def lib():
+    global L
+    L = B.lib()
+    return L
+
+
+def test_exports_every_declared_function():
+    names = B.declared_functions()
+    assert set(names) >= {"fp4_quantize_mx", "fp4_quantize_nv", "fp4_hadamard32_quantize", "fp4_gemm_mx",
+                          "fp4_gemm_nv"}
+    for n in names:
+        assert hasattr(L, n), n
+    assert B.abi_version() == 1
+    for s in range(6):
+        assert B.status_str(s)
+
+
+def q_mx(x=X, rows=64, cols=64, ld=64, axis=0, rnd=0, codes=CODES, scales=SCALES, layout=0):
+    return L.fp4_quantize_mx(x, rows, cols, ld, axis, rnd, 7, 0, codes, scales, layout, None)
+
+
+def test_quantize_mx_status_codes():
+    assert q_mx(axis=2) == B.EINVAL
+    assert q_mx(rnd=5) == B.EINVAL
+    assert q_mx(layout=3) == B.EINVAL
+    assert q_mx(x=None) == B.EINVAL
+    assert q_mx(codes=None) == B.EINVAL
+    assert q_mx(scales=None) == B.EINVAL
+    assert q_mx(cols=48, ld=48) == B.ESHAPE          # K % 32
+    assert q_mx(axis=1, rows=48) == B.ESHAPE         # K = rows % 32
+    assert q_mx(axis=1, cols=62, ld=64) == B.ESHAPE  # column axis needs cols % 4
+    assert q_mx(ld=32) == B.ESHAPE                   # ld < cols
+    assert q_mx(rows=-1) == B.ESHAPE
+    assert q_mx(rows=2**31) == B.ESHAPE
+    assert q_mx(x=X + 8) == B.EALIGN
+    assert q_mx(codes=CODES + 4) == B.EALIGN
+    assert q_mx(ld=68) == B.EALIGN
+    assert q_mx(codes=X + 64) == B.EINVAL            # output overlaps input
+    assert q_mx(scales=CODES + 16) == B.EINVAL       # outputs overlap
+    # empty operands are valid and enqueue nothing
+    assert q_mx(rows=0) == B.OK
+    assert q_mx(axis=1, rows=0) == B.OK
+
+
+def test_hadamard_status_codes():
+    f = L.fp4_hadamard32_quantize
+    assert f(X, 64, 64, 64, 1, 0xFFFF, 0, 0, 0, CODES, SCALES, 1, None) == B.EINVAL
+    assert f(X, 40, 64, 64, 1, 0xFFFF, 0, 0, 0, CODES, SCALES, 0, None) == B.ESHAPE
+    assert f(X, 0, 64, 64, 1, 0xFFFF, 0, 0, 0, CODES, SCALES, 0, None) == B.OK
+
+
+def q_nv(rows=64, cols=64, ld=64, axis=0, dom=0, ts=TS, ws=WS, wbytes=None, x=X):
+    if wbytes is None:
+        wbytes = L.fp4q_nv_workspace_bytes(rows, cols, axis, dom)
+    return L.fp4_quantize_nv(x, rows, cols, ld, axis, 0, 0, 0, dom, CODES, SCALES, ts, ws, wbytes, 0, None)
+
+
+def test_quantize_nv_status_codes():
+    assert L.fp4q_nv_workspace_bytes(64, 64, 0, 0) > 0
+    assert L.fp4q_nv_workspace_bytes(64, 64, 0, 1) == 0
+    assert q_nv(dom=2) == B.EINVAL
+    assert q_nv(axis=1) == B.EUNSUPPORTED
+    assert q_nv(cols=40, ld=48) == B.ESHAPE
+    assert q_nv(ts=None) == B.EINVAL
+    assert q_nv(ws=None) == B.EINVAL
+    assert q_nv(wbytes=4) == B.EINVAL
+    assert q_nv(ts=TS + 2) == B.EALIGN
+    assert q_nv(ws=X) == B.EINVAL                    # workspace overlaps input
+    assert q_nv(dom=1, ws=None, wbytes=0, rows=0) == B.OK
+
+
+def g_mx(M=256, N=256, K=256, layout=0, ctype=0, ldc=None, c=C, a_codes=CODES, a_scales=SCALES):
+    ldc = N if ldc is None else ldc
+    return L.fp4_gemm_mx(a_codes, a_scales, 0x7F6000000000, 0x7F7000000000, M, N, K, 1.0, layout, c, ctype, ldc,
+                         None)
+
+
+def test_gemm_mx_status_codes():
+    assert g_mx(layout=1) == B.EINVAL
+    assert g_mx(ctype=3) == B.EINVAL
+    assert g_mx(c=None) == B.EINVAL
+    assert g_mx(a_codes=None) == B.EINVAL
+    assert g_mx(K=96) == B.ESHAPE
+    assert g_mx(ldc=100) == B.ESHAPE
+    assert g_mx(M=-3) == B.ESHAPE
+    assert g_mx(a_codes=CODES + 8) == B.EALIGN
+    assert g_mx(a_scales=SCALES + 2) == B.EALIGN
+    assert g_mx(c=C + 2) == B.EALIGN
+    assert g_mx(c=CODES) == B.EINVAL                 # C overlaps A codes
+    assert g_mx(M=0) == B.OK and g_mx(N=0) == B.OK
+
+
+def test_gemm_nv_status_codes():
+    f = L.fp4_gemm_nv
+    args = (CODES, SCALES, TS, 0x7F6000000000, 0x7F7000000000, 0x7F8000000000)
+    assert f(*args, 2, 256, 256, 256, 1.0, 0, C, 0, 256, None) == B.EINVAL
+    assert f(*args, 0, 256, 256, 200, 1.0, 0, C, 0, 256, None) == B.ESHAPE
+    assert f(CODES, SCALES, None, 0x7F6000000000, 0x7F7000000000, 0x7F8000000000, 1, 256, 256, 256, 1.0, 0, C, 0,
+             256, None) == B.EINVAL
+    assert f(*args, 1, 256, 256, 256, 1.0, 0, TS, 0, 256, None) == B.EINVAL  # C overlaps a tensor scale
+    assert f(*args, 0, 0, 256, 256, 1.0, 0, C, 0, 256, None) == B.OK
+
+
+def test_binding_has_no_cpu_fallback(monkeypatch, tmp_path):
+    # the binding refuses to run when the library is absent
+    monkeypatch.setattr(B, "_lib", None)
+    monkeypatch.setattr(B, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(FileNotFoundError):
+        B.lib()

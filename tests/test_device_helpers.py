@@ -1,0 +1,124 @@
+"""The GPU kernels' scalar building blocks (csrc/fp4q_device.h), compiled for
+the host, against the oracle over large input sets.  CPU only: this runs the
+kernels' own code, not the oracle's, on the CPU."""
+import ctypes
+import os
+import shutil
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle
+from tests import second_formulation as sf
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(os.path.dirname(HERE), "fp4_block_scaled_quantizer_amd", "csrc")
+
+
+@pytest.fixture(scope="module")
+def H(tmp_path_factory):
+    hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(hipcc):
+        pytest.skip("hipcc not available")
+    so = str(tmp_path_factory.mktemp("devh") / "devh.so")
+    subprocess.run([hipcc, "--offload-arch=gfx950", "-O2", "-std=c++17", "-ffp-contract=off", "-fPIC", "-shared",
+                    "-I", CSRC, os.path.join(HERE, "helpers", "device_helpers_host.cpp"), "-o", so],
+                   check=True, capture_output=True)
+    L = ctypes.CDLL(so)
+    f32, u32 = ctypes.c_float, ctypes.c_uint32
+    for name, res, args in [("h_e2m1_sr", u32, [f32, u32]), ("h_e4m3_rne_satfinite", u32, [f32]),
+                            ("h_e4m3_value", f32, [u32]), ("h_nv_block_scale", u32, [f32, f32]),
+                            ("h_nv_inv_decode", f32, [u32, f32]), ("h_nv_tensor_scale", f32, [f32]),
+                            ("h_mx_scale_byte", u32, [u32]), ("h_mx_inv_scale", f32, [u32]),
+                            ("h_f32_to_bf16_rne", u32, [f32])]:
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
+    L.h_philox.argtypes = [u32] * 6 + [ctypes.POINTER(u32)]
+    L.h_e4m3_batch.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t]
+    L.h_e2m1_sr_batch.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t]
+    return L
+
+
+def e4m3_inputs():
+    t = np.array([oracle.e4m3_value(c) for c in range(0x7F)])
+    mids = (t[:-1] + t[1:]) / 2
+    pts = np.concatenate([t, mids]).astype(np.float32)
+    near = np.concatenate([np.nextafter(pts, np.float32(0)), np.nextafter(pts, np.float32(1e9)), pts])
+    rng = np.random.default_rng(0)
+    rnd = np.exp(rng.uniform(np.log(1e-6), np.log(600), 200000)).astype(np.float32)
+    tiny = np.array([0, 2.0 ** -10, 2.0 ** -10 * 1.0001, 2.0 ** -149, 1e-30, 448, 463.9, 464, 1e30], np.float32)
+    return np.concatenate([near, rnd, tiny]).astype(np.float32)
+
+
+def test_e4m3_encode_matches_oracle(H):
+    z = e4m3_inputs()
+    got = np.zeros(z.size, dtype=np.uint8)
+    H.h_e4m3_batch(z.ctypes.data, got.ctypes.data, z.size)
+    lib = oracle._load()
+    want = np.fromiter((lib.oc_e4m3_rne_satfinite(float(v)) for v in z), dtype=np.uint8, count=z.size)
+    assert np.array_equal(got, want)
+    for c in range(0x7F):
+        assert H.h_e4m3_value(c) == np.float32(oracle.e4m3_value(c))
+
+
+def test_e2m1_sr_matches_oracle(H):
+    rng = np.random.default_rng(1)
+    bits = rng.integers(0, 65536, 300000).astype(np.uint16)
+    f = sf.bf16_to_f32(bits)
+    e = rng.integers(-3, 4, f.size)
+    with np.errstate(all="ignore"):
+        y = (f * np.float32(2.0) ** e.astype(np.float32)).astype(np.float32)
+    y = y[np.isfinite(y)]
+    y = np.concatenate([y, np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5, 6, -6, 4, 2, 0.5, 7.9, 1e-40], np.float32)])
+    r = rng.integers(0, 65536, y.size).astype(np.uint32)
+    r[-14:] = [0, 65535, 32768, 32767, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10]
+    got = np.zeros(y.size, dtype=np.uint8)
+    H.h_e2m1_sr_batch(y.ctypes.data, r.ctypes.data, got.ctypes.data, y.size)
+    lib = oracle._load()
+    want = np.fromiter((lib.oc_e2m1_sr(float(a), int(b)) for a, b in zip(y, r)), dtype=np.uint8, count=y.size)
+    assert np.array_equal(got, want)
+
+
+def test_mx_scale_byte_matches_oracle(H):
+    for b in range(0x8000):  # every non-negative bf16 magnitude as a block amax
+        a = float(sf.bf16_to_f32(np.array([b], np.uint16))[0])
+        if not np.isfinite(a):
+            continue
+        want = oracle.mx_shared_exponent(a) + 127
+        assert H.h_mx_scale_byte(b << 16) == want, hex(b)
+        # the power of two the kernel multiplies by is 2^-E
+        assert H.h_mx_inv_scale(want) == np.float32(2.0 ** -(want - 127))
+
+
+def test_nv_scales_match_oracle(H):
+    rng = np.random.default_rng(2)
+    for _ in range(20000):
+        A = float(np.float32(np.exp(rng.uniform(np.log(1e-20), np.log(1e30)))))
+        b = float(np.float32(A * rng.choice([1.0, rng.uniform(0, 1), rng.uniform(0, 1e-4), 0.0])))
+        S = oracle.nv_tensor_scale(A)
+        assert H.h_nv_tensor_scale(A) == np.float32(S)
+        sb = oracle.nv_block_scale(b, S)
+        assert H.h_nv_block_scale(b, S) == sb
+        d = np.float32(np.float32(oracle.e4m3_value(sb)) * np.float32(S))
+        assert H.h_nv_inv_decode(sb, S) == np.float32(np.float32(1.0) / d)
+    assert H.h_nv_tensor_scale(0.0) == 1.0
+
+
+def test_philox_matches_oracle(H):
+    rng = np.random.default_rng(3)
+    out = (ctypes.c_uint32 * 4)()
+    for _ in range(2000):
+        c = [int(v) for v in rng.integers(0, 2**32, 4)]
+        k = [int(v) for v in rng.integers(0, 2**32, 2)]
+        H.h_philox(*c, *k, out)
+        assert list(out) == oracle.philox4x32_10(c, k)
+
+
+def test_bf16_rne_output_conversion(H):
+    rng = np.random.default_rng(4)
+    v = (rng.standard_normal(100000) * 10.0 ** rng.integers(-30, 30, 100000)).astype(np.float32)
+    want = sf.f32_to_bf16_bits_rne(v)
+    got = np.array([H.h_f32_to_bf16_rne(float(x)) for x in v], dtype=np.uint16)
+    assert np.array_equal(got, want)

@@ -1,0 +1,208 @@
+"""GPU parity of the quantization producers against the CPU oracle: codes,
+scale bytes and FP32 tensor scales must be identical byte for byte, for RNE
+and for stochastic rounding at a fixed seed, on small ragged shapes and on the
+full Llama-3-8B operand sizes the benchmark uses."""
+import numpy as np
+import pytest
+import torch
+
+from tests.gpu_common import B, announce, assert_bytes_equal, device, np_u8, oracle, synth, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def special_values(rows, cols, seed):
+    """bf16 with zeros blocks, subnormals, exact ties after scaling, huge values."""
+    rng = np.random.default_rng(seed)
+    x = synth.bf16_bits(synth.activation(rows, cols, seed)).copy()
+    flat = x.reshape(-1)
+    n = flat.size
+    picks = rng.integers(0, n, n // 4)
+    specials = np.array([0x0000, 0x8000, 0x0001, 0x8001, 0x007F, 0x3E80, 0x3F40, 0x3FA0, 0x3FE0, 0x4020, 0x4060,
+                         0x40A0, 0x40C0, 0x40E0, 0x7F7F, 0xFF7F, 0x0080, 0xBE80], dtype=np.uint16)
+    flat[picks] = specials[rng.integers(0, specials.size, picks.size)]
+    if cols >= 64 and rows >= 2:
+        x[1, :32] = 0          # an all-zero block
+        x[0, 32:64] = 0x0001   # a subnormal-only block
+    return x
+
+
+MX_SHAPES = [(1, 32, None), (3, 64, None), (37, 96, None), (256, 256, None), (50, 96, 136), (129, 4096, None)]
+
+
+@pytest.mark.parametrize("rows,cols,ld", MX_SHAPES)
+@pytest.mark.parametrize("sr", [False, True])
+@pytest.mark.parametrize("dist", ["act", "special"])
+def test_mx_rows_small(rows, cols, ld, sr, dist):
+    dev = device()
+    announce(f"mx rows {rows}x{cols} ld={ld} sr={sr} {dist}")
+    xb = synth.bf16_bits(synth.activation(rows, cols, 3)) if dist == "act" else special_values(rows, cols, 4)
+    x = to_dev(synth.from_bf16_bits(xb), dev, ld)
+    codes, scales = B.fp4_quantize_mx(x, round=B.SR if sr else B.RNE, seed=7, stream_id=3)
+    torch.cuda.synchronize()
+    oc, os_ = oracle.quantize_mx(xb, sr=sr, seed=7, stream=3)
+    assert_bytes_equal(np_u8(scales), os_, "scales")
+    assert_bytes_equal(np_u8(codes), oc, "codes")
+
+
+COL_SHAPES = [(32, 4, 8), (64, 40, None), (96, 260, 264), (256, 256, 264), (128, 1028, 1032)]
+
+
+@pytest.mark.parametrize("rows,cols,ld", COL_SHAPES)
+@pytest.mark.parametrize("sr", [False, True])
+@pytest.mark.parametrize("had", [False, True])
+def test_mx_cols_small(rows, cols, ld, sr, had):
+    dev = device()
+    announce(f"mx cols {rows}x{cols} ld={ld} sr={sr} hadamard={had}")
+    xb = special_values(rows, cols, 5) if not had else synth.bf16_bits(synth.grad_student_t3(rows, cols, 6))
+    x = to_dev(synth.from_bf16_bits(xb), dev, ld)
+    mask = synth.sign_mask(7)
+    rnd = B.SR if sr else B.RNE
+    if had:
+        codes, scales = B.fp4_hadamard32_quantize(x, mask, axis=B.ALONG_COLS, round=rnd, seed=7, stream_id=1)
+        oc, os_ = oracle.hadamard32_quantize(xb, mask, axis=oracle.AXIS_COLS, sr=sr, seed=7, stream=1)
+    else:
+        codes, scales = B.fp4_quantize_mx(x, axis=B.ALONG_COLS, round=rnd, seed=7, stream_id=1)
+        oc, os_ = oracle.quantize_mx(xb, axis=oracle.AXIS_COLS, sr=sr, seed=7, stream=1)
+    torch.cuda.synchronize()
+    assert_bytes_equal(np_u8(scales), os_, "scales")
+    assert_bytes_equal(np_u8(codes), oc, "codes")
+
+
+@pytest.mark.parametrize("rows,cols", [(1, 32), (5, 64), (64, 512)])
+@pytest.mark.parametrize("sr", [False, True])
+def test_hadamard_rows_small(rows, cols, sr):
+    dev = device()
+    announce(f"hadamard rows {rows}x{cols} sr={sr}")
+    xb = synth.bf16_bits(synth.grad_student_t3(rows, cols, 8))
+    for mask in (0, 0xFFFFFFFF, synth.sign_mask(7)):
+        codes, scales = B.fp4_hadamard32_quantize(synth.from_bf16_bits(xb).to(dev), mask, axis=B.ALONG_ROWS,
+                                                  round=B.SR if sr else B.RNE, seed=9, stream_id=0)
+        torch.cuda.synchronize()
+        oc, os_ = oracle.hadamard32_quantize(xb, mask, axis=oracle.AXIS_ROWS, sr=sr, seed=9, stream=0)
+        assert_bytes_equal(np_u8(scales), os_, f"scales mask={mask:#x}")
+        assert_bytes_equal(np_u8(codes), oc, f"codes mask={mask:#x}")
+
+
+NV_SHAPES = [(1, 16, None), (3, 48, None), (130, 144, None), (300, 400, 416), (256, 256, None)]
+
+
+@pytest.mark.parametrize("rows,cols,ld", NV_SHAPES)
+@pytest.mark.parametrize("domain", [0, 1])
+@pytest.mark.parametrize("sr", [False, True])
+def test_nv_small(rows, cols, ld, domain, sr):
+    dev = device()
+    announce(f"nv {rows}x{cols} ld={ld} domain={domain} sr={sr}")
+    xb = synth.bf16_bits(synth.activation(rows, cols, 10))
+    x = to_dev(synth.from_bf16_bits(xb), dev, ld)
+    codes, scales, ts = B.fp4_quantize_nv(x, domain, round=B.SR if sr else B.RNE, seed=7, stream_id=2)
+    torch.cuda.synchronize()
+    oc, os_, ots = oracle.quantize_nv(xb, sr=sr, seed=7, stream=2, domain=domain)
+    assert_bytes_equal(ts.cpu().numpy().view(np.uint32), ots.view(np.uint32), "tensor scales")
+    assert_bytes_equal(np_u8(scales), os_, "block scales")
+    assert_bytes_equal(np_u8(codes), oc, "codes")
+
+
+def test_nv_zero_tile_and_empty():
+    dev = device()
+    announce("nv zero tile / empty operand")
+    xb = synth.bf16_bits(synth.activation(256, 256, 11)).copy()
+    xb[:128, 128:] = 0
+    for domain in (0, 1):
+        codes, scales, ts = B.fp4_quantize_nv(synth.from_bf16_bits(xb).to(dev), domain)
+        torch.cuda.synchronize()
+        oc, os_, ots = oracle.quantize_nv(xb, domain=domain)
+        assert_bytes_equal(ts.cpu().numpy().view(np.uint32), ots.view(np.uint32), "tensor scales")
+        assert_bytes_equal(np_u8(scales), os_, "block scales")
+        assert_bytes_equal(np_u8(codes), oc, "codes")
+    # an empty operand still gets its global tensor scale (1.0)
+    empty = torch.zeros((0, 64), dtype=torch.bfloat16, device=dev)
+    _, _, ts = B.fp4_quantize_nv(empty, B.NV_GLOBAL)
+    torch.cuda.synchronize()
+    assert ts.item() == 1.0
+
+
+def test_outputs_written_exactly_guard_bytes():
+    # poison the outputs and a 4 KiB tail: every logical byte is overwritten, the tail is untouched
+    dev = device()
+    announce("guard bytes")
+    rows, cols = 40, 96
+    xb = synth.bf16_bits(synth.activation(rows, cols, 12))
+    x = synth.from_bf16_bits(xb).to(dev)
+    nbytes_c, nbytes_s = rows * cols // 2, rows * cols // 32
+    cbuf = torch.full((nbytes_c + 4096,), 0xA5, dtype=torch.uint8, device=dev)
+    sbuf = torch.full((nbytes_s + 4096,), 0xA5, dtype=torch.uint8, device=dev)
+    codes = cbuf[:nbytes_c].view(rows, cols // 2)
+    scales = sbuf[:nbytes_s].view(rows, cols // 32)
+    B.fp4_quantize_mx(x, codes=codes, scales=scales)
+    torch.cuda.synchronize()
+    oc, os_ = oracle.quantize_mx(xb)
+    assert_bytes_equal(np_u8(codes), oc, "codes")
+    assert_bytes_equal(np_u8(scales), os_, "scales")
+    assert np.all(np_u8(cbuf[nbytes_c:]) == 0xA5) and np.all(np_u8(sbuf[nbytes_s:]) == 0xA5)
+
+
+def test_repeat_is_deterministic():
+    dev = device()
+    announce("determinism")
+    x = synth.grad_student_t3(512, 1024, 13).to(dev)
+    a = B.fp4_quantize_mx(x, round=B.SR, seed=7)
+    b = B.fp4_quantize_mx(x, round=B.SR, seed=7)
+    c = B.fp4_hadamard32_quantize(x, 0x1234, round=B.SR, seed=7)
+    d = B.fp4_hadamard32_quantize(x, 0x1234, round=B.SR, seed=7)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+    assert torch.equal(c[0], d[0]) and torch.equal(c[1], d[1])
+
+
+# ------------------------------------------------------------------ full sizes
+
+FULL = [
+    ("qkv", "X", "rows", False, False),
+    ("qkv", "W", "rows", False, False),
+    ("mlp_gate_up", "W", "rows", False, False),
+    ("mlp_down", "H", "rows", False, False),
+    ("mlp_down", "W", "rows", False, False),
+    ("backward", "dY", "rows", True, False),      # dgrad A: SR along rows
+    ("backward", "W", "cols", False, False),      # dgrad B: W^T, transpose-quantize
+    ("backward", "dY", "cols", True, True),       # wgrad A: Hadamard + SR along tokens
+    ("backward", "X", "cols", False, True),       # wgrad B: Hadamard along tokens
+]
+
+
+@pytest.mark.parametrize("cfg,role,axis,sr,had", FULL)
+def test_mx_full_size(cfg, role, axis, sr, had):
+    dev = device()
+    announce(f"full {cfg}.{role} axis={axis} sr={sr} hadamard={had}")
+    xt = synth.config_tensor(cfg, role)
+    xb = synth.bf16_bits(xt)
+    x = xt.to(dev)
+    ax = B.ALONG_ROWS if axis == "rows" else B.ALONG_COLS
+    stream = 0 if axis == "rows" else 1
+    mask = synth.sign_mask(synth.HADAMARD_MASK_SEED)
+    if had:
+        codes, scales = B.fp4_hadamard32_quantize(x, mask, axis=ax, round=B.SR if sr else B.RNE,
+                                                  seed=synth.SR_SEED, stream_id=stream)
+        oc, os_ = oracle.hadamard32_quantize(xb, mask, axis=ax, sr=sr, seed=synth.SR_SEED, stream=stream)
+    else:
+        codes, scales = B.fp4_quantize_mx(x, axis=ax, round=B.SR if sr else B.RNE, seed=synth.SR_SEED,
+                                          stream_id=stream)
+        oc, os_ = oracle.quantize_mx(xb, axis=ax, sr=sr, seed=synth.SR_SEED, stream=stream)
+    torch.cuda.synchronize()
+    assert_bytes_equal(np_u8(scales), os_, "scales")
+    assert_bytes_equal(np_u8(codes), oc, "codes")
+
+
+@pytest.mark.parametrize("role", ["X", "W"])
+@pytest.mark.parametrize("domain", [0, 1])
+def test_nv_full_size(role, domain):
+    dev = device()
+    announce(f"full nvfp4.{role} domain={domain}")
+    xt = synth.config_tensor("nvfp4", role)
+    xb = synth.bf16_bits(xt)
+    codes, scales, ts = B.fp4_quantize_nv(xt.to(dev), domain)
+    torch.cuda.synchronize()
+    oc, os_, ots = oracle.quantize_nv(xb, domain=domain)
+    assert_bytes_equal(ts.cpu().numpy().view(np.uint32), ots.view(np.uint32), "tensor scales")
+    assert_bytes_equal(np_u8(scales), os_, "block scales")
+    assert_bytes_equal(np_u8(codes), oc, "codes")
