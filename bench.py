@@ -1,0 +1,354 @@
+#!/usr/bin/env python3
+"""Benchmark of the FP4 hot path on one MI355X.
+
+A step is one pass of the path over one batch of synthetic Llama-3-8B-shaped
+operands: quantize the activation, quantize the weight (both re-quantized every
+step, as in training where weights change), then the block-scaled FP4 GEMM.
+The default workload is the QKV projection forward (MXFP4, RNE):
+X bf16 8192x4096, W bf16 6144x4096, C = X W^T bf16 8192x6144.
+
+Prints one JSON line.  `value` is quantize+GEMM TFLOP/s = 2MNK / (time per
+step), with inputs resident in HBM (several input copies are rotated so the
+producers read from HBM, not from the 256 MB Infinity Cache).  `roofline`
+describes the dominant kernel (average launch duration from HIP events on the
+launch stream inside the timed region); `kernels` lists every kernel of the
+step; `cpu_baseline` times the CPU oracle on one full step on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+FP4_PEAK_TFLOPS = 10100.0    # dense MFMA, fp4/fp6
+BF16_PEAK_TFLOPS = 2500.0    # dense MFMA, bf16
+
+# algorithmic bytes per element (payload + block scales + tensor scales, logical rows)
+MX_BYTES_PER_ELEM = 2 + 0.5 + 1 / 32
+NV_TILE_BYTES_PER_ELEM = 2 + 0.5 + 1 / 16 + 4 / (128 * 128)
+NV_GLOBAL_BYTES_PER_ELEM = 2 + 2 + 0.5 + 1 / 16   # includes the amax pre-pass read
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="qkv", choices=["qkv", "mlp", "backward", "nvfp4_global", "nvfp4_tile"])
+    ap.add_argument("--copies", type=int, default=4, help="input copies rotated across steps (cold producers)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def build_workload(name, dev, copies):
+    """Returns (config dict, list of ops, flops per step).  An op is
+    (label, kernel, launch(step), amount, unit, peak, bound)."""
+    import torch
+
+    from fp4_block_scaled_quantizer_amd import binding as B
+    from fp4_block_scaled_quantizer_amd import synth
+
+    def gen(cfg, role, extra_copies):
+        base = synth.config_tensor(cfg, role).to(dev)
+        out = [base]
+        for i in range(1, extra_copies):
+            # distinct buffers with the same distribution: a cheap bit-level
+            # perturbation (sign flip of alternate copies) keeps amax patterns
+            out.append(base.neg() if i % 2 else base.clone())
+        return out
+
+    ops = []
+    if name == "qkv":
+        X = gen("qkv", "X", copies)
+        W = gen("qkv", "W", copies)
+        M, K = X[0].shape
+        N = W[0].shape[0]
+        cx = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
+        sx = torch.empty((M, K // 32), dtype=torch.uint8, device=dev)
+        cw = torch.empty((N, K // 2), dtype=torch.uint8, device=dev)
+        sw = torch.empty((N, K // 32), dtype=torch.uint8, device=dev)
+        C = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        ops = [
+            ("quantize X (MXFP4, RNE)", "quant_mx_rows_kernel",
+             lambda s: B.fp4_quantize_mx(X[s % copies], codes=cx, scales=sx),
+             M * K * MX_BYTES_PER_ELEM, "GB/s", HBM_PEAK_GBS, "hbm"),
+            ("quantize W (MXFP4, RNE)", "quant_mx_rows_kernel",
+             lambda s: B.fp4_quantize_mx(W[s % copies], codes=cw, scales=sw),
+             N * K * MX_BYTES_PER_ELEM, "GB/s", HBM_PEAK_GBS, "hbm"),
+            ("GEMM MXFP4 X W^T -> bf16", "gemm_mx_kernel",
+             lambda s: B.fp4_gemm_mx(cx, sx, cw, sw, c=C),
+             2.0 * M * N * K, "TFLOP/s", FP4_PEAK_TFLOPS, "mfma"),
+        ]
+        cfg = {"workload": "Llama-3-8B QKV forward, MXFP4 RNE", "X": [M, K], "W": [N, K], "gemm_mnk": [M, N, K],
+               "out": "bf16", "global_batch_tokens": M, "input_copies": copies}
+        return cfg, ops, 2.0 * M * N * K
+    if name == "mlp":
+        X = gen("mlp_gate_up", "X", copies)
+        Wg = gen("mlp_gate_up", "W", copies)
+        H = gen("mlp_down", "H", copies)
+        Wd = gen("mlp_down", "W", copies)
+        M, K1 = X[0].shape
+        N1 = Wg[0].shape[0]
+        K2 = H[0].shape[1]
+        N2 = Wd[0].shape[0]
+        bufs = {}
+
+        def q(tag, src, R, K):
+            bufs[tag] = (torch.empty((R, K // 2), dtype=torch.uint8, device=dev),
+                         torch.empty((R, K // 32), dtype=torch.uint8, device=dev))
+            return lambda s: B.fp4_quantize_mx(src[s % copies], codes=bufs[tag][0], scales=bufs[tag][1])
+
+        C1 = torch.empty((M, N1), dtype=torch.bfloat16, device=dev)
+        C2 = torch.empty((M, N2), dtype=torch.bfloat16, device=dev)
+        ops = [
+            ("quantize X", "quant_mx_rows_kernel", q("x", X, M, K1), M * K1 * MX_BYTES_PER_ELEM, "GB/s",
+             HBM_PEAK_GBS, "hbm"),
+            ("quantize W_gate_up", "quant_mx_rows_kernel", q("wg", Wg, N1, K1), N1 * K1 * MX_BYTES_PER_ELEM, "GB/s",
+             HBM_PEAK_GBS, "hbm"),
+            ("GEMM gate/up", "gemm_mx_kernel", lambda s: B.fp4_gemm_mx(*bufs["x"], *bufs["wg"], c=C1),
+             2.0 * M * N1 * K1, "TFLOP/s", FP4_PEAK_TFLOPS, "mfma"),
+            ("quantize H", "quant_mx_rows_kernel", q("h", H, M, K2), M * K2 * MX_BYTES_PER_ELEM, "GB/s",
+             HBM_PEAK_GBS, "hbm"),
+            ("quantize W_down", "quant_mx_rows_kernel", q("wd", Wd, N2, K2), N2 * K2 * MX_BYTES_PER_ELEM, "GB/s",
+             HBM_PEAK_GBS, "hbm"),
+            ("GEMM down", "gemm_mx_kernel", lambda s: B.fp4_gemm_mx(*bufs["h"], *bufs["wd"], c=C2),
+             2.0 * M * N2 * K2, "TFLOP/s", FP4_PEAK_TFLOPS, "mfma"),
+        ]
+        cfg = {"workload": "Llama-3-8B MLP forward (gate/up + down), MXFP4 RNE",
+               "gemms_mnk": [[M, N1, K1], [M, N2, K2]], "out": "bf16", "input_copies": copies}
+        return cfg, ops, 2.0 * M * N1 * K1 + 2.0 * M * N2 * K2
+    if name == "backward":
+        dY = gen("backward", "dY", copies)
+        W = gen("backward", "W", copies)
+        X = gen("backward", "X", copies)
+        T, O = dY[0].shape
+        I = W[0].shape[1]
+        mask = synth.sign_mask(synth.HADAMARD_MASK_SEED)
+        bufs = {}
+
+        def alloc(tag, R, K):
+            bufs[tag] = (torch.empty((R, K // 2), dtype=torch.uint8, device=dev),
+                         torch.empty((R, K // 32), dtype=torch.uint8, device=dev))
+
+        alloc("dy_r", T, O)
+        alloc("wt", I, O)
+        alloc("dy_c", O, T)
+        alloc("x_c", I, T)
+        dX = torch.empty((T, I), dtype=torch.bfloat16, device=dev)
+        dW = torch.empty((O, I), dtype=torch.float32, device=dev)
+        seed = synth.SR_SEED
+        ops = [
+            ("quantize dY rows (SR)", "quant_mx_rows_kernel",
+             lambda s: B.fp4_quantize_mx(dY[s % copies], round=B.SR, seed=seed, stream_id=0, codes=bufs["dy_r"][0],
+                                         scales=bufs["dy_r"][1]), T * O * MX_BYTES_PER_ELEM, "GB/s", HBM_PEAK_GBS,
+             "hbm"),
+            ("quantize W^T (cols)", "quant_mx_cols_kernel",
+             lambda s: B.fp4_quantize_mx(W[s % copies], axis=B.ALONG_COLS, codes=bufs["wt"][0],
+                                         scales=bufs["wt"][1]), O * I * MX_BYTES_PER_ELEM, "GB/s", HBM_PEAK_GBS,
+             "hbm"),
+            ("GEMM dgrad dY W", "gemm_mx_kernel", lambda s: B.fp4_gemm_mx(*bufs["dy_r"], *bufs["wt"], c=dX),
+             2.0 * T * I * O, "TFLOP/s", FP4_PEAK_TFLOPS, "mfma"),
+            ("Hadamard-quantize dY^T (SR)", "quant_mx_cols_kernel",
+             lambda s: B.fp4_hadamard32_quantize(dY[s % copies], mask, axis=B.ALONG_COLS, round=B.SR, seed=seed,
+                                                 stream_id=1, codes=bufs["dy_c"][0], scales=bufs["dy_c"][1]),
+             T * O * MX_BYTES_PER_ELEM, "GB/s", HBM_PEAK_GBS, "hbm"),
+            ("Hadamard-quantize X^T", "quant_mx_cols_kernel",
+             lambda s: B.fp4_hadamard32_quantize(X[s % copies], mask, axis=B.ALONG_COLS, codes=bufs["x_c"][0],
+                                                 scales=bufs["x_c"][1]), T * I * MX_BYTES_PER_ELEM, "GB/s",
+             HBM_PEAK_GBS, "hbm"),
+            ("GEMM wgrad dY^T X (alpha 1/32)", "gemm_mx_kernel",
+             lambda s: B.fp4_gemm_mx(*bufs["dy_c"], *bufs["x_c"], alpha=1.0 / 32, c=dW),
+             2.0 * O * I * T, "TFLOP/s", FP4_PEAK_TFLOPS, "mfma"),
+        ]
+        cfg = {"workload": "Llama-3-8B o_proj backward, MXFP4: SR on dY, fixed-sign Hadamard-32 on wgrad",
+               "dgrad_mnk": [T, I, O], "wgrad_mnk": [O, I, T], "input_copies": copies}
+        return cfg, ops, 2.0 * T * I * O * 2
+    # NVFP4
+    domain = B.NV_GLOBAL if name == "nvfp4_global" else B.NV_TILE128
+    X = gen("nvfp4", "X", copies)
+    W = gen("nvfp4", "W", copies)
+    M, K = X[0].shape
+    N = W[0].shape[0]
+    bufs = {}
+
+    def qnv(tag, src, R):
+        ts_shape = B.nv_tensor_scale_shape(R, K, domain)
+        bufs[tag] = (torch.empty((R, K // 2), dtype=torch.uint8, device=dev),
+                     torch.empty((R, K // 16), dtype=torch.uint8, device=dev),
+                     torch.empty(ts_shape, dtype=torch.float32, device=dev),
+                     torch.empty((max(1, B.fp4q_nv_workspace_bytes(R, K, 0, domain)),), dtype=torch.uint8,
+                                 device=dev))
+        b = bufs[tag]
+        return lambda s: B.fp4_quantize_nv(src[s % copies], domain, codes=b[0], scales=b[1], tensor_scale=b[2],
+                                           workspace=b[3] if domain == B.NV_GLOBAL else None)
+
+    C = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    bpe = NV_GLOBAL_BYTES_PER_ELEM if domain == B.NV_GLOBAL else NV_TILE_BYTES_PER_ELEM
+    kname = "nv_quant_global (amax + quantize)" if domain == B.NV_GLOBAL else "nv_quant_tile_kernel"
+    ops = [
+        ("quantize X (NVFP4)", kname, qnv("x", X, M), M * K * bpe, "GB/s", HBM_PEAK_GBS, "hbm"),
+        ("quantize W (NVFP4)", kname, qnv("w", W, N), N * K * bpe, "GB/s", HBM_PEAK_GBS, "hbm"),
+        ("GEMM NVFP4 (bf16 MFMA)", "gemm_nv_kernel",
+         lambda s: B.fp4_gemm_nv(bufs["x"][0], bufs["x"][1], bufs["x"][2], bufs["w"][0], bufs["w"][1], bufs["w"][2],
+                                 domain, c=C), 2.0 * M * N * K, "TFLOP/s", BF16_PEAK_TFLOPS, "mfma"),
+    ]
+    cfg = {"workload": f"NVFP4 {'global' if domain == B.NV_GLOBAL else 'per-128x128-tile'} tensor scale",
+           "gemm_mnk": [M, N, K], "out": "bf16", "input_copies": copies}
+    return cfg, ops, 2.0 * M * N * K
+
+
+def read_traffic(kernel, workload):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, if one
+    exists for this kernel and workload and still matches the kernel source."""
+    import hashlib
+
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_pmc.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if "=" in line and not line.lstrip().startswith("#"):
+                k, v = line.split("=", 1)
+                vals[k.strip()] = v.strip()
+    src = vals.get("source")
+    if not src or "traffic_bytes" not in vals:
+        return None
+    h = hashlib.sha256(open(os.path.join(ROOT, src), "rb").read()).hexdigest()[:16]
+    if h != vals.get("source_sha256_16"):
+        return None  # kernel changed since the counters were taken
+    return float(vals["traffic_bytes"])
+
+
+def cpu_baseline(workload):
+    """The oracle, as it stands, on one full step of the qkv workload."""
+    if workload != "qkv":
+        return None
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import oracle
+    from fp4_block_scaled_quantizer_amd import synth
+
+    x = synth.bf16_bits(synth.config_tensor("qkv", "X"))
+    w = synth.bf16_bits(synth.config_tensor("qkv", "W"))
+    M, K = x.shape
+    N = w.shape[0]
+    t0 = time.perf_counter()
+    cx, sx = oracle.quantize_mx(x)
+    cw, sw = oracle.quantize_mx(w)
+    C, W = oracle.gemm_ref(oracle.dequant_mx(cx, sx), oracle.dequant_mx(cw, sw))
+    dt = time.perf_counter() - t0
+    del C, W
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {"value": 2.0 * M * N * K / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "seconds": round(dt, 3),
+            "sample": f"one full step: oracle.quantize_mx of X {M}x{K} and W {N}x{K} (single-threaded C), "
+                      f"dequantize, float64 numpy matmul for C and sum|ab| ({threads} BLAS threads)",
+            "host_cpu": platform.processor() or platform.machine(), "host_nproc": os.cpu_count()}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU: --gpus {args.gpus} / WORLD_SIZE {world} is not supported "
+              "(this build runs the FP4 producer and GEMM on a single MI355X)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    cfg, ops, step_flops = build_workload(args.workload, dev, args.copies)
+    stream = torch.cuda.current_stream()
+
+    for s in range(args.warmup):
+        for op in ops:
+            op[2](s)
+    torch.cuda.synchronize()
+
+    nops = len(ops)
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nops)]
+          for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for s in range(args.steps):
+        for i, op in enumerate(ops):
+            ev[s][i][0].record(stream)
+            op[2](s)
+            ev[s][i][1].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    gpu_ms = t_start.elapsed_time(t_end)
+    ms_per_step = gpu_ms / args.steps
+
+    # Per-launch events carry a few microseconds of their own, which matters
+    # for the short producers: each op is also timed as a batch of
+    # back-to-back launches (outside the timed region) and reported as
+    # avg_us_batched; `achieved` uses the in-step events for ops longer than
+    # 100 us and the batched figure otherwise.
+    batch = 20
+    batched_ms = []
+    for i, op in enumerate(ops):
+        b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        b0.record(stream)
+        for r in range(batch):
+            op[2](r)
+        b1.record(stream)
+        torch.cuda.synchronize()
+        batched_ms.append(b0.elapsed_time(b1) / batch)
+
+    kernels = []
+    for i, (label, kname, _, amount, unit, peak, bound) in enumerate(ops):
+        durs = [ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(args.steps)]
+        avg_ms = sum(durs) / len(durs)
+        use_ms = avg_ms if avg_ms > 0.1 else batched_ms[i]
+        achieved = amount / (use_ms * 1e-3) / (1e9 if unit == "GB/s" else 1e12)
+        kernels.append({"op": label, "kernel": kname, "avg_us": round(avg_ms * 1e3, 2),
+                        "avg_us_batched": round(batched_ms[i] * 1e3, 2), "min_us": round(min(durs) * 1e3, 2),
+                        "achieved": round(achieved, 1), "unit": unit, "peak": peak,
+                        "frac": round(achieved / peak, 4), "bound": bound, "algorithmic": amount})
+    dom = max(range(nops), key=lambda i: kernels[i]["avg_us"])
+    dk = kernels[dom]
+    roofline = {"bound": dk["bound"], "achieved": dk["achieved"], "peak": dk["peak"], "unit": dk["unit"],
+                "frac": dk["frac"], "traffic": read_traffic(dk["kernel"], args.workload), "kernel": dk["kernel"],
+                "op": dk["op"], "avg_us": dk["avg_us"]}
+    value = step_flops / (ms_per_step * 1e-3) / 1e12
+    out = {
+        "metric": "quantize+FP4 GEMM TFLOP/s (Llama-3-8B shapes)",
+        "value": round(value, 1),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "e2m1 x e2m1 -> f32 accumulate" if "nvfp4" not in args.workload else "bf16(e2m1*e4m3) -> f32",
+        "data": "synthetic",
+        "config": cfg,
+        "roofline": roofline,
+        "kernels": kernels,
+        "wall_s_timed": round(wall, 4),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(args.workload)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
