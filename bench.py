@@ -43,11 +43,13 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="qkv", choices=["qkv", "mlp", "backward", "nvfp4_global", "nvfp4_tile"])
     ap.add_argument("--copies", type=int, default=4, help="input copies rotated across steps (cold producers)")
+    ap.add_argument("--layout", default="tiled", choices=["tiled", "linear"],
+                    help="MX operand layout between producer and GEMM (tiled = the GEMM's consumer layout)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     return ap.parse_args()
 
 
-def build_workload(name, dev, copies):
+def build_workload(name, dev, copies, layout_name="tiled"):
     """Returns (config dict, list of ops, flops per step).  An op is
     (label, kernel, launch(step), amount, unit, peak, bound)."""
     import torch
@@ -64,30 +66,35 @@ def build_workload(name, dev, copies):
             out.append(base.neg() if i % 2 else base.clone())
         return out
 
+    L = B.LAYOUT_TILED if layout_name == "tiled" else B.LAYOUT_LINEAR
+
+    def mx_bufs(R, K):
+        cs, ss = B.mx_output_shapes(R, K, L)
+        return (torch.empty(cs, dtype=torch.uint8, device=dev), torch.empty(ss, dtype=torch.uint8, device=dev))
+
     ops = []
     if name == "qkv":
         X = gen("qkv", "X", copies)
         W = gen("qkv", "W", copies)
         M, K = X[0].shape
         N = W[0].shape[0]
-        cx = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
-        sx = torch.empty((M, K // 32), dtype=torch.uint8, device=dev)
-        cw = torch.empty((N, K // 2), dtype=torch.uint8, device=dev)
-        sw = torch.empty((N, K // 32), dtype=torch.uint8, device=dev)
+        cx, sx = mx_bufs(M, K)
+        cw, sw = mx_bufs(N, K)
         C = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        qk = "quant_mx_rows_tiled_kernel" if L == B.LAYOUT_TILED else "quant_mx_rows_kernel"
         ops = [
-            ("quantize X (MXFP4, RNE)", "quant_mx_rows_kernel",
-             lambda s: B.fp4_quantize_mx(X[s % copies], codes=cx, scales=sx),
+            ("quantize X (MXFP4, RNE)", qk,
+             lambda s: B.fp4_quantize_mx(X[s % copies], codes=cx, scales=sx, layout=L),
              M * K * MX_BYTES_PER_ELEM, "GB/s", HBM_PEAK_GBS, "hbm"),
-            ("quantize W (MXFP4, RNE)", "quant_mx_rows_kernel",
-             lambda s: B.fp4_quantize_mx(W[s % copies], codes=cw, scales=sw),
+            ("quantize W (MXFP4, RNE)", qk,
+             lambda s: B.fp4_quantize_mx(W[s % copies], codes=cw, scales=sw, layout=L),
              N * K * MX_BYTES_PER_ELEM, "GB/s", HBM_PEAK_GBS, "hbm"),
             ("GEMM MXFP4 X W^T -> bf16", "gemm_mx_kernel",
-             lambda s: B.fp4_gemm_mx(cx, sx, cw, sw, c=C),
+             lambda s: B.fp4_gemm_mx(cx, sx, cw, sw, c=C, layout=L, m=M, n=N),
              2.0 * M * N * K, "TFLOP/s", FP4_PEAK_TFLOPS, "mfma"),
         ]
         cfg = {"workload": "Llama-3-8B QKV forward, MXFP4 RNE", "X": [M, K], "W": [N, K], "gemm_mnk": [M, N, K],
-               "out": "bf16", "global_batch_tokens": M, "input_copies": copies}
+               "out": "bf16", "layout": layout_name, "global_batch_tokens": M, "input_copies": copies}
         return cfg, ops, 2.0 * M * N * K
     if name == "mlp":
         X = gen("mlp_gate_up", "X", copies)
@@ -101,9 +108,8 @@ def build_workload(name, dev, copies):
         bufs = {}
 
         def q(tag, src, R, K):
-            bufs[tag] = (torch.empty((R, K // 2), dtype=torch.uint8, device=dev),
-                         torch.empty((R, K // 32), dtype=torch.uint8, device=dev))
-            return lambda s: B.fp4_quantize_mx(src[s % copies], codes=bufs[tag][0], scales=bufs[tag][1])
+            bufs[tag] = mx_bufs(R, K)
+            return lambda s: B.fp4_quantize_mx(src[s % copies], codes=bufs[tag][0], scales=bufs[tag][1], layout=L)
 
         C1 = torch.empty((M, N1), dtype=torch.bfloat16, device=dev)
         C2 = torch.empty((M, N2), dtype=torch.bfloat16, device=dev)
@@ -112,17 +118,18 @@ def build_workload(name, dev, copies):
              HBM_PEAK_GBS, "hbm"),
             ("quantize W_gate_up", "quant_mx_rows_kernel", q("wg", Wg, N1, K1), N1 * K1 * MX_BYTES_PER_ELEM, "GB/s",
              HBM_PEAK_GBS, "hbm"),
-            ("GEMM gate/up", "gemm_mx_kernel", lambda s: B.fp4_gemm_mx(*bufs["x"], *bufs["wg"], c=C1),
+            ("GEMM gate/up", "gemm_mx_kernel",
+             lambda s: B.fp4_gemm_mx(*bufs["x"], *bufs["wg"], c=C1, layout=L, m=M, n=N1),
              2.0 * M * N1 * K1, "TFLOP/s", FP4_PEAK_TFLOPS, "mfma"),
             ("quantize H", "quant_mx_rows_kernel", q("h", H, M, K2), M * K2 * MX_BYTES_PER_ELEM, "GB/s",
              HBM_PEAK_GBS, "hbm"),
             ("quantize W_down", "quant_mx_rows_kernel", q("wd", Wd, N2, K2), N2 * K2 * MX_BYTES_PER_ELEM, "GB/s",
              HBM_PEAK_GBS, "hbm"),
-            ("GEMM down", "gemm_mx_kernel", lambda s: B.fp4_gemm_mx(*bufs["h"], *bufs["wd"], c=C2),
+            ("GEMM down", "gemm_mx_kernel", lambda s: B.fp4_gemm_mx(*bufs["h"], *bufs["wd"], c=C2, layout=L, m=M, n=N2),
              2.0 * M * N2 * K2, "TFLOP/s", FP4_PEAK_TFLOPS, "mfma"),
         ]
         cfg = {"workload": "Llama-3-8B MLP forward (gate/up + down), MXFP4 RNE",
-               "gemms_mnk": [[M, N1, K1], [M, N2, K2]], "out": "bf16", "input_copies": copies}
+               "gemms_mnk": [[M, N1, K1], [M, N2, K2]], "out": "bf16", "layout": layout_name, "input_copies": copies}
         return cfg, ops, 2.0 * M * N1 * K1 + 2.0 * M * N2 * K2
     if name == "backward":
         dY = gen("backward", "dY", copies)
@@ -134,8 +141,7 @@ def build_workload(name, dev, copies):
         bufs = {}
 
         def alloc(tag, R, K):
-            bufs[tag] = (torch.empty((R, K // 2), dtype=torch.uint8, device=dev),
-                         torch.empty((R, K // 32), dtype=torch.uint8, device=dev))
+            bufs[tag] = mx_bufs(R, K)
 
         alloc("dy_r", T, O)
         alloc("wt", I, O)
@@ -147,28 +153,32 @@ def build_workload(name, dev, copies):
         ops = [
             ("quantize dY rows (SR)", "quant_mx_rows_kernel",
              lambda s: B.fp4_quantize_mx(dY[s % copies], round=B.SR, seed=seed, stream_id=0, codes=bufs["dy_r"][0],
-                                         scales=bufs["dy_r"][1]), T * O * MX_BYTES_PER_ELEM, "GB/s", HBM_PEAK_GBS,
+                                         scales=bufs["dy_r"][1], layout=L), T * O * MX_BYTES_PER_ELEM, "GB/s",
+             HBM_PEAK_GBS,
              "hbm"),
             ("quantize W^T (cols)", "quant_mx_cols_kernel",
              lambda s: B.fp4_quantize_mx(W[s % copies], axis=B.ALONG_COLS, codes=bufs["wt"][0],
-                                         scales=bufs["wt"][1]), O * I * MX_BYTES_PER_ELEM, "GB/s", HBM_PEAK_GBS,
+                                         scales=bufs["wt"][1], layout=L), O * I * MX_BYTES_PER_ELEM, "GB/s",
+             HBM_PEAK_GBS,
              "hbm"),
-            ("GEMM dgrad dY W", "gemm_mx_kernel", lambda s: B.fp4_gemm_mx(*bufs["dy_r"], *bufs["wt"], c=dX),
+            ("GEMM dgrad dY W", "gemm_mx_kernel",
+             lambda s: B.fp4_gemm_mx(*bufs["dy_r"], *bufs["wt"], c=dX, layout=L, m=T, n=I),
              2.0 * T * I * O, "TFLOP/s", FP4_PEAK_TFLOPS, "mfma"),
             ("Hadamard-quantize dY^T (SR)", "quant_mx_cols_kernel",
              lambda s: B.fp4_hadamard32_quantize(dY[s % copies], mask, axis=B.ALONG_COLS, round=B.SR, seed=seed,
-                                                 stream_id=1, codes=bufs["dy_c"][0], scales=bufs["dy_c"][1]),
+                                                 stream_id=1, codes=bufs["dy_c"][0], scales=bufs["dy_c"][1],
+                                                 layout=L),
              T * O * MX_BYTES_PER_ELEM, "GB/s", HBM_PEAK_GBS, "hbm"),
             ("Hadamard-quantize X^T", "quant_mx_cols_kernel",
              lambda s: B.fp4_hadamard32_quantize(X[s % copies], mask, axis=B.ALONG_COLS, codes=bufs["x_c"][0],
-                                                 scales=bufs["x_c"][1]), T * I * MX_BYTES_PER_ELEM, "GB/s",
+                                                 scales=bufs["x_c"][1], layout=L), T * I * MX_BYTES_PER_ELEM, "GB/s",
              HBM_PEAK_GBS, "hbm"),
             ("GEMM wgrad dY^T X (alpha 1/32)", "gemm_mx_kernel",
-             lambda s: B.fp4_gemm_mx(*bufs["dy_c"], *bufs["x_c"], alpha=1.0 / 32, c=dW),
+             lambda s: B.fp4_gemm_mx(*bufs["dy_c"], *bufs["x_c"], alpha=1.0 / 32, c=dW, layout=L, m=O, n=I),
              2.0 * O * I * T, "TFLOP/s", FP4_PEAK_TFLOPS, "mfma"),
         ]
         cfg = {"workload": "Llama-3-8B o_proj backward, MXFP4: SR on dY, fixed-sign Hadamard-32 on wgrad",
-               "dgrad_mnk": [T, I, O], "wgrad_mnk": [O, I, T], "input_copies": copies}
+               "dgrad_mnk": [T, I, O], "wgrad_mnk": [O, I, T], "layout": layout_name, "input_copies": copies}
         return cfg, ops, 2.0 * T * I * O * 2
     # NVFP4
     domain = B.NV_GLOBAL if name == "nvfp4_global" else B.NV_TILE128
@@ -268,7 +278,7 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     dev = torch.device("cuda:0")
-    cfg, ops, step_flops = build_workload(args.workload, dev, args.copies)
+    cfg, ops, step_flops = build_workload(args.workload, dev, args.copies, args.layout)
     stream = torch.cuda.current_stream()
 
     for s in range(args.warmup):

@@ -23,7 +23,7 @@ OK, EINVAL, ESHAPE, EALIGN, ELAUNCH, EUNSUPPORTED = 0, 1, 2, 3, 4, 5
 ALONG_ROWS, ALONG_COLS = 0, 1
 RNE, SR = 0, 1
 NV_GLOBAL, NV_TILE128 = 0, 1
-LAYOUT_LINEAR = 0
+LAYOUT_LINEAR, LAYOUT_TILED = 0, 1
 OUT_F32, OUT_BF16 = 0, 1
 
 _lib = None
@@ -106,35 +106,45 @@ def _logical(rows: int, cols: int, axis: int):
     return (rows, cols) if axis == ALONG_ROWS else (cols, rows)
 
 
+def mx_output_shapes(R: int, K: int, layout: int):
+    """(codes shape, scales shape) of an MX operand [R x K] in `layout`."""
+    if layout == LAYOUT_TILED:
+        Rp = (R + 31) // 32 * 32
+        return (Rp, K // 2), (K // 128, Rp, 4)
+    return (R, K // 2), (R, K // 32)
+
+
+def _mx_outputs(R, K, layout, codes, scales, device):
+    cshape, sshape = mx_output_shapes(R, K, layout)
+    if codes is None:
+        codes = torch.empty(cshape, dtype=torch.uint8, device=device)
+    if scales is None:
+        scales = torch.empty(sshape, dtype=torch.uint8, device=device)
+    return codes, scales
+
+
 def fp4_quantize_mx(x: torch.Tensor, *, cols: Optional[int] = None, axis: int = ALONG_ROWS, round: int = RNE,
-                    seed: int = 0, stream_id: int = 0, codes: Optional[torch.Tensor] = None,
-                    scales: Optional[torch.Tensor] = None, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+                    seed: int = 0, stream_id: int = 0, layout: int = LAYOUT_LINEAR,
+                    codes: Optional[torch.Tensor] = None, scales: Optional[torch.Tensor] = None,
+                    stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
     rows, cols, ld = _input(x, cols)
     R, K = _logical(rows, cols, axis)
-    if codes is None:
-        codes = torch.empty((R, K // 2), dtype=torch.uint8, device=x.device)
-    if scales is None:
-        scales = torch.empty((R, K // 32), dtype=torch.uint8, device=x.device)
+    codes, scales = _mx_outputs(R, K, layout, codes, scales, x.device)
     _check("fp4_quantize_mx", lib().fp4_quantize_mx(x.data_ptr(), rows, cols, ld, axis, round, seed, stream_id,
-                                                    codes.data_ptr(), scales.data_ptr(), LAYOUT_LINEAR,
-                                                    _stream(stream)))
+                                                    codes.data_ptr(), scales.data_ptr(), layout, _stream(stream)))
     return codes, scales
 
 
 def fp4_hadamard32_quantize(x: torch.Tensor, sign_mask: int, *, cols: Optional[int] = None, axis: int = ALONG_COLS,
-                            round: int = RNE, seed: int = 0, stream_id: int = 0,
+                            round: int = RNE, seed: int = 0, stream_id: int = 0, layout: int = LAYOUT_LINEAR,
                             codes: Optional[torch.Tensor] = None, scales: Optional[torch.Tensor] = None,
                             stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
     rows, cols, ld = _input(x, cols)
     R, K = _logical(rows, cols, axis)
-    if codes is None:
-        codes = torch.empty((R, K // 2), dtype=torch.uint8, device=x.device)
-    if scales is None:
-        scales = torch.empty((R, K // 32), dtype=torch.uint8, device=x.device)
+    codes, scales = _mx_outputs(R, K, layout, codes, scales, x.device)
     _check("fp4_hadamard32_quantize",
            lib().fp4_hadamard32_quantize(x.data_ptr(), rows, cols, ld, axis, sign_mask & 0xFFFFFFFF, round, seed,
-                                         stream_id, codes.data_ptr(), scales.data_ptr(), LAYOUT_LINEAR,
-                                         _stream(stream)))
+                                         stream_id, codes.data_ptr(), scales.data_ptr(), layout, _stream(stream)))
     return codes, scales
 
 
@@ -180,13 +190,18 @@ def _gemm_out(M: int, N: int, out_dtype, device, c: Optional[torch.Tensor]):
 
 def fp4_gemm_mx(a_codes: torch.Tensor, a_scales: torch.Tensor, b_codes: torch.Tensor, b_scales: torch.Tensor, *,
                 alpha: float = 1.0, out_dtype=torch.float32, c: Optional[torch.Tensor] = None,
+                layout: int = LAYOUT_LINEAR, m: Optional[int] = None, n: Optional[int] = None,
                 stream=None) -> torch.Tensor:
-    M, N, K = a_codes.shape[0], b_codes.shape[0], a_codes.shape[1] * 2
+    """C = alpha * A B^T.  In the tiled layout the code tensors carry rows
+    padded to a multiple of 32, so pass the logical m and n."""
+    M = a_codes.shape[0] if m is None else m
+    N = b_codes.shape[0] if n is None else n
+    K = a_codes.shape[1] * 2
     if b_codes.shape[1] * 2 != K:
         raise ValueError("A and B must have the same K")
     c, ctype, ldc = _gemm_out(M, N, out_dtype, a_codes.device, c)
     _check("fp4_gemm_mx", lib().fp4_gemm_mx(a_codes.data_ptr(), a_scales.data_ptr(), b_codes.data_ptr(),
-                                            b_scales.data_ptr(), M, N, K, float(alpha), LAYOUT_LINEAR,
+                                            b_scales.data_ptr(), M, N, K, float(alpha), layout,
                                             c.data_ptr(), ctype, ldc, _stream(stream)))
     return c
 

@@ -36,22 +36,25 @@ fp4q_status check_mx_producer(const void *x, int64_t rows, int64_t cols, int64_t
                               const void *codes, const void *scales, int layout, bool *empty)
 {
     if ((axis != FP4Q_ALONG_ROWS && axis != FP4Q_ALONG_COLS) || (round != FP4Q_RNE && round != FP4Q_SR) ||
-        layout != FP4Q_LAYOUT_LINEAR)
+        (layout != FP4Q_LAYOUT_LINEAR && layout != FP4Q_LAYOUT_TILED))
         return FP4Q_EINVAL;
     if (rows < 0 || cols < 0 || ld_x < cols || rows > kMaxDim || cols > kMaxDim || ld_x > kMaxDim)
         return FP4Q_ESHAPE;
+    const bool tiled = layout == FP4Q_LAYOUT_TILED;
     const int64_t R = axis == FP4Q_ALONG_ROWS ? rows : cols;
     const int64_t K = axis == FP4Q_ALONG_ROWS ? cols : rows;
-    if (K % 32 != 0) return FP4Q_ESHAPE;
+    if (K % (tiled ? 128 : 32) != 0) return FP4Q_ESHAPE;
     if (axis == FP4Q_ALONG_COLS && cols % 4 != 0) return FP4Q_ESHAPE;
-    if ((uint64_t)R * (uint64_t)(K / 8) >= (1ull << 32)) return FP4Q_ESHAPE;
+    const int64_t Rs = tiled ? (R + 31) / 32 * 32 : R;  // rows of the stored operand
+    if ((uint64_t)Rs * (uint64_t)(K / 8) >= (1ull << 32)) return FP4Q_ESHAPE;
     *empty = (R == 0 || K == 0);
     if (*empty) return FP4Q_OK;
     if (!x || !codes || !scales) return FP4Q_EINVAL;
     if (!aligned(x, 16) || !aligned(codes, 16) || ld_x % 8 != 0) return FP4Q_EALIGN;
+    if (tiled && !aligned(scales, 16)) return FP4Q_EALIGN;
     const Range rx = bytes(x, input_span(rows, cols, ld_x));
-    const Range rc = bytes(codes, (uint64_t)R * (uint64_t)K / 2);
-    const Range rs = bytes(scales, (uint64_t)R * (uint64_t)K / 32);
+    const Range rc = bytes(codes, (uint64_t)Rs * (uint64_t)K / 2);
+    const Range rs = bytes(scales, (uint64_t)Rs * (uint64_t)K / 32);
     if (overlap(rx, rc) || overlap(rx, rs) || overlap(rc, rs)) return FP4Q_EINVAL;
     return FP4Q_OK;
 }
@@ -71,6 +74,7 @@ fp4q_status run_mx_producer(const void *x, int64_t rows, int64_t cols, int64_t l
     a.axis = axis;
     a.sr = round == FP4Q_SR;
     a.hadamard = hadamard;
+    a.tiled = layout == FP4Q_LAYOUT_TILED;
     a.seed = seed;
     a.stream_id = stream_id;
     a.sign_mask = sign_mask;
@@ -84,12 +88,16 @@ fp4q_status check_gemm_common(const void *a_codes, const void *a_scales, const v
                               int64_t M, int64_t N, int64_t K, int layout, const void *c, int c_type, int64_t ldc,
                               int scale_div, bool *empty)
 {
-    if (layout != FP4Q_LAYOUT_LINEAR || (c_type != FP4Q_OUT_F32 && c_type != FP4Q_OUT_BF16)) return FP4Q_EINVAL;
+    if ((layout != FP4Q_LAYOUT_LINEAR && layout != FP4Q_LAYOUT_TILED) ||
+        (c_type != FP4Q_OUT_F32 && c_type != FP4Q_OUT_BF16))
+        return FP4Q_EINVAL;
+    const bool tiled = layout == FP4Q_LAYOUT_TILED;
     if (M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim || ldc < N || ldc > kMaxDim)
         return FP4Q_ESHAPE;
     if (K % 128 != 0) return FP4Q_ESHAPE;
-    if ((uint64_t)M * (uint64_t)K / 2 >= (1ull << 32) || (uint64_t)N * (uint64_t)K / 2 >= (1ull << 32))
-        return FP4Q_ESHAPE;
+    const uint64_t Ms = tiled ? (uint64_t)(M + 31) / 32 * 32 : (uint64_t)M;  // stored rows
+    const uint64_t Ns = tiled ? (uint64_t)(N + 31) / 32 * 32 : (uint64_t)N;
+    if (Ms * (uint64_t)K / 2 >= (1ull << 32) || Ns * (uint64_t)K / 2 >= (1ull << 32)) return FP4Q_ESHAPE;
     *empty = (M == 0 || N == 0);
     if (*empty) return FP4Q_OK;
     if (!c) return FP4Q_EINVAL;
@@ -100,8 +108,8 @@ fp4q_status check_gemm_common(const void *a_codes, const void *a_scales, const v
     if (!aligned(a_codes, 16) || !aligned(b_codes, 16) || !aligned(a_scales, 4) || !aligned(b_scales, 4))
         return FP4Q_EALIGN;
     const Range rc = bytes(c, ((uint64_t)(M - 1) * (uint64_t)ldc + (uint64_t)N) * esize);
-    const Range ins[4] = {bytes(a_codes, (uint64_t)M * K / 2), bytes(a_scales, (uint64_t)M * K / scale_div),
-                          bytes(b_codes, (uint64_t)N * K / 2), bytes(b_scales, (uint64_t)N * K / scale_div)};
+    const Range ins[4] = {bytes(a_codes, Ms * K / 2), bytes(a_scales, Ms * K / scale_div),
+                          bytes(b_codes, Ns * K / 2), bytes(b_scales, Ns * K / scale_div)};
     for (const Range &r : ins)
         if (overlap(rc, r)) return FP4Q_EINVAL;
     return FP4Q_OK;
@@ -139,8 +147,10 @@ fp4q_status fp4_quantize_nv(const void *x, int64_t rows, int64_t cols, int64_t l
                             float *tensor_scale, void *workspace, size_t workspace_bytes, int layout, void *stream)
 {
     if ((axis != FP4Q_ALONG_ROWS && axis != FP4Q_ALONG_COLS) || (round != FP4Q_RNE && round != FP4Q_SR) ||
-        (domain != FP4Q_NV_GLOBAL && domain != FP4Q_NV_TILE128) || layout != FP4Q_LAYOUT_LINEAR)
+        (domain != FP4Q_NV_GLOBAL && domain != FP4Q_NV_TILE128) ||
+        (layout != FP4Q_LAYOUT_LINEAR && layout != FP4Q_LAYOUT_TILED))
         return FP4Q_EINVAL;
+    if (layout == FP4Q_LAYOUT_TILED) return FP4Q_EUNSUPPORTED;
     if (rows < 0 || cols < 0 || ld_x < cols || rows > kMaxDim || cols > kMaxDim || ld_x > kMaxDim)
         return FP4Q_ESHAPE;
     if (axis == FP4Q_ALONG_COLS) return FP4Q_EUNSUPPORTED;
@@ -200,6 +210,7 @@ fp4q_status fp4_gemm_mx(const void *a_codes, const void *a_scales, const void *b
     g.c = c;
     g.c_bf16 = c_type == FP4Q_OUT_BF16;
     g.ldc = ldc;
+    g.tiled = layout == FP4Q_LAYOUT_TILED;
     (void)hipGetLastError();
     return launched(fp4q::launch_gemm_mx(g, as_stream(stream)));
 }
@@ -209,6 +220,7 @@ fp4q_status fp4_gemm_nv(const void *a_codes, const void *a_scales, const float *
                         int64_t K, float alpha, int layout, void *c, int c_type, int64_t ldc, void *stream)
 {
     if (domain != FP4Q_NV_GLOBAL && domain != FP4Q_NV_TILE128) return FP4Q_EINVAL;
+    if (layout == FP4Q_LAYOUT_TILED) return FP4Q_EUNSUPPORTED;
     bool empty = false;
     const fp4q_status st =
         check_gemm_common(a_codes, a_scales, b_codes, b_scales, M, N, K, layout, c, c_type, ldc, 16, &empty);

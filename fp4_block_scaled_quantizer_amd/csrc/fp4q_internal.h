@@ -14,6 +14,7 @@ struct QuantArgs {
     int axis;        // 0: along rows, 1: along columns (x^T)
     bool sr;
     bool hadamard;
+    bool tiled;      // FP4Q_LAYOUT_TILED outputs (MX only)
     uint64_t seed;
     uint32_t stream_id;
     uint32_t sign_mask;
@@ -25,6 +26,7 @@ struct GemmArgs {
     const void *a_codes, *a_scales, *b_codes, *b_scales;
     const float *a_ts, *b_ts;  // NV tensor scales (null for MX)
     int nv_domain;             // NV only: 0 global, 1 tile128
+    bool tiled;                // MX only: FP4Q_LAYOUT_TILED operands
     int64_t M, N, K;
     float alpha;
     void *c;

@@ -217,30 +217,36 @@ __global__ __launch_bounds__(kThreads) void quant_mx_rows_kernel(const uint16_t 
 // ------------------------------------------------------------------
 // MXFP4 along columns: the logical operand is x^T, blocks run down 32 rows of
 // one column of x.  A lane owns 4 adjacent columns (8-byte loads, so a
-// wavefront reads 512 contiguous bytes of each row) and walks kBlocks
-// consecutive 32-row blocks, so its 16-byte code stores for one output row
-// land next to each other.
+// wavefront reads 512 contiguous bytes of each row) and walks kColBlocks
+// consecutive 32-row blocks.  Each (output row, block) gives 16 bytes of
+// codes, which in the tiled layout is exactly one lane slot of a 1 KiB block:
+// a wavefront's 256 columns fill 512 contiguous bytes of each of 8 blocks,
+// and the 4 scale bytes of the 4 blocks form one 32-bit word per output row.
 // ------------------------------------------------------------------
 constexpr int kColBlocks = 4;
 
-template <bool kSR, bool kHad>
+template <bool kSR, bool kHad, bool kTiled>
 __global__ __launch_bounds__(64) void quant_mx_cols_kernel(const uint16_t *__restrict__ x, uint32_t rows,
-                                                           uint32_t cols, uint32_t ld, uint8_t *__restrict__ codes,
-                                                           uint8_t *__restrict__ scales, uint32_t seed_lo,
-                                                           uint32_t seed_hi, uint32_t stream_id, uint32_t sign_mask)
+                                                           uint32_t cols, uint32_t ld, uint32_t Rp,
+                                                           uint8_t *__restrict__ codes, uint8_t *__restrict__ scales,
+                                                           uint32_t seed_lo, uint32_t seed_hi, uint32_t stream_id,
+                                                           uint32_t sign_mask)
 {
     const uint32_t col0 = (blockIdx.x * 64 + threadIdx.x) * 4;  // first of this lane's 4 columns
     const uint32_t Kb = rows >> 5;                               // blocks per output row
     const uint32_t j0 = blockIdx.y * kColBlocks;
-    if (col0 >= cols) return;  // whole lane idle; no cross-lane work below
+    // columns past `cols` exist only as the zero padding rows of the tiled layout
+    if (col0 >= (kTiled ? Rp : cols)) return;  // whole lane idle; no cross-lane work below
+    const bool live = col0 < cols;              // cols % 4 == 0: all 4 columns live or none
     const uint32_t K2 = rows >> 1;  // bytes of codes per output row
+    uint32_t sword[4] = {0u, 0u, 0u, 0u};
     for (int jb = 0; jb < kColBlocks; ++jb) {
         const uint32_t j = j0 + jb;
         if (j >= Kb) break;
         uint2 raw[32];
 #pragma unroll
         for (int i = 0; i < 32; ++i)
-            raw[i] = load_nt8(x + (size_t)(32 * j + i) * ld + col0);
+            raw[i] = live ? load_nt8(x + (size_t)(32 * j + i) * ld + col0) : make_uint2(0u, 0u);
 #pragma unroll
         for (int cq = 0; cq < 4; ++cq) {
             const uint32_t col = col0 + cq;
@@ -285,12 +291,98 @@ __global__ __launch_bounds__(64) void quant_mx_cols_kernel(const uint16_t *__res
                 }
                 out[g] = packed;
             }
-            if (col < cols) {
-                uint4 o = make_uint4(out[0], out[1], out[2], out[3]);
+            const uint4 o = make_uint4(out[0], out[1], out[2], out[3]);
+            if (kTiled) {
+                const size_t blk = (size_t)(col >> 5) * (rows >> 6) + (j >> 1);
+                *reinterpret_cast<uint4 *>(codes + blk * 1024 + ((col & 31) + 32 * (j & 1)) * 16) = o;
+                sword[cq] |= sbyte << (8 * jb);
+            } else {
                 *reinterpret_cast<uint4 *>(codes + (size_t)col * K2 + (size_t)j * 16) = o;
                 scales[(size_t)col * Kb + j] = (uint8_t)sbyte;
             }
         }
+    }
+    if (kTiled) {
+        // K % 128 == 0 in the tiled layout, so j0 / 4 is a whole 128-wide step
+#pragma unroll
+        for (int cq = 0; cq < 4; ++cq)
+            *reinterpret_cast<uint32_t *>(scales + ((size_t)(j0 >> 2) * Rp + col0 + cq) * 4) = sword[cq];
+    }
+}
+
+// ------------------------------------------------------------------
+// MXFP4 along rows into the tiled layout.  A workgroup owns 32 rows x 512 K
+// (up to 4 K steps): wavefront w reads row 4 i + w of the group, i < 8, with
+// contiguous 1 KiB loads (lane = 8-element chunk), quantizes exactly like the
+// linear kernel, assembles the group's eight 1 KiB lane-order code blocks and
+// its step-major scale words in LDS, then writes both out contiguously.
+// ------------------------------------------------------------------
+template <bool kSR, bool kHad>
+__global__ __launch_bounds__(kThreads) void quant_mx_rows_tiled_kernel(
+    const uint16_t *__restrict__ x, uint32_t R, uint32_t K, uint32_t ld, uint32_t Rp, uint8_t *__restrict__ codes,
+    uint8_t *__restrict__ scales, uint32_t seed_lo, uint32_t seed_hi, uint32_t stream_id, uint32_t sign_mask)
+{
+    __shared__ __attribute__((aligned(16))) uint8_t tile[8192 + 512];
+    const uint32_t g = blockIdx.y;         // 32-row group
+    const uint32_t k0 = blockIdx.x * 512;  // first K of this workgroup
+    const uint32_t nsteps = min(4u, (K - k0) >> 7);
+    const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
+    const int quad_lane = lane & 3;
+    const uint32_t c8 = lane;  // 8-element chunk within the 512-wide window
+    const bool kvalid = (c8 >> 4) < nsteps;
+    uint4 q[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint32_t row = g * 32 + i * 4 + wave;
+        q[i] = make_uint4(0u, 0u, 0u, 0u);
+        if (row < R && kvalid) q[i] = load_nt16(x + (size_t)row * ld + k0 + 8 * c8);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint32_t rl = i * 4 + wave, row = g * 32 + rl;
+        uint32_t packed = 0, sbyte;
+        if (!kHad && !kSR) {
+            uint32_t amax = amax8_bf16(q[i]);
+            amax = xor_max<1>(amax);
+            amax = xor_max<2>(amax);
+            sbyte = mx_scale_byte(amax << 16);
+            packed = cvt8_bf16(q[i], mx_scale_f32(sbyte));
+        } else {
+            float f[8];
+            unpack8(q[i], f);
+            if (kHad) hadamard32_quad(f, (sign_mask >> (8 * quad_lane)) & 0xFFu, quad_lane);
+            uint32_t amax = 0;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) amax = max(amax, f2u(f[j]) & 0x7FFFFFFFu);
+            amax = xor_max<1>(amax);
+            amax = xor_max<2>(amax);
+            sbyte = mx_scale_byte(amax);
+            if (kSR) {
+                const float inv = mx_inv_scale(sbyte);
+                uint32_t w[4];
+                philox4x32_10((k0 >> 3) + c8, row, stream_id, 0u, seed_lo, seed_hi, w);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) packed |= e2m1_sr(f[j] * inv, r16_of(w, j)) << (4 * j);
+            } else {
+                packed = cvt8_f32(f, mx_scale_f32(sbyte));
+            }
+        }
+        // lane-order block (c8 / 8), slot = row + 32 * (32-element half), 4 bytes per chunk
+        *reinterpret_cast<uint32_t *>(tile + (c8 >> 3) * 1024 + (rl + 32 * ((c8 >> 2) & 1)) * 16 + (c8 & 3) * 4) =
+            packed;
+        if (quad_lane == 0) {
+            const uint32_t jb = c8 >> 2;  // MX block within the window, 0..15
+            tile[8192 + (jb >> 2) * 128 + rl * 4 + (jb & 3)] = (uint8_t)sbyte;
+        }
+    }
+    __syncthreads();
+    uint8_t *dst = codes + ((size_t)g * (K >> 6) + (k0 >> 6)) * 1024;
+    for (uint32_t o = t * 16; o < nsteps * 2048; o += kThreads * 16)
+        *reinterpret_cast<uint4 *>(dst + o) = *reinterpret_cast<const uint4 *>(tile + o);
+    if ((uint32_t)t < 8 * nsteps) {
+        const uint32_t s = t >> 3, part = t & 7;
+        *reinterpret_cast<uint4 *>(scales + ((size_t)((k0 >> 7) + s) * Rp + 32 * g) * 4 + part * 16) =
+            *reinterpret_cast<const uint4 *>(tile + 8192 + s * 128 + part * 16);
     }
 }
 
@@ -459,15 +551,27 @@ __global__ __launch_bounds__(kThreads) void nv_quant_tile_kernel(const uint16_t 
 int launch_quant_mx(const QuantArgs &a, hipStream_t st)
 {
     const uint32_t seed_lo = (uint32_t)a.seed, seed_hi = (uint32_t)(a.seed >> 32);
-    if (a.axis == 0) {
+    auto *x = reinterpret_cast<const uint16_t *>(a.x);
+    auto *scales = reinterpret_cast<uint8_t *>(a.scales);
+    if (a.axis == 0 && a.tiled) {
+        const uint32_t R = (uint32_t)a.rows, K = (uint32_t)a.cols;
+        if (R == 0 || K == 0) return 0;
+        const uint32_t Rp = (R + 31) / 32 * 32;
+        dim3 grid((K + 511) / 512, Rp / 32);
+        auto *codes = reinterpret_cast<uint8_t *>(a.codes);
+#define FP4Q_LAUNCH_ROWS_T(SR, HAD)                                                                            \
+    hipLaunchKernelGGL((quant_mx_rows_tiled_kernel<SR, HAD>), grid, dim3(kThreads), 0, st, x, R, K, (uint32_t)a.ld, \
+                       Rp, codes, scales, seed_lo, seed_hi, a.stream_id, a.sign_mask)
+        if (a.sr) { if (a.hadamard) FP4Q_LAUNCH_ROWS_T(true, true); else FP4Q_LAUNCH_ROWS_T(true, false); }
+        else { if (a.hadamard) FP4Q_LAUNCH_ROWS_T(false, true); else FP4Q_LAUNCH_ROWS_T(false, false); }
+#undef FP4Q_LAUNCH_ROWS_T
+    } else if (a.axis == 0) {
         const uint32_t R = (uint32_t)a.rows, K = (uint32_t)a.cols;
         const uint64_t nchunks = (uint64_t)R * (K >> 3);
         if (nchunks == 0) return 0;
         const uint32_t grid = (uint32_t)((nchunks + kThreads * kChunksPerThread - 1) / (kThreads * kChunksPerThread));
         const bool contig = a.ld == a.cols;
         auto *codes = reinterpret_cast<uint32_t *>(a.codes);
-        auto *scales = reinterpret_cast<uint8_t *>(a.scales);
-        auto *x = reinterpret_cast<const uint16_t *>(a.x);
 #define FP4Q_LAUNCH_ROWS(SR, HAD, CONTIG)                                                                   \
     hipLaunchKernelGGL((quant_mx_rows_kernel<SR, HAD, CONTIG>), dim3(grid), dim3(kThreads), 0, st, x, K,       \
                        (uint32_t)a.ld, (uint32_t)nchunks, codes, scales, seed_lo, seed_hi, a.stream_id, a.sign_mask)
@@ -483,15 +587,18 @@ int launch_quant_mx(const QuantArgs &a, hipStream_t st)
         const uint32_t rows = (uint32_t)a.rows, cols = (uint32_t)a.cols;
         if (rows == 0 || cols == 0) return 0;
         const uint32_t Kb = rows >> 5;
-        dim3 grid((cols + 255) / 256, (Kb + kColBlocks - 1) / kColBlocks);
-        auto *x = reinterpret_cast<const uint16_t *>(a.x);
+        const uint32_t Rp = (cols + 31) / 32 * 32;
+        const uint32_t span = a.tiled ? Rp : cols;
+        dim3 grid((span + 255) / 256, (Kb + kColBlocks - 1) / kColBlocks);
         auto *codes = reinterpret_cast<uint8_t *>(a.codes);
-        auto *scales = reinterpret_cast<uint8_t *>(a.scales);
-#define FP4Q_LAUNCH_COLS(SR, HAD)                                                                         \
-    hipLaunchKernelGGL((quant_mx_cols_kernel<SR, HAD>), grid, dim3(64), 0, st, x, rows, cols, (uint32_t)a.ld, \
-                       codes, scales, seed_lo, seed_hi, a.stream_id, a.sign_mask)
-        if (a.sr) { if (a.hadamard) FP4Q_LAUNCH_COLS(true, true); else FP4Q_LAUNCH_COLS(true, false); }
-        else { if (a.hadamard) FP4Q_LAUNCH_COLS(false, true); else FP4Q_LAUNCH_COLS(false, false); }
+#define FP4Q_LAUNCH_COLS(SR, HAD, T)                                                                          \
+    hipLaunchKernelGGL((quant_mx_cols_kernel<SR, HAD, T>), grid, dim3(64), 0, st, x, rows, cols, (uint32_t)a.ld, \
+                       Rp, codes, scales, seed_lo, seed_hi, a.stream_id, a.sign_mask)
+#define FP4Q_LAUNCH_COLS2(SR, HAD) \
+    do { if (a.tiled) FP4Q_LAUNCH_COLS(SR, HAD, true); else FP4Q_LAUNCH_COLS(SR, HAD, false); } while (0)
+        if (a.sr) { if (a.hadamard) FP4Q_LAUNCH_COLS2(true, true); else FP4Q_LAUNCH_COLS2(true, false); }
+        else { if (a.hadamard) FP4Q_LAUNCH_COLS2(false, true); else FP4Q_LAUNCH_COLS2(false, false); }
+#undef FP4Q_LAUNCH_COLS2
 #undef FP4Q_LAUNCH_COLS
     }
     return hipGetLastError() == hipSuccess ? 0 : 1;

@@ -58,6 +58,20 @@
  *   scales  MX: [R x K/32] E8M0 bytes; NV: [R x K/16] E4M3 bytes, row-major;
  *   tensor_scale  NV global: 1 float; NV tile128: [ceil(R/128) x ceil(K/128)]
  *           floats, row-major, one per 128 x 128 tile of the logical operand.
+ * Tiled layout (FP4Q_LAYOUT_TILED; MX operands only; K % 128 == 0): the
+ * consumer layout of the MX GEMM ([Fusion], section "The Design Philosophy
+ * of Format-Aware Fusion": the producer writes what the consumer loads).
+ * With Rp = 32 * ceil(R/32):
+ *   codes   [Rp/32][K/64][64][16] bytes.  The 16 bytes at (g, kb, l) hold row
+ *           32 g + (l mod 32), K elements 64 kb + 32 (l / 32) .. +31, element
+ *           2j in the low nibble of byte j: one 1 KiB block is exactly the
+ *           operand of one gfx950 scaled-MFMA instruction, lane l's 16 bytes
+ *           at offset 16 l.  Rows R .. Rp-1 hold zero codes.
+ *   scales  [K/128][Rp][4] bytes: byte q of (s, r) is the E8M0 scale of row r,
+ *           K block 4 s + q (one 32-bit word per row per 128-wide K step).
+ *           Rows R .. Rp-1 hold 0.
+ *   Sizes: codes Rp * K / 2 bytes, scales Rp * K / 32 bytes, both 16-byte
+ *   aligned.  Producers write every byte, padding included.
  *
  * GEMM.  C[M x N] = alpha * A * B^T, A the logical [M x K] operand and B the
  * logical [N x K] operand, both quantized along K; fp32 accumulation; C is
@@ -118,7 +132,7 @@ typedef enum {
 typedef enum { FP4Q_ALONG_ROWS = 0, FP4Q_ALONG_COLS = 1 } fp4q_axis;
 typedef enum { FP4Q_RNE = 0, FP4Q_SR = 1 } fp4q_round;
 typedef enum { FP4Q_NV_GLOBAL = 0, FP4Q_NV_TILE128 = 1 } fp4q_nv_domain;
-typedef enum { FP4Q_LAYOUT_LINEAR = 0 } fp4q_layout;
+typedef enum { FP4Q_LAYOUT_LINEAR = 0, FP4Q_LAYOUT_TILED = 1 } fp4q_layout;
 typedef enum { FP4Q_OUT_F32 = 0, FP4Q_OUT_BF16 = 1 } fp4q_out;
 
 /* MXFP4 producer ("native mxfp", [Fusion] section "The Design Philosophy of
@@ -126,7 +140,8 @@ typedef enum { FP4Q_OUT_F32 = 0, FP4Q_OUT_BF16 = 1 } fp4q_out;
  * x: bf16 [rows x ld_x]; writes codes [R x K/2] and E8M0 scales [R x K/32].
  * round = FP4Q_SR uses (seed, stream_id) as stated above ("row-gradient
  * stochastic rounding", [Fusion] section "Two Key Numerical Techniques").
- * Requires K % 32 == 0.  Both axes, both rounding modes. */
+ * Requires K % 32 == 0 (linear) or K % 128 == 0 (tiled).  Both axes, both
+ * rounding modes, both layouts. */
 FP4Q_API fp4q_status fp4_quantize_mx(const void *x, int64_t rows, int64_t cols, int64_t ld_x, int axis,
                             int round, uint64_t seed, uint32_t stream_id, void *codes, void *scales,
                             int layout, void *stream);
@@ -150,7 +165,7 @@ FP4Q_API size_t fp4q_nv_workspace_bytes(int64_t rows, int64_t cols, int axis, in
  * Format-Aware Fusion"; the two-level scale of [Stack] section "NVFP4 is more
  * than a 4-bit value").  Writes codes [R x K/2], E4M3 scales [R x K/16] and
  * tensor_scale.  Requires K % 16 == 0.  FP4Q_EUNSUPPORTED: axis
- * FP4Q_ALONG_COLS. */
+ * FP4Q_ALONG_COLS, layout FP4Q_LAYOUT_TILED. */
 FP4Q_API fp4q_status fp4_quantize_nv(const void *x, int64_t rows, int64_t cols, int64_t ld_x, int axis, int round,
                             uint64_t seed, uint32_t stream_id, int domain, void *codes, void *scales,
                             float *tensor_scale, void *workspace, size_t workspace_bytes, int layout,
@@ -158,8 +173,10 @@ FP4Q_API fp4q_status fp4_quantize_nv(const void *x, int64_t rows, int64_t cols, 
 
 /* MXFP4 GEMM on gfx950's scaled FP4 MFMA (E8M0 scales applied by the matrix
  * core): C = alpha * A * B^T.  a_codes [M x K/2], a_scales [M x K/32],
- * b_codes [N x K/2], b_scales [N x K/32] as written by the MX producers.
- * Requires K % 128 == 0; M and N are arbitrary. */
+ * b_codes [N x K/2], b_scales [N x K/32] as written by the MX producers,
+ * in the layout given by `layout` (both operands in the same layout; the
+ * tiled layout is the fast one).  Requires K % 128 == 0; M and N are
+ * arbitrary. */
 FP4Q_API fp4q_status fp4_gemm_mx(const void *a_codes, const void *a_scales, const void *b_codes, const void *b_scales,
                         int64_t M, int64_t N, int64_t K, float alpha, int layout, void *c, int c_type,
                         int64_t ldc, void *stream);
@@ -168,7 +185,8 @@ FP4Q_API fp4q_status fp4_gemm_mx(const void *a_codes, const void *a_scales, cons
  * bf16 MFMA; the FP32 tensor scales multiply the fp32 partial sums (once in
  * the epilogue for the global domain, per 128-wide K slice for tile128).
  * a_tensor_scale / b_tensor_scale as written by fp4_quantize_nv with the same
- * domain.  Requires K % 128 == 0. */
+ * domain.  Requires K % 128 == 0.  FP4Q_EUNSUPPORTED: layout
+ * FP4Q_LAYOUT_TILED. */
 FP4Q_API fp4q_status fp4_gemm_nv(const void *a_codes, const void *a_scales, const float *a_tensor_scale,
                         const void *b_codes, const void *b_scales, const float *b_tensor_scale, int domain,
                         int64_t M, int64_t N, int64_t K, float alpha, int layout, void *c, int c_type,

@@ -208,6 +208,30 @@ def quantize_nv(x, cols=None, axis=AXIS_ROWS, sr=False, seed=0, stream=0, domain
     return codes, scales, ts
 
 
+def tile_mx(codes, scales):
+    """The tiled consumer layout of an MX operand, as a pure index map of the
+    linear one (definition in the library header): with Rp = 32 * ceil(R/32),
+    codes become [Rp/32][K/64][64 lanes][16 bytes] where lane l of block
+    (g, kb) holds row 32 g + l mod 32, K elements 64 kb + 32 (l / 32) .. +31;
+    scales become [K/128][Rp][4] (byte q of (s, r) = scale of row r, block
+    4 s + q).  Padding rows are zero.  Returns (codes [Rp, K/2], scales
+    [K/128, Rp, 4]) as uint8 arrays."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    scales = np.asarray(scales, dtype=np.uint8)
+    R, K2 = codes.shape
+    K = 2 * K2
+    assert K % 128 == 0 and scales.shape == (R, K // 32)
+    Rp = (R + 31) // 32 * 32
+    c = np.zeros((Rp, K2), dtype=np.uint8)
+    c[:R] = codes
+    # [g, row in group, kb, half, 16 bytes] -> [g, kb, half, row in group, 16 bytes]
+    tiled = c.reshape(Rp // 32, 32, K // 64, 2, 16).transpose(0, 2, 3, 1, 4).reshape(Rp, K2)
+    s = np.zeros((Rp, K // 32), dtype=np.uint8)
+    s[:R] = scales
+    ts = s.reshape(Rp, K // 128, 4).transpose(1, 0, 2)
+    return np.ascontiguousarray(tiled), np.ascontiguousarray(ts)
+
+
 def dequant_mx(codes, scales):
     codes = np.ascontiguousarray(codes, dtype=np.uint8)
     scales = np.ascontiguousarray(scales, dtype=np.uint8)

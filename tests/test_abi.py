@@ -63,7 +63,7 @@ def test_quantize_mx_status_codes():
 
 def test_hadamard_status_codes():
     f = L.fp4_hadamard32_quantize
-    assert f(X, 64, 64, 64, 1, 0xFFFF, 0, 0, 0, CODES, SCALES, 1, None) == B.EINVAL
+    assert f(X, 64, 64, 64, 1, 0xFFFF, 0, 0, 0, CODES, SCALES, 2, None) == B.EINVAL
     assert f(X, 40, 64, 64, 1, 0xFFFF, 0, 0, 0, CODES, SCALES, 0, None) == B.ESHAPE
     assert f(X, 0, 64, 64, 1, 0xFFFF, 0, 0, 0, CODES, SCALES, 0, None) == B.OK
 
@@ -95,7 +95,7 @@ def g_mx(M=256, N=256, K=256, layout=0, ctype=0, ldc=None, c=C, a_codes=CODES, a
 
 
 def test_gemm_mx_status_codes():
-    assert g_mx(layout=1) == B.EINVAL
+    assert g_mx(layout=2) == B.EINVAL
     assert g_mx(ctype=3) == B.EINVAL
     assert g_mx(c=None) == B.EINVAL
     assert g_mx(a_codes=None) == B.EINVAL
@@ -126,3 +126,12 @@ def test_binding_has_no_cpu_fallback(monkeypatch, tmp_path):
     monkeypatch.setattr(B, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(FileNotFoundError):
         B.lib()
+
+
+def test_tiled_layout_status_codes():
+    assert q_mx(layout=1, cols=96, ld=96) == B.ESHAPE             # tiled needs K % 128
+    assert q_mx(layout=1, cols=128, ld=128, scales=SCALES + 4) == B.EALIGN
+    assert q_mx(layout=2) == B.EINVAL
+    assert L.fp4_quantize_nv(X, 64, 64, 64, 0, 0, 0, 0, 0, CODES, SCALES, TS, WS, 4096, 1, None) == B.EUNSUPPORTED
+    assert g_mx(layout=1, K=96) == B.ESHAPE
+    assert g_mx(layout=3) == B.EINVAL

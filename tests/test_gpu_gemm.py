@@ -205,3 +205,80 @@ def test_nv_full_size_sampled_rows(domain):
     cref, w = oracle.gemm_ref(Afull_rows, Bd)
     worst = gemm_check(c[torch.as_tensor(rows, device=dev)].cpu().numpy(), cref, w, f"nv full d{domain}")
     print(f"nv domain {domain}: worst |err| / sum|ab| = {worst:.3e}")
+
+
+# ------------------------------------------------------------------ tiled layout
+
+
+def mx_operand_tiled(xt, dev, axis=B.ALONG_ROWS, sr=False, had=False, mask=0, stream=0):
+    """Tiled operand from the GPU producer (checked against the oracle's tiled
+    bytes) plus the oracle's linear codes for the reference."""
+    xb = synth.bf16_bits(xt)
+    x = xt.to(dev)
+    if had:
+        c, s = B.fp4_hadamard32_quantize(x, mask, axis=axis, round=B.SR if sr else B.RNE, seed=synth.SR_SEED,
+                                         stream_id=stream, layout=B.LAYOUT_TILED)
+        oc, os_ = oracle.hadamard32_quantize(xb, mask, axis=axis, sr=sr, seed=synth.SR_SEED, stream=stream)
+    else:
+        c, s = B.fp4_quantize_mx(x, axis=axis, round=B.SR if sr else B.RNE, seed=synth.SR_SEED, stream_id=stream,
+                                 layout=B.LAYOUT_TILED)
+        oc, os_ = oracle.quantize_mx(xb, axis=axis, sr=sr, seed=synth.SR_SEED, stream=stream)
+    torch.cuda.synchronize()
+    tc, ts = oracle.tile_mx(oc, os_)
+    assert_bytes_equal(np_u8(c), tc, "tiled operand codes")
+    assert_bytes_equal(np_u8(s), ts, "tiled operand scales")
+    return c, s, oc, os_
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 1, 128), (33, 257, 384), (300, 200, 256), (256, 512, 1024),
+                                   (511, 129, 128), (640, 384, 2048), (4096, 256, 512)])
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_mx_tiled_ragged(M, N, K, out):
+    dev = device()
+    announce(f"gemm mx tiled {M}x{N}x{K} {out}")
+    a, sa, oa, osa = mx_operand_tiled(synth.activation(M, K, 60), dev)
+    b, sb, ob, osb = mx_operand_tiled(synth.weight(N, K, 61), dev)
+    c = B.fp4_gemm_mx(a, sa, b, sb, alpha=0.75, layout=B.LAYOUT_TILED, m=M, n=N)
+    torch.cuda.synchronize()
+    cref, w = oracle.gemm_ref(oracle.dequant_mx(oa, osa), oracle.dequant_mx(ob, osb), 0.75)
+    gemm_check(c.cpu().numpy(), cref, w, f"tiled {M}x{N}x{K}")
+    if out == "bf16":
+        c16 = B.fp4_gemm_mx(a, sa, b, sb, alpha=0.75, layout=B.LAYOUT_TILED, m=M, n=N, out_dtype=torch.bfloat16)
+        # odd ldc: the epilogue's element path
+        big = torch.zeros((M, N + 3), dtype=torch.bfloat16, device=dev)
+        B.fp4_gemm_mx(a, sa, b, sb, alpha=0.75, layout=B.LAYOUT_TILED, m=M, n=N, c=big[:, :N])
+        torch.cuda.synchronize()
+        want16 = sf.f32_to_bf16_bits_rne(c.cpu().numpy())
+        assert np.array_equal(c16.view(torch.int16).cpu().numpy().view(np.uint16), want16)
+        assert np.array_equal(big[:, :N].contiguous().view(torch.int16).cpu().numpy().view(np.uint16), want16)
+        assert torch.all(big[:, N:] == 0)
+
+
+TILED_FULL_GEMMS = [
+    ("qkv", ("qkv", "X", "rows", False, False, 0), ("qkv", "W", "rows", False, False, 0), 1.0),
+    ("dgrad", ("backward", "dY", "rows", True, False, 0), ("backward", "W", "cols", False, False, 1), 1.0),
+    ("wgrad", ("backward", "dY", "cols", True, True, 1), ("backward", "X", "cols", False, True, 1), 1.0 / 32),
+]
+
+
+@pytest.mark.parametrize("name,aspec,bspec,alpha", TILED_FULL_GEMMS, ids=[g[0] for g in TILED_FULL_GEMMS])
+def test_mx_tiled_full_size_sampled_rows(name, aspec, bspec, alpha):
+    dev = device()
+    announce(f"gemm mx tiled full {name}")
+    mask = synth.sign_mask(synth.HADAMARD_MASK_SEED)
+
+    def operand(spec):
+        cfg, role, axis, sr, had, stream = spec
+        return mx_operand_tiled(synth.config_tensor(cfg, role), dev,
+                                axis=B.ALONG_ROWS if axis == "rows" else B.ALONG_COLS, sr=sr, had=had, mask=mask,
+                                stream=stream)
+
+    a, sa, oa, osa = operand(aspec)
+    b, sb, ob, osb = operand(bspec)
+    M, N = oa.shape[0], ob.shape[0]
+    c = B.fp4_gemm_mx(a, sa, b, sb, alpha=alpha, layout=B.LAYOUT_TILED, m=M, n=N)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([np.arange(0, M, max(1, M // 96)), [M - 1]]))[:128]
+    cref, w = oracle.gemm_ref(oracle.dequant_mx(oa[rows], osa[rows]), oracle.dequant_mx(ob, osb), alpha)
+    worst = gemm_check(c[torch.as_tensor(rows, device=dev)].cpu().numpy(), cref, w, name)
+    print(f"tiled {name}: worst |err| / sum|ab| = {worst:.3e}")

@@ -206,3 +206,88 @@ def test_nv_full_size(role, domain):
     assert_bytes_equal(ts.cpu().numpy().view(np.uint32), ots.view(np.uint32), "tensor scales")
     assert_bytes_equal(np_u8(scales), os_, "block scales")
     assert_bytes_equal(np_u8(codes), oc, "codes")
+
+
+# ------------------------------------------------------------------ tiled (consumer) layout
+
+TILED_CASES = [
+    # rows, cols, axis, sr, had
+    (1, 128, "rows", False, False), (33, 384, "rows", False, False), (70, 640, "rows", True, False),
+    (64, 1024, "rows", False, True), (96, 512, "rows", True, True), (300, 1152, "rows", False, False),
+    (128, 36, "cols", False, False), (256, 100, "cols", True, False), (384, 64, "cols", False, True),
+    (128, 260, "cols", True, True),
+]
+
+
+@pytest.mark.parametrize("rows,cols,axis,sr,had", TILED_CASES)
+def test_mx_tiled_small(rows, cols, axis, sr, had):
+    dev = device()
+    announce(f"tiled {axis} {rows}x{cols} sr={sr} hadamard={had}")
+    ld = (cols + 7) // 8 * 8
+    xb = synth.bf16_bits(synth.grad_student_t3(rows, cols, 50) if had else synth.activation(rows, cols, 51))
+    x = to_dev(synth.from_bf16_bits(xb), dev, ld)
+    ax = B.ALONG_ROWS if axis == "rows" else B.ALONG_COLS
+    mask = synth.sign_mask(7)
+    rnd = B.SR if sr else B.RNE
+    if had:
+        codes, scales = B.fp4_hadamard32_quantize(x, mask, axis=ax, round=rnd, seed=7, stream_id=1, layout=B.LAYOUT_TILED)
+        oc, os_ = oracle.hadamard32_quantize(xb, mask, axis=ax, sr=sr, seed=7, stream=1)
+    else:
+        codes, scales = B.fp4_quantize_mx(x, axis=ax, round=rnd, seed=7, stream_id=1, layout=B.LAYOUT_TILED)
+        oc, os_ = oracle.quantize_mx(xb, axis=ax, sr=sr, seed=7, stream=1)
+    torch.cuda.synchronize()
+    tc, ts = oracle.tile_mx(oc, os_)
+    assert_bytes_equal(np_u8(scales), ts, "tiled scales")
+    assert_bytes_equal(np_u8(codes), tc, "tiled codes")
+
+
+def test_tiled_padding_overwritten():
+    # poisoned outputs: the producer writes every byte of the tiled buffers, padding rows included
+    dev = device()
+    announce("tiled padding poison")
+    rows, cols = 45, 256
+    xb = synth.bf16_bits(synth.activation(rows, cols, 52))
+    (cs, ss) = B.mx_output_shapes(rows, cols, B.LAYOUT_TILED)
+    codes = torch.full(cs, 0xA5, dtype=torch.uint8, device=dev)
+    scales = torch.full(ss, 0xA5, dtype=torch.uint8, device=dev)
+    B.fp4_quantize_mx(synth.from_bf16_bits(xb).to(dev), layout=B.LAYOUT_TILED, codes=codes, scales=scales)
+    torch.cuda.synchronize()
+    oc, os_ = oracle.quantize_mx(xb)
+    tc, ts = oracle.tile_mx(oc, os_)
+    assert_bytes_equal(np_u8(codes), tc, "codes")
+    assert_bytes_equal(np_u8(scales), ts, "scales")
+
+
+TILED_FULL = [
+    ("qkv", "X", "rows", False, False),
+    ("qkv", "W", "rows", False, False),
+    ("mlp_down", "H", "rows", False, False),
+    ("backward", "dY", "rows", True, False),
+    ("backward", "W", "cols", False, False),
+    ("backward", "dY", "cols", True, True),
+    ("backward", "X", "cols", False, True),
+]
+
+
+@pytest.mark.parametrize("cfg,role,axis,sr,had", TILED_FULL)
+def test_mx_tiled_full_size(cfg, role, axis, sr, had):
+    dev = device()
+    announce(f"tiled full {cfg}.{role} axis={axis} sr={sr} hadamard={had}")
+    xt = synth.config_tensor(cfg, role)
+    xb = synth.bf16_bits(xt)
+    ax = B.ALONG_ROWS if axis == "rows" else B.ALONG_COLS
+    stream = 0 if axis == "rows" else 1
+    mask = synth.sign_mask(synth.HADAMARD_MASK_SEED)
+    rnd = B.SR if sr else B.RNE
+    if had:
+        codes, scales = B.fp4_hadamard32_quantize(xt.to(dev), mask, axis=ax, round=rnd, seed=synth.SR_SEED,
+                                                  stream_id=stream, layout=B.LAYOUT_TILED)
+        oc, os_ = oracle.hadamard32_quantize(xb, mask, axis=ax, sr=sr, seed=synth.SR_SEED, stream=stream)
+    else:
+        codes, scales = B.fp4_quantize_mx(xt.to(dev), axis=ax, round=rnd, seed=synth.SR_SEED, stream_id=stream,
+                                          layout=B.LAYOUT_TILED)
+        oc, os_ = oracle.quantize_mx(xb, axis=ax, sr=sr, seed=synth.SR_SEED, stream=stream)
+    torch.cuda.synchronize()
+    tc, ts = oracle.tile_mx(oc, os_)
+    assert_bytes_equal(np_u8(scales), ts, "tiled scales")
+    assert_bytes_equal(np_u8(codes), tc, "tiled codes")
