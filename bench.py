@@ -41,7 +41,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="qkv", choices=["qkv", "mlp", "backward", "nvfp4_global", "nvfp4_tile"])
+    ap.add_argument("--workload", default="qkv",
+                    choices=["qkv", "mlp", "backward", "nvfp4_global", "nvfp4_tile", "copy"],
+                    help="copy = a plain 1 GiB device copy: the HBM reference for counter scaling")
     ap.add_argument("--copies", type=int, default=4, help="input copies rotated across steps (cold producers)")
     ap.add_argument("--layout", default="tiled", choices=["tiled", "linear"],
                     help="MX operand layout between producer and GEMM (tiled = the GEMM's consumer layout)")
@@ -73,6 +75,14 @@ def build_workload(name, dev, copies, layout_name="tiled"):
         return (torch.empty(cs, dtype=torch.uint8, device=dev), torch.empty(ss, dtype=torch.uint8, device=dev))
 
     ops = []
+    if name == "copy":
+        # a plain copy kernel of known size: 1 GiB read + 1 GiB written per launch
+        n = 1 << 29
+        src = [torch.empty(n, dtype=torch.bfloat16, device=dev).fill_(1.0) for _ in range(2)]
+        dst = torch.empty(n, dtype=torch.bfloat16, device=dev)
+        ops = [("device copy 1 GiB", "elementwise copy", lambda s: dst.copy_(src[s % 2]), 2.0 * 2 * n, "GB/s",
+                HBM_PEAK_GBS, "hbm")]
+        return {"workload": "plain device copy, 1 GiB in + 1 GiB out"}, ops, 0.0
     if name == "qkv":
         X = gen("qkv", "X", copies)
         W = gen("qkv", "W", copies)
@@ -336,7 +346,7 @@ def main():
     roofline = {"bound": dk["bound"], "achieved": dk["achieved"], "peak": dk["peak"], "unit": dk["unit"],
                 "frac": dk["frac"], "traffic": read_traffic(dk["kernel"], args.workload), "kernel": dk["kernel"],
                 "op": dk["op"], "avg_us": dk["avg_us"]}
-    value = step_flops / (ms_per_step * 1e-3) / 1e12
+    value = step_flops / (ms_per_step * 1e-3) / 1e12 if step_flops else dk["achieved"]
     out = {
         "metric": "quantize+FP4 GEMM TFLOP/s (Llama-3-8B shapes)",
         "value": round(value, 1),

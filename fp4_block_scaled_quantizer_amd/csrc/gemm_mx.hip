@@ -39,12 +39,15 @@ typedef int v8i_t __attribute__((ext_vector_type(8)));
 typedef float v16f_t __attribute__((ext_vector_type(16)));
 
 constexpr int kBM = 256, kBN = 256;
-constexpr int kStages = 4;                                  // LDS ring depth (K steps in flight)
+constexpr int kStages = 3;                                  // LDS ring depth (K steps in flight)
 constexpr int kCodeBytes = kBM * 64;                        // one operand's codes per 128-wide K step
 constexpr int kScaleOff = 2 * kCodeBytes;                   // A scales, then B scales (u32 per row)
 constexpr int kStageBytes = 2 * kCodeBytes + (kBM + kBN) * 4;  // 34 KiB
-constexpr int kLdsBytes = kStages * kStageBytes;            // 136 KiB
+constexpr int kRingBytes = kStages * kStageBytes;           // 102 KiB
+constexpr int kEpiWaveBytes = 16 * (512 + 16);              // one wave's epilogue band: 16 x 128 fp32, padded rows
+constexpr int kLdsBytes = kRingBytes + 4 * kEpiWaveBytes;   // 136 KiB
 constexpr int kDmaPerStage = 10;                            // DMA instructions per wave per stage
+constexpr int kDmaPerPhase = kDmaPerStage / 2;
 
 // Tile order: XCD-contiguous ranges (workgroup b runs on XCD b mod 8), then
 // groups of 8 tile rows swept column by column inside each range.
@@ -63,23 +66,23 @@ __device__ __forceinline__ void tile_coords(int bid, int tiles_m, int tiles_n, i
     tn = w / gsz;
 }
 
-// Global -> LDS copies that bypass VGPRs (gfx950 LDS DMA): lane i writes its
-// 16 (or 4) bytes to LDS address m0 + 16 i (4 i).  They are issued from
-// inline assembly so that the only waits on them are the explicit
-// vmcnt waits of the K loop: every vector-memory instruction of the loop is
-// one of these, so the count of DMA instructions issued after a stage is
-// exactly the vmcnt value that guarantees that stage has landed.
-// lds_addr must be the same in every lane (it is moved through
-// readfirstlane into the scalar M0 register).
-__device__ __forceinline__ void dma16(const void *gptr, uint32_t lds_addr)
+// Global -> LDS copies that bypass VGPRs (gfx950 LDS DMA): lane i reads
+// base + voff_i (base a 64-bit scalar address, voff a 32-bit per-lane byte
+// offset) and writes its 16 (or 4) bytes to LDS address m0 + 16 i (4 i).
+// They are issued from inline assembly so that the only waits on them are
+// the explicit vmcnt waits of the K loop: every vector-memory instruction of
+// the loop is one of these, so the count of DMA instructions issued after a
+// stage is exactly the vmcnt value that guarantees that stage has landed.
+// base and lds_addr must be the same in every lane.
+__device__ __forceinline__ void dma16(const void *base, uint32_t voff, uint32_t lds_addr)
 {
     const uint32_t m = __builtin_amdgcn_readfirstlane(lds_addr);
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(m) : "memory", "m0");
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "s"(m) : "memory", "m0");
 }
-__device__ __forceinline__ void dma4(const void *gptr, uint32_t lds_addr)
+__device__ __forceinline__ void dma4(const void *base, uint32_t voff, uint32_t lds_addr)
 {
     const uint32_t m = __builtin_amdgcn_readfirstlane(lds_addr);
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(gptr), "s"(m) : "memory", "m0");
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(base), "s"(m) : "memory", "m0");
 }
 
 // All of this wave's LDS reads have returned and at most kAhead DMA
@@ -90,6 +93,14 @@ __device__ __forceinline__ void wait_and_barrier()
     asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kAhead) : "memory");
 }
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Persistent kernel: one workgroup per CU walks tiles b, b + G, b + 2G, ...
+// (G = grid size).  Each tile: 256 x 256 outputs, four waves of 128 x 128.
+// Between two tiles the next tile's first two K steps are put in flight
+// before the finished tile's epilogue runs, so the epilogue hides the start
+// latency of the next tile.
 template <bool kTiled>
 __global__ __launch_bounds__(256) void gemm_mx_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
                                                       const uint8_t *__restrict__ B, const uint8_t *__restrict__ Bs,
@@ -97,161 +108,253 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(const uint8_t *__restrict_
                                                       int64_t ldc, int c_bf16, int vec_ok, int tiles_m, int tiles_n)
 {
     __shared__ __attribute__((aligned(1024))) uint8_t lds[kLdsBytes];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave: keeps LDS addresses scalar
     const int wm = wave >> 1, wn = wave & 1;
-    int tm, tn;
-    tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);
-    const int m0 = tm * kBM, n0 = tn * kBN;
+    const int fr = lane & 31, fh = lane >> 5;
     const uint32_t KB = (uint32_t)K >> 1;  // code bytes per row
     const uint32_t KS = (uint32_t)K >> 5;  // scale bytes per row
     const int nk = K >> 7;                 // 128-wide K steps
     const uint32_t Mp = ((uint32_t)M + 31) & ~31u, Np = ((uint32_t)N + 31) & ~31u;
     const uint32_t lds_base = (uint32_t)(uintptr_t)lds;
-
-    // LDS image of a stage: the codes of 32 rows x 64 K elements are one
-    // 1 KiB block in matrix-core lane order (lane l's 16 bytes = row l mod 32,
-    // K half l / 32), blocks ordered (row group g, K half kk) -> 2 g + kk.
-    // Wave w copies blocks 4w .. 4w+3 of A and of B.  In the tiled layout a
-    // block is 1 KiB of contiguous global memory; in the linear layout lane l
-    // of block b reads row 32 (b / 2) + l mod 32, bytes 32 (b mod 2) +
-    // 16 (l / 32) of the step.  Rows past the operand re-read its last row
-    // (linear) or row group (tiled); their results are never stored.
-    uint32_t a_goff[4], b_goff[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int b = wave * 4 + i;
-        if (kTiled) {
-            const uint32_t ga = min((uint32_t)(m0 / 32 + (b >> 1)), Mp / 32 - 1);
-            const uint32_t gb = min((uint32_t)(n0 / 32 + (b >> 1)), Np / 32 - 1);
-            a_goff[i] = (ga * (uint32_t)(K >> 6) + (b & 1)) * 1024 + lane * 16;
-            b_goff[i] = (gb * (uint32_t)(K >> 6) + (b & 1)) * 1024 + lane * 16;
-        } else {
-            const int r = 32 * (b >> 1) + (lane & 31);
-            const uint32_t col = 32 * (b & 1) + 16 * (lane >> 5);
-            a_goff[i] = (uint32_t)min(m0 + r, M - 1) * KB + col;
-            b_goff[i] = (uint32_t)min(n0 + r, N - 1) * KB + col;
-        }
-    }
+    const int ntiles = tiles_m * tiles_n;
     const uint32_t code_step = kTiled ? 2048u : 64u;
-    // scales: wave w copies rows 64 w + lane of A and of B (one u32 per row per step)
-    uint32_t as_goff, bs_goff, as_step, bs_step;
-    if (kTiled) {
-        as_goff = min((uint32_t)(m0 + wave * 64 + lane), Mp - 1) * 4;
-        bs_goff = min((uint32_t)(n0 + wave * 64 + lane), Np - 1) * 4;
-        as_step = Mp * 4;
-        bs_step = Np * 4;
-    } else {
-        as_goff = (uint32_t)min(m0 + wave * 64 + lane, M - 1) * KS;
-        bs_goff = (uint32_t)min(n0 + wave * 64 + lane, N - 1) * KS;
-        as_step = bs_step = 4;
-    }
 
-    auto issue = [&](int ks, int slot) {
-        const uint32_t st = lds_base + slot * kStageBytes;
-        const uint32_t kc = (uint32_t)ks * code_step;
+    // Per-tile DMA sources.  LDS image of a stage: the codes of 32 rows x 64 K
+    // elements are one 1 KiB block in matrix-core lane order (lane l's 16
+    // bytes = row l mod 32, K half l / 32), blocks ordered (row group g, K
+    // half kk) -> 2 g + kk.  Wave w copies blocks 4w .. 4w+3 of A and of B
+    // and the scale words of rows 64 w + lane.  In the tiled layout a block is
+    // 1 KiB of contiguous global memory; in the linear layout lane l of block
+    // b reads row 32 (b / 2) + l mod 32, bytes 32 (b mod 2) + 16 (l / 32) of
+    // the step.  Rows past the operand re-read its last row (linear) or row
+    // group (tiled); their results are never stored.
+    uint32_t a_goff[4], b_goff[4], as_goff, bs_goff, as_step, bs_step;
+    int m0 = 0, n0 = 0;
+    auto setup = [&](int tile) {
+        int tm, tn;
+        tile_coords(tile, tiles_m, tiles_n, tm, tn);
+        m0 = tm * kBM;
+        n0 = tn * kBN;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            dma16(A + a_goff[i] + kc, st + (wave * 4 + i) * 1024);
-            dma16(B + b_goff[i] + kc, st + kCodeBytes + (wave * 4 + i) * 1024);
+            const int b = wave * 4 + i;
+            if (kTiled) {
+                const uint32_t ga = min((uint32_t)(m0 / 32 + (b >> 1)), Mp / 32 - 1);
+                const uint32_t gb = min((uint32_t)(n0 / 32 + (b >> 1)), Np / 32 - 1);
+                a_goff[i] = (ga * (uint32_t)(K >> 6) + (b & 1)) * 1024 + lane * 16;
+                b_goff[i] = (gb * (uint32_t)(K >> 6) + (b & 1)) * 1024 + lane * 16;
+            } else {
+                const int r = 32 * (b >> 1) + (lane & 31);
+                const uint32_t col = 32 * (b & 1) + 16 * (lane >> 5);
+                a_goff[i] = (uint32_t)min(m0 + r, M - 1) * KB + col;
+                b_goff[i] = (uint32_t)min(n0 + r, N - 1) * KB + col;
+            }
         }
-        dma4(As + as_goff + (uint32_t)ks * as_step, st + kScaleOff + wave * 256);
-        dma4(Bs + bs_goff + (uint32_t)ks * bs_step, st + kScaleOff + kBM * 4 + wave * 256);
+        if (kTiled) {
+            as_goff = min((uint32_t)(m0 + wave * 64 + lane), Mp - 1) * 4;
+            bs_goff = min((uint32_t)(n0 + wave * 64 + lane), Np - 1) * 4;
+            as_step = Mp * 4;
+            bs_step = Np * 4;
+        } else {
+            as_goff = (uint32_t)min(m0 + wave * 64 + lane, M - 1) * KS;
+            bs_goff = (uint32_t)min(n0 + wave * 64 + lane, N - 1) * KS;
+            as_step = bs_step = 4;
+        }
+    };
+    auto dma_piece = [&](int ks, int slot, int d) {  // the d-th of this wave's 10 DMA instructions of a step
+        const uint32_t st = lds_base + slot * kStageBytes;
+        if (d < 8) {
+            const int i = d >> 1;
+            if ((d & 1) == 0)
+                dma16(A + (size_t)ks * code_step, a_goff[i], st + (wave * 4 + i) * 1024);
+            else
+                dma16(B + (size_t)ks * code_step, b_goff[i], st + kCodeBytes + (wave * 4 + i) * 1024);
+        } else if (d == 8) {
+            dma4(As + (size_t)ks * as_step, as_goff, st + kScaleOff + wave * 256);
+        } else {
+            dma4(Bs + (size_t)ks * bs_step, bs_goff, st + kScaleOff + kBM * 4 + wave * 256);
+        }
+    };
+    // a tile's first two K steps (steps past the end re-read the last step)
+    auto prologue = [&]() {
+#pragma unroll
+        for (int s2 = 0; s2 < kStages - 1; ++s2)
+#pragma unroll
+            for (int d = 0; d < kDmaPerStage; ++d) dma_piece(min(s2, nk - 1), s2, d);
     };
 
-    const int fr = lane & 31, fh = lane >> 5;
+    auto frag = [&](const uint8_t *st, int operand, int i, int kk) -> v8i_t {
+        const int g = operand == 0 ? wm * 4 + i : wn * 4 + i;
+        const uint4 t = *reinterpret_cast<const uint4 *>(st + operand * kCodeBytes + (g * 2 + kk) * 1024 + lane * 16);
+        return (v8i_t){(int)t.x, (int)t.y, (int)t.z, (int)t.w, 0, 0, 0, 0};
+    };
+    auto scale_word = [&](const uint8_t *st, int operand, int i) -> uint32_t {
+        const int row = (operand == 0 ? wm * 128 : wn * 128) + i * 32 + fr;
+        return *reinterpret_cast<const uint32_t *>(st + kScaleOff + operand * kBM * 4 + row * 4);
+    };
 
     v16f_t acc[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = (v16f_t){};
+    v8i_t fa0[4], fb0[4], fa1[4], fb1[4];
+    uint32_t sa[4], sb[4], nsa[4], nsb[4];
 
-    // prologue: kStages - 1 steps in flight (steps past the end re-read the
-    // last step into free slots, so the loop's wait count never changes)
-#pragma unroll
-    for (int s = 0; s < kStages - 1; ++s) issue(min(s, nk - 1), s);
-
-    for (int ks = 0; ks < nk; ++ks) {
-        const int slot = ks % kStages;
-        wait_and_barrier<(kStages - 2) * kDmaPerStage>();
-        // the slot read in step ks-1 is free for step ks + kStages - 1
-        issue(min(ks + kStages - 1, nk - 1), (ks + kStages - 1) % kStages);
-
-        const uint8_t *st = lds + slot * kStageBytes;
-        uint32_t sa[4], sb[4];
+    int tile = blockIdx.x;
+    setup(tile);
+    prologue();
+    for (;;) {
+        // stage 0 of this tile has landed (vmcnt(0) also covers the previous
+        // tile's output stores, which share the counter)
+        wait_and_barrier<0>();
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            sa[i] = *reinterpret_cast<const uint32_t *>(st + kScaleOff + (wm * 128 + i * 32 + fr) * 4);
-            sb[i] = *reinterpret_cast<const uint32_t *>(st + kScaleOff + kBM * 4 + (wn * 128 + i * 32 + fr) * 4);
+            fa0[i] = frag(lds, 0, i, 0);
+            fb0[i] = frag(lds, 1, i, 0);
+            sa[i] = scale_word(lds, 0, i);
+            sb[i] = scale_word(lds, 1, i);
         }
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            v8i_t af[4], bfr[4];
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[i][j] = (v16f_t){};
+
+        // Software pipeline.  A 128-wide K step is two 64-wide halves
+        // (kk = 0, 1); its fragments are read from LDS one half ahead of the
+        // matrix cores and every memory instruction is issued between two
+        // MFMAs, so LDS reads, DMA issue and MFMAs overlap:
+        //   phase A of step ks: MFMAs of half 0 (operands in registers),
+        //     interleaved with half of the DMA of step ks+2 (into the slot of
+        //     step ks-1, free since the previous barrier) and the LDS reads
+        //     of half 1 of step ks;
+        //   barrier: step ks+1 has landed in LDS for every wave;
+        //   phase B: MFMAs of half 1, interleaved with the rest of the DMA of
+        //     step ks+2 and the LDS reads of half 0 and the scales of ks+1.
+        for (int ks = 0; ks < nk; ++ks) {
+            const uint8_t *st = lds + (ks % kStages) * kStageBytes;
+            const uint8_t *stn = lds + ((ks + 1) % kStages) * kStageBytes;  // a re-read copy past the end
+            const int dma_step = min(ks + kStages - 1, nk - 1), dma_slot = (ks + kStages - 1) % kStages;
+#pragma unroll
+            for (int t = 0; t < 16; ++t) {
+                const int i = t >> 2, j = t & 3;
+                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa0[i], fb0[j], acc[i][j], 4, 4, 0,
+                                                                             (int)(sa[i] >> (8 * fh)), 0,
+                                                                             (int)(sb[j] >> (8 * fh)));
+                if (t < kDmaPerPhase) dma_piece(dma_step, dma_slot, t);
+                if (t < 4) fa1[t] = frag(st, 0, t, 1);
+                else if (t < 8) fb1[t - 4] = frag(st, 1, t - 4, 1);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            // step ks+1's DMA was issued one step ago; only this step's first
+            // kDmaPerPhase instructions may still be in flight
+            wait_and_barrier<kDmaPerPhase>();
+#pragma unroll
+            for (int t = 0; t < 16; ++t) {
+                const int i = t >> 2, j = t & 3;
+                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa1[i], fb1[j], acc[i][j], 4, 4, 0,
+                                                                             (int)(sa[i] >> (8 * (2 + fh))), 0,
+                                                                             (int)(sb[j] >> (8 * (2 + fh))));
+                if (t < kDmaPerPhase) dma_piece(dma_step, dma_slot, kDmaPerPhase + t);
+                if (t < 4) fa0[t] = frag(stn, 0, t, 0);
+                else if (t < 8) fb0[t - 4] = frag(stn, 1, t - 4, 0);
+                else if (t < 12) nsa[t - 8] = scale_word(stn, 0, t - 8);
+                else nsb[t - 12] = scale_word(stn, 1, t - 12);
+                __builtin_amdgcn_sched_barrier(0);
+            }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const uint4 ta = *reinterpret_cast<const uint4 *>(st + ((wm * 4 + i) * 2 + kk) * 1024 + lane * 16);
-                const uint4 tb =
-                    *reinterpret_cast<const uint4 *>(st + kCodeBytes + ((wn * 4 + i) * 2 + kk) * 1024 + lane * 16);
-                af[i] = (v8i_t){(int)ta.x, (int)ta.y, (int)ta.z, (int)ta.w, 0, 0, 0, 0};
-                bfr[i] = (v8i_t){(int)tb.x, (int)tb.y, (int)tb.z, (int)tb.w, 0, 0, 0, 0};
+                sa[i] = nsa[i];
+                sb[i] = nsb[i];
             }
-            const int sh = 8 * (2 * kk + fh);  // this lane's block within the 128-wide step
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                        af[i], bfr[j], acc[i][j], 4, 4, 0, (int)(sa[i] >> sh), 0, (int)(sb[j] >> sh));
         }
-    }
-    // drain the re-read steps still in flight, and let every wave finish its
-    // last LDS reads before the ring is reused for the epilogue
-    wait_and_barrier<0>();
+        // the ring is idle: every DMA landed, every wave finished its reads
+        wait_and_barrier<0>();
+        const int tm0 = m0, tn0 = n0;
+        const int next = tile + (int)gridDim.x;
+        if (next < ntiles) {
+            setup(next);
+            prologue();
+        }
 
-    // epilogue: each wave stages a 32 x 128 band of alpha * acc in its own LDS
-    // region (row pitch padded by 16 bytes), then writes it out in contiguous
-    // 16-byte pieces: 256 contiguous bytes per row of the band.
-    const int esize = c_bf16 ? 2 : 4;
-    const int pitch = 128 * esize + 16;
-    uint8_t *ep = lds + wave * (32 * (128 * 4 + 16));
-    const int row_base = m0 + wm * 128, col_base = n0 + wn * 128;
+        // Epilogue: each wave stages its 128 x 128 accumulators in its own
+        // LDS region, 16 rows at a time in fp32 (row pitch padded by 16
+        // bytes), straight from the accumulator registers; then every lane
+        // reads back contiguous pieces, scales them by alpha, converts
+        // (bf16: v_cvt_pk_bf16_f32, round to nearest even) and writes 16
+        // bytes per store.  Nothing else of the tile needs registers here:
+        // converting in the accumulator layout instead makes the compiler
+        // copy the accumulators to VGPRs and spill.
+        uint8_t *ep = lds + kRingBytes + wave * kEpiWaveBytes;
+        const int row_base = tm0 + wm * 128, col_base = tn0 + wn * 128;
+        // The epilogue's lane-derived offsets are recomputed per tile from an
+        // opaque copy of the lane index: hoisted out of the tile loop they
+        // would stay live across the K loop and spill to scratch, whose
+        // reloads wait on the whole vector-memory counter (the next tile's
+        // DMA included).
+        int el;
+        asm volatile("v_mov_b32 %0, %1" : "=v"(el) : "v"(lane));
+        const int efr = el & 31, efh = el >> 5;
+        {
+            constexpr int pitch = 512 + 16;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+            for (int i = 0; i < 4; ++i) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+                for (int half = 0; half < 2; ++half) {  // rows 16 half .. +15 of the band
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int rl = 8 * (r >> 2) + 4 * fh + (r & 3);
-                const int cl = j * 32 + fr;
-                const float v = alpha * acc[i][j][r];
-                if (c_bf16)
-                    *reinterpret_cast<uint16_t *>(ep + rl * pitch + cl * 2) = (uint16_t)f32_to_bf16_rne(v);
-                else
-                    *reinterpret_cast<float *>(ep + rl * pitch + cl * 4) = v;
-            }
-        }
-        // the band is 32 rows x (128 * esize) bytes = 16-byte pieces per row: 16 (bf16) or 32 (fp32)
-        const int per_row = 8 * esize;
-        const int pieces = 32 * per_row;
-        for (int pc = lane; pc < pieces; pc += 64) {
-            const int rl = pc / per_row, cp = pc - rl * per_row;
-            const int row = row_base + i * 32 + rl;
-            const int col = col_base + cp * (16 / esize);
-            if (row >= M) continue;
-            const uint8_t *srcp = ep + rl * pitch + cp * 16;
-            uint8_t *dstp = reinterpret_cast<uint8_t *>(C) + ((int64_t)row * ldc + col) * esize;
-            if (vec_ok && col + 16 / esize <= N) {
-                *reinterpret_cast<uint4 *>(dstp) = *reinterpret_cast<const uint4 *>(srcp);
-            } else {
-                for (int e = 0; e < 16 / esize; ++e)
-                    if (col + e < N) {
-                        if (c_bf16)
-                            reinterpret_cast<uint16_t *>(dstp)[e] = reinterpret_cast<const uint16_t *>(srcp)[e];
-                        else
-                            reinterpret_cast<float *>(dstp)[e] = reinterpret_cast<const float *>(srcp)[e];
+                    for (int j = 0; j < 4; ++j) {
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const int rl = 8 * (r >> 2) + 4 * efh + (r & 3);
+                            if ((r >> 3) != half) continue;
+                            *reinterpret_cast<float *>(ep + (rl & 15) * pitch + (j * 32 + efr) * 4) = acc[i][j][r];
+                        }
                     }
+                    if (c_bf16) {
+                        // 16 rows x 128 bf16 = 256 pieces of 16 bytes, 4 per lane
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) {
+                            const int pc = el + 64 * u;
+                            const int rl = pc >> 4, cp = pc & 15;
+                            const int row = row_base + i * 32 + half * 16 + rl, col = col_base + cp * 8;
+                            const float4 lo = *reinterpret_cast<const float4 *>(ep + rl * pitch + cp * 32);
+                            const float4 hi = *reinterpret_cast<const float4 *>(ep + rl * pitch + cp * 32 + 16);
+                            uint4 o;
+                            o.x = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){alpha * lo.x, alpha * lo.y}, bf16x2_t));
+                            o.y = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){alpha * lo.z, alpha * lo.w}, bf16x2_t));
+                            o.z = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){alpha * hi.x, alpha * hi.y}, bf16x2_t));
+                            o.w = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){alpha * hi.z, alpha * hi.w}, bf16x2_t));
+                            if (row >= M) continue;
+                            uint16_t *dstp = reinterpret_cast<uint16_t *>(C) + (int64_t)row * ldc + col;
+                            if (vec_ok && col + 8 <= N) {
+                                *reinterpret_cast<uint4 *>(dstp) = o;
+                            } else {
+                                const uint16_t *ov = reinterpret_cast<const uint16_t *>(&o);
+                                for (int e = 0; e < 8; ++e)
+                                    if (col + e < N) dstp[e] = ov[e];
+                            }
+                        }
+                    } else {
+#pragma unroll
+                        for (int u = 0; u < 8; ++u) {
+                            const int pc = el + 64 * u;
+                            const int rl = pc >> 5, cp = pc & 31;
+                            const int row = row_base + i * 32 + half * 16 + rl, col = col_base + cp * 4;
+                            float4 v = *reinterpret_cast<const float4 *>(ep + rl * pitch + cp * 16);
+                            v.x *= alpha; v.y *= alpha; v.z *= alpha; v.w *= alpha;
+                            if (row >= M) continue;
+                            float *dstp = reinterpret_cast<float *>(C) + (int64_t)row * ldc + col;
+                            if (vec_ok && col + 4 <= N) {
+                                *reinterpret_cast<float4 *>(dstp) = v;
+                            } else {
+                                const float *vv = reinterpret_cast<const float *>(&v);
+                                for (int e = 0; e < 4; ++e)
+                                    if (col + e < N) dstp[e] = vv[e];
+                            }
+                        }
+                    }
+                }
             }
         }
+        if (next >= ntiles) break;
+        tile = next;
     }
 }
 
@@ -285,12 +388,19 @@ int launch_gemm_mx(const GemmArgs &g, hipStream_t st)
     auto *as = reinterpret_cast<const uint8_t *>(g.a_scales);
     auto *b = reinterpret_cast<const uint8_t *>(g.b_codes);
     auto *bs = reinterpret_cast<const uint8_t *>(g.b_scales);
+    // persistent grid: one workgroup per CU (the kernel's 136 KiB of LDS
+    // allows no more), never more workgroups than tiles
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
+                                                 hipSuccess || cus <= 0)
+        return 1;
+    const int grid = min(tiles_m * tiles_n, cus);
     if (g.tiled)
-        hipLaunchKernelGGL(gemm_mx_kernel<true>, dim3(tiles_m * tiles_n), dim3(256), 0, st, a, as, b, bs, M, N, K,
-                           g.alpha, g.c, g.ldc, (int)g.c_bf16, vec_ok, tiles_m, tiles_n);
+        hipLaunchKernelGGL(gemm_mx_kernel<true>, dim3(grid), dim3(256), 0, st, a, as, b, bs, M, N, K, g.alpha, g.c,
+                           g.ldc, (int)g.c_bf16, vec_ok, tiles_m, tiles_n);
     else
-        hipLaunchKernelGGL(gemm_mx_kernel<false>, dim3(tiles_m * tiles_n), dim3(256), 0, st, a, as, b, bs, M, N, K,
-                           g.alpha, g.c, g.ldc, (int)g.c_bf16, vec_ok, tiles_m, tiles_n);
+        hipLaunchKernelGGL(gemm_mx_kernel<false>, dim3(grid), dim3(256), 0, st, a, as, b, bs, M, N, K, g.alpha, g.c,
+                           g.ldc, (int)g.c_bf16, vec_ok, tiles_m, tiles_n);
     return hipGetLastError() == hipSuccess ? 0 : 1;
 }
 
