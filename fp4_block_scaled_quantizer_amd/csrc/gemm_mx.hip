@@ -28,6 +28,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "fp4q_device.h"
 #include "fp4q_internal.h"
 
@@ -44,7 +46,8 @@ constexpr int kCodeBytes = kBM * 64;                        // one operand's cod
 constexpr int kScaleOff = 2 * kCodeBytes;                   // A scales, then B scales (u32 per row)
 constexpr int kStageBytes = 2 * kCodeBytes + (kBM + kBN) * 4;  // 34 KiB
 constexpr int kRingBytes = kStages * kStageBytes;           // 102 KiB
-constexpr int kEpiWaveBytes = 16 * (512 + 16);              // one wave's epilogue band: 16 x 128 fp32, padded rows
+constexpr int kEpiPitch = 64 * 4 + 16;                      // epilogue staging row: 64 fp32 + 16 bytes of padding
+constexpr int kEpiWaveBytes = 32 * kEpiPitch;               // one wave's epilogue chunk: 32 x 64 fp32
 constexpr int kLdsBytes = kRingBytes + 4 * kEpiWaveBytes;   // 136 KiB
 constexpr int kDmaPerStage = 10;                            // DMA instructions per wave per stage
 constexpr int kDmaPerPhase = kDmaPerStage / 2;
@@ -235,9 +238,9 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(const uint8_t *__restrict_
 #pragma unroll
             for (int t = 0; t < 16; ++t) {
                 const int i = t >> 2, j = t & 3;
-                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa0[i], fb0[j], acc[i][j], 4, 4, 0,
-                                                                             (int)(sa[i] >> (8 * fh)), 0,
-                                                                             (int)(sb[j] >> (8 * fh)));
+                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb0[j], fa0[i], acc[i][j], 4, 4, 0,
+                                                                             (int)(sb[j] >> (8 * fh)), 0,
+                                                                             (int)(sa[i] >> (8 * fh)));
                 if (t < kDmaPerPhase) dma_piece(dma_step, dma_slot, t);
                 if (t < 4) fa1[t] = frag(st, 0, t, 1);
                 else if (t < 8) fb1[t - 4] = frag(st, 1, t - 4, 1);
@@ -249,9 +252,9 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(const uint8_t *__restrict_
 #pragma unroll
             for (int t = 0; t < 16; ++t) {
                 const int i = t >> 2, j = t & 3;
-                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa1[i], fb1[j], acc[i][j], 4, 4, 0,
-                                                                             (int)(sa[i] >> (8 * (2 + fh))), 0,
-                                                                             (int)(sb[j] >> (8 * (2 + fh))));
+                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb1[j], fa1[i], acc[i][j], 4, 4, 0,
+                                                                             (int)(sb[j] >> (8 * (2 + fh))), 0,
+                                                                             (int)(sa[i] >> (8 * (2 + fh))));
                 if (t < kDmaPerPhase) dma_piece(dma_step, dma_slot, kDmaPerPhase + t);
                 if (t < 4) fa0[t] = frag(stn, 0, t, 0);
                 else if (t < 8) fb0[t - 4] = frag(stn, 1, t - 4, 0);
@@ -274,53 +277,93 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(const uint8_t *__restrict_
             prologue();
         }
 
-        // Epilogue: each wave stages its 128 x 128 accumulators in its own
-        // LDS region, 16 rows at a time in fp32 (row pitch padded by 16
-        // bytes), straight from the accumulator registers; then every lane
-        // reads back contiguous pieces, scales them by alpha, converts
-        // (bf16: v_cvt_pk_bf16_f32, round to nearest even) and writes 16
-        // bytes per store.  Nothing else of the tile needs registers here:
-        // converting in the accumulator layout instead makes the compiler
-        // copy the accumulators to VGPRs and spill.
+        // Epilogue.  The B fragment is the matrix cores' first operand, so
+        // register r of lane l holds C[row (l mod 32)][col 8 (r/4) + 4 (l/32)
+        // + r mod 4] of its 32 x 32 block: each aligned group of four
+        // accumulator registers is four consecutive columns of one row.  A
+        // wave writes its 128 x 128 block in eight chunks of 32 rows x 64
+        // columns: 16-byte LDS writes straight from the accumulator registers
+        // (fp32, rows padded by 16 bytes), then 16-byte LDS reads of row
+        // pieces, alpha, conversion (bf16: v_cvt_pk_bf16_f32, round to
+        // nearest even) and 16-byte global stores.  Fewest instructions per
+        // output: with one wave per SIMD every instruction costs a full issue
+        // cycle that nothing else hides.
         uint8_t *ep = lds + kRingBytes + wave * kEpiWaveBytes;
         const int row_base = tm0 + wm * 128, col_base = tn0 + wn * 128;
-        // The epilogue's lane-derived offsets are recomputed per tile from an
-        // opaque copy of the lane index: hoisted out of the tile loop they
-        // would stay live across the K loop and spill to scratch, whose
-        // reloads wait on the whole vector-memory counter (the next tile's
-        // DMA included).
+        // Lane-derived offsets are recomputed per tile from an opaque copy of
+        // the lane index: hoisted out of the tile loop they would stay live
+        // across the K loop and spill to scratch, whose reloads wait on the
+        // whole vector-memory counter (the next tile's DMA included).
         int el;
         asm volatile("v_mov_b32 %0, %1" : "=v"(el) : "v"(lane));
         const int efr = el & 31, efh = el >> 5;
-        {
-            constexpr int pitch = 512 + 16;
+        const bool full = vec_ok && row_base + 128 <= M && col_base + 128 <= N;
+        // alpha == 1 (the common case) skips the multiplies; either way the
+        // chunk loop is branch-free apart from the full-tile test
+        auto epilogue = [&](auto scale_tag) {
+            constexpr bool kScale = decltype(scale_tag)::value;
+            const int esize = c_bf16 ? 2 : 4;
+            // LDS -> registers: one 16-byte output piece (bf16: 8 columns from
+            // two fp32 reads; fp32: 4 columns) of the staged 32 x 64 chunk
+            auto piece_bf16 = [&](int rl, int cp) -> uint4 {
+                float4 lo = *reinterpret_cast<const float4 *>(ep + rl * kEpiPitch + cp * 32);
+                float4 hi = *reinterpret_cast<const float4 *>(ep + rl * kEpiPitch + cp * 32 + 16);
+                if (kScale) {
+                    lo.x *= alpha; lo.y *= alpha; lo.z *= alpha; lo.w *= alpha;
+                    hi.x *= alpha; hi.y *= alpha; hi.z *= alpha; hi.w *= alpha;
+                }
+                uint4 o;
+                o.x = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo.x, lo.y}, bf16x2_t));
+                o.y = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo.z, lo.w}, bf16x2_t));
+                o.z = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){hi.x, hi.y}, bf16x2_t));
+                o.w = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){hi.z, hi.w}, bf16x2_t));
+                return o;
+            };
+            auto piece_f32 = [&](int rl, int cp) -> uint4 {
+                float4 v = *reinterpret_cast<const float4 *>(ep + rl * kEpiPitch + cp * 16);
+                if (kScale) {
+                    v.x *= alpha; v.y *= alpha; v.z *= alpha; v.w *= alpha;
+                }
+                return __builtin_bit_cast(uint4, v);
+            };
+            // lane's byte offset inside a chunk: bf16 pieces are (row el/8 + 8u,
+            // 8 columns at 8 (el mod 8)), fp32 pieces (row el/16 + 4u, 4 columns
+            // at 4 (el mod 16)); the launcher keeps 32 rows of C under 2 GiB
+            const uint32_t lane_off = c_bf16 ? ((uint32_t)(el >> 3) * (uint32_t)ldc + (el & 7) * 8) * 2
+                                             : ((uint32_t)(el >> 4) * (uint32_t)ldc + (el & 15) * 4) * 4;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
 #pragma unroll
-                for (int half = 0; half < 2; ++half) {  // rows 16 half .. +15 of the band
+                for (int jp = 0; jp < 2; ++jp) {
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
+                    for (int jj = 0; jj < 2; ++jj) {
+                        const v16f_t &a = acc[i][2 * jp + jj];
 #pragma unroll
-                        for (int r = 0; r < 16; ++r) {
-                            const int rl = 8 * (r >> 2) + 4 * efh + (r & 3);
-                            if ((r >> 3) != half) continue;
-                            *reinterpret_cast<float *>(ep + (rl & 15) * pitch + (j * 32 + efr) * 4) = acc[i][j][r];
-                        }
+                        for (int g = 0; g < 4; ++g)
+                            *reinterpret_cast<float4 *>(ep + efr * kEpiPitch + (jj * 32 + 8 * g + 4 * efh) * 4) =
+                                make_float4(a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]);
                     }
-                    if (c_bf16) {
-                        // 16 rows x 128 bf16 = 256 pieces of 16 bytes, 4 per lane
+                    const int row0 = row_base + i * 32, col0 = col_base + jp * 64;
+                    if (full) {
+                        // whole chunk inside C and 16-byte aligned: no guards
+                        uint8_t *base = reinterpret_cast<uint8_t *>(C) + ((int64_t)row0 * ldc + col0) * esize;
+                        if (c_bf16) {
+#pragma unroll
+                            for (int u = 0; u < 4; ++u)
+                                *reinterpret_cast<uint4 *>(base + (int64_t)u * 8 * ldc * 2 + lane_off) =
+                                    piece_bf16((el >> 3) + 8 * u, el & 7);
+                        } else {
+#pragma unroll
+                            for (int u = 0; u < 8; ++u)
+                                *reinterpret_cast<uint4 *>(base + (int64_t)u * 4 * ldc * 4 + lane_off) =
+                                    piece_f32((el >> 4) + 4 * u, el & 15);
+                        }
+                    } else if (c_bf16) {
 #pragma unroll
                         for (int u = 0; u < 4; ++u) {
-                            const int pc = el + 64 * u;
-                            const int rl = pc >> 4, cp = pc & 15;
-                            const int row = row_base + i * 32 + half * 16 + rl, col = col_base + cp * 8;
-                            const float4 lo = *reinterpret_cast<const float4 *>(ep + rl * pitch + cp * 32);
-                            const float4 hi = *reinterpret_cast<const float4 *>(ep + rl * pitch + cp * 32 + 16);
-                            uint4 o;
-                            o.x = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){alpha * lo.x, alpha * lo.y}, bf16x2_t));
-                            o.y = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){alpha * lo.z, alpha * lo.w}, bf16x2_t));
-                            o.z = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){alpha * hi.x, alpha * hi.y}, bf16x2_t));
-                            o.w = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){alpha * hi.z, alpha * hi.w}, bf16x2_t));
+                            const int rl = (el >> 3) + 8 * u, cp = el & 7;
+                            const uint4 o = piece_bf16(rl, cp);
+                            const int row = row0 + rl, col = col0 + cp * 8;
                             if (row >= M) continue;
                             uint16_t *dstp = reinterpret_cast<uint16_t *>(C) + (int64_t)row * ldc + col;
                             if (vec_ok && col + 8 <= N) {
@@ -334,17 +377,15 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(const uint8_t *__restrict_
                     } else {
 #pragma unroll
                         for (int u = 0; u < 8; ++u) {
-                            const int pc = el + 64 * u;
-                            const int rl = pc >> 5, cp = pc & 31;
-                            const int row = row_base + i * 32 + half * 16 + rl, col = col_base + cp * 4;
-                            float4 v = *reinterpret_cast<const float4 *>(ep + rl * pitch + cp * 16);
-                            v.x *= alpha; v.y *= alpha; v.z *= alpha; v.w *= alpha;
+                            const int rl = (el >> 4) + 4 * u, cp = el & 15;
+                            const uint4 o = piece_f32(rl, cp);
+                            const int row = row0 + rl, col = col0 + cp * 4;
                             if (row >= M) continue;
                             float *dstp = reinterpret_cast<float *>(C) + (int64_t)row * ldc + col;
                             if (vec_ok && col + 4 <= N) {
-                                *reinterpret_cast<float4 *>(dstp) = v;
+                                *reinterpret_cast<uint4 *>(dstp) = o;
                             } else {
-                                const float *vv = reinterpret_cast<const float *>(&v);
+                                const float *vv = reinterpret_cast<const float *>(&o);
                                 for (int e = 0; e < 4; ++e)
                                     if (col + e < N) dstp[e] = vv[e];
                             }
@@ -352,7 +393,11 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(const uint8_t *__restrict_
                     }
                 }
             }
-        }
+        };
+        if (alpha != 1.0f)
+            epilogue(std::true_type{});
+        else
+            epilogue(std::false_type{});
         if (next >= ntiles) break;
         tile = next;
     }
@@ -383,7 +428,9 @@ int launch_gemm_mx(const GemmArgs &g, hipStream_t st)
     }
     const int tiles_m = (M + kBM - 1) / kBM, tiles_n = (N + kBN - 1) / kBN;
     const int esize = g.c_bf16 ? 2 : 4;
-    const int vec_ok = ((uintptr_t)g.c % 16 == 0) && (g.ldc % (16 / esize) == 0);
+    // 16-byte output stores need a 16-byte aligned C and ldc; the fast
+    // epilogue also keeps a lane's in-chunk byte offset in 32 bits
+    const int vec_ok = ((uintptr_t)g.c % 16 == 0) && (g.ldc % (16 / esize) == 0) && g.ldc <= (int64_t(1) << 26);
     auto *a = reinterpret_cast<const uint8_t *>(g.a_codes);
     auto *as = reinterpret_cast<const uint8_t *>(g.a_scales);
     auto *b = reinterpret_cast<const uint8_t *>(g.b_codes);
