@@ -71,21 +71,26 @@ __device__ __forceinline__ void tile_coords(int bid, int tiles_m, int tiles_n, i
 
 // Global -> LDS copies that bypass VGPRs (gfx950 LDS DMA): lane i reads
 // base + voff_i (base a 64-bit scalar address, voff a 32-bit per-lane byte
-// offset) and writes its 16 (or 4) bytes to LDS address m0 + 16 i (4 i).
+// offset) and writes its 16 (or 4) bytes to LDS address m0 + 16 i (4 i),
+// m0 = lds_slot + kLdsOff (the add clobbers SCC, declared as such).
 // They are issued from inline assembly so that the only waits on them are
 // the explicit vmcnt waits of the K loop: every vector-memory instruction of
 // the loop is one of these, so the count of DMA instructions issued after a
 // stage is exactly the vmcnt value that guarantees that stage has landed.
-// base and lds_addr must be the same in every lane.
-__device__ __forceinline__ void dma16(const void *base, uint32_t voff, uint32_t lds_addr)
+// base and lds_slot must be the same in every lane (scalar operands).
+template <uint32_t kLdsOff>
+__device__ __forceinline__ void dma16(const void *base, uint32_t voff, uint32_t lds_slot)
 {
-    const uint32_t m = __builtin_amdgcn_readfirstlane(lds_addr);
-    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "s"(m) : "memory", "m0");
+    asm volatile("s_add_u32 m0, %2, %3\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "s"(lds_slot),
+                 "n"(kLdsOff)
+                 : "memory", "m0", "scc");
 }
-__device__ __forceinline__ void dma4(const void *base, uint32_t voff, uint32_t lds_addr)
+template <uint32_t kLdsOff>
+__device__ __forceinline__ void dma4(const void *base, uint32_t voff, uint32_t lds_slot)
 {
-    const uint32_t m = __builtin_amdgcn_readfirstlane(lds_addr);
-    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(base), "s"(m) : "memory", "m0");
+    asm volatile("s_add_u32 m0, %2, %3\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(base), "s"(lds_slot),
+                 "n"(kLdsOff)
+                 : "memory", "m0", "scc");
 }
 
 // All of this wave's LDS reads have returned and at most kAhead DMA
@@ -94,6 +99,16 @@ template <int kAhead>
 __device__ __forceinline__ void wait_and_barrier()
 {
     asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kAhead) : "memory");
+}
+
+// f(integral_constant<int, 0>) ... f(integral_constant<int, N-1>)
+template <int N, int I = 0, typename F>
+__device__ __forceinline__ void static_for(F &&f)
+{
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for<N, I + 1>(f);
+    }
 }
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -134,6 +149,11 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(const uint8_t *__restrict_
     // group (tiled); their results are never stored.
     uint32_t a_goff[4], b_goff[4], as_goff, bs_goff, as_step, bs_step;
     int m0 = 0, n0 = 0;
+    // Scalar sources of the K step the next DMA copies (dstep): advanced by
+    // one step after each step's DMA, never past the last step, so a
+    // pipeline running past the end re-reads the last step.
+    const uint8_t *pa = A, *pb = B, *pas = As, *pbs = Bs;
+    int dstep = 0;
     auto setup = [&](int tile) {
         int tm, tn;
         tile_coords(tile, tiles_m, tiles_n, tm, tn);
@@ -164,27 +184,63 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(const uint8_t *__restrict_
             bs_goff = (uint32_t)min(n0 + wave * 64 + lane, N - 1) * KS;
             as_step = bs_step = 4;
         }
+        pa = A;
+        pb = B;
+        pas = As;
+        pbs = Bs;
+        dstep = 0;
     };
-    auto dma_piece = [&](int ks, int slot, int d) {  // the d-th of this wave's 10 DMA instructions of a step
-        const uint32_t st = lds_base + slot * kStageBytes;
-        if (d < 8) {
-            const int i = d >> 1;
-            if ((d & 1) == 0)
-                dma16(A + (size_t)ks * code_step, a_goff[i], st + (wave * 4 + i) * 1024);
+    // the d-th of this wave's 10 DMA instructions of a step, into the stage
+    // at LDS address slot_addr
+    auto dma_piece = [&](uint32_t slot_addr, auto d_tag) {
+        constexpr int d = decltype(d_tag)::value;
+        const uint32_t wslot = slot_addr + wave * 4096;  // this wave's 4 KiB of each operand's codes
+        if constexpr (d < 8) {
+            constexpr int i = d >> 1;
+            if constexpr ((d & 1) == 0)
+                dma16<i * 1024>(pa, a_goff[i], wslot);
             else
-                dma16(B + (size_t)ks * code_step, b_goff[i], st + kCodeBytes + (wave * 4 + i) * 1024);
-        } else if (d == 8) {
-            dma4(As + (size_t)ks * as_step, as_goff, st + kScaleOff + wave * 256);
+                dma16<kCodeBytes + i * 1024>(pb, b_goff[i], wslot);
+        } else if constexpr (d == 8) {
+            dma4<kScaleOff>(pas, as_goff, slot_addr + wave * 256);
         } else {
-            dma4(Bs + (size_t)ks * bs_step, bs_goff, st + kScaleOff + kBM * 4 + wave * 256);
+            dma4<kScaleOff + kBM * 4>(pbs, bs_goff, slot_addr + wave * 256);
         }
     };
-    // a tile's first two K steps (steps past the end re-read the last step)
+    // Branch-free (a branch here would let the compiler sink the MFMAs of
+    // the step below it, out of their interleaved slots); the K loop spreads
+    // the four pointer updates over separate MFMA slots.
+    auto advance_ptr = [&](int which, uint32_t more) {
+        if (which == 0) {
+            pa += more * code_step;
+            asm volatile("" : "+s"(pa));
+        }
+        if (which == 1) {
+            pb += more * code_step;
+            asm volatile("" : "+s"(pb));
+        }
+        if (which == 2) {
+            pas += more * as_step;
+            asm volatile("" : "+s"(pas));
+        }
+        if (which == 3) {
+            pbs += more * bs_step;
+            asm volatile("" : "+s"(pbs));
+        }
+    };
+    auto advance = [&]() {
+        const uint32_t more = dstep < nk - 1 ? 1u : 0u;
+        for (int w = 0; w < 4; ++w) advance_ptr(w, more);
+        dstep += (int)more;
+    };
+    // a tile's first two K steps, into ring slots 0 and 1
     auto prologue = [&]() {
 #pragma unroll
-        for (int s2 = 0; s2 < kStages - 1; ++s2)
-#pragma unroll
-            for (int d = 0; d < kDmaPerStage; ++d) dma_piece(min(s2, nk - 1), s2, d);
+        for (int s2 = 0; s2 < kStages - 1; ++s2) {
+            const uint32_t slot_addr = lds_base + s2 * kStageBytes;
+            static_for<kDmaPerStage>([&](auto d) { dma_piece(slot_addr, d); });
+            advance();
+        }
     };
 
     auto frag = [&](const uint8_t *st, int operand, int i, int kk) -> v8i_t {
@@ -192,6 +248,10 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(const uint8_t *__restrict_
         const uint4 t = *reinterpret_cast<const uint4 *>(st + operand * kCodeBytes + (g * 2 + kk) * 1024 + lane * 16);
         return (v8i_t){(int)t.x, (int)t.y, (int)t.z, (int)t.w, 0, 0, 0, 0};
     };
+    // A lane's scale word of a 128-wide step holds the E8M0 bytes of K
+    // blocks 0..3; lanes 32..63 feed the matrix cores K blocks 1 and 3, so
+    // their word is shifted down one byte and both halves select byte 0
+    // (K half 0) or byte 2 (K half 1) with the instruction's byte select.
     auto scale_word = [&](const uint8_t *st, int operand, int i) -> uint32_t {
         const int row = (operand == 0 ? wm * 128 : wn * 128) + i * 32 + fr;
         return *reinterpret_cast<const uint32_t *>(st + kScaleOff + operand * kBM * 4 + row * 4);
@@ -212,8 +272,8 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(const uint8_t *__restrict_
         for (int i = 0; i < 4; ++i) {
             fa0[i] = frag(lds, 0, i, 0);
             fb0[i] = frag(lds, 1, i, 0);
-            sa[i] = scale_word(lds, 0, i);
-            sb[i] = scale_word(lds, 1, i);
+            sa[i] = scale_word(lds, 0, i) >> (8 * fh);
+            sb[i] = scale_word(lds, 1, i) >> (8 * fh);
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -231,42 +291,74 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(const uint8_t *__restrict_
         //   barrier: step ks+1 has landed in LDS for every wave;
         //   phase B: MFMAs of half 1, interleaved with the rest of the DMA of
         //     step ks+2 and the LDS reads of half 0 and the scales of ks+1.
+        // Ring slots rotate through three scalar offsets (current step,
+        // next step, DMA target) so that every LDS address is a scalar plus a
+        // constant.
+        uint32_t off_cur = 0, off_nxt = kStageBytes, off_dma = 2 * kStageBytes;
         for (int ks = 0; ks < nk; ++ks) {
-            const uint8_t *st = lds + (ks % kStages) * kStageBytes;
-            const uint8_t *stn = lds + ((ks + 1) % kStages) * kStageBytes;  // a re-read copy past the end
-            const int dma_step = min(ks + kStages - 1, nk - 1), dma_slot = (ks + kStages - 1) % kStages;
-#pragma unroll
-            for (int t = 0; t < 16; ++t) {
-                const int i = t >> 2, j = t & 3;
+            const uint8_t *st = lds + off_cur;
+            const uint8_t *stn = lds + off_nxt;  // a re-read copy past the end
+            const uint32_t dma_addr = lds_base + off_dma;
+            static_for<16>([&](auto t_tag) {
+                constexpr int t = decltype(t_tag)::value;
+                constexpr int i = t >> 2, j = t & 3;
                 acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb0[j], fa0[i], acc[i][j], 4, 4, 0,
-                                                                             (int)(sb[j] >> (8 * fh)), 0,
-                                                                             (int)(sa[i] >> (8 * fh)));
-                if (t < kDmaPerPhase) dma_piece(dma_step, dma_slot, t);
-                if (t < 4) fa1[t] = frag(st, 0, t, 1);
-                else if (t < 8) fb1[t - 4] = frag(st, 1, t - 4, 1);
+                                                                             (int)sb[j], 0, (int)sa[i]);
+                if constexpr (t < kDmaPerPhase) dma_piece(dma_addr, t_tag);
+                if constexpr (t < 4) fa1[t] = frag(st, 0, t, 1);
+                else if constexpr (t < 8) fb1[t - 4] = frag(st, 1, t - 4, 1);
                 __builtin_amdgcn_sched_barrier(0);
-            }
+            });
             // step ks+1's DMA was issued one step ago; only this step's first
             // kDmaPerPhase instructions may still be in flight
             wait_and_barrier<kDmaPerPhase>();
-#pragma unroll
-            for (int t = 0; t < 16; ++t) {
-                const int i = t >> 2, j = t & 3;
-                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb1[j], fa1[i], acc[i][j], 4, 4, 0,
-                                                                             (int)(sb[j] >> (8 * (2 + fh))), 0,
-                                                                             (int)(sa[i] >> (8 * (2 + fh))));
-                if (t < kDmaPerPhase) dma_piece(dma_step, dma_slot, kDmaPerPhase + t);
-                if (t < 4) fa0[t] = frag(stn, 0, t, 0);
-                else if (t < 8) fb0[t - 4] = frag(stn, 1, t - 4, 0);
-                else if (t < 12) nsa[t - 8] = scale_word(stn, 0, t - 8);
-                else nsb[t - 12] = scale_word(stn, 1, t - 12);
+            const uint32_t more = dstep < nk - 1 ? 1u : 0u;
+            static_for<16>([&](auto t_tag) {
+                constexpr int t = decltype(t_tag)::value;
+                constexpr int i = t >> 2, j = t & 3;
+                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb1[j], fa1[i], acc[i][j], 4, 4, 2,
+                                                                             (int)sb[j], 2, (int)sa[i]);
+                if constexpr (t < kDmaPerPhase)
+                    dma_piece(dma_addr, std::integral_constant<int, kDmaPerPhase + t>{});
+                // next step's operands, in the order phase A consumes them,
+                // two per slot so they land well before the phase ends
+                if constexpr (t < 8) {
+                    constexpr int q = t >> 1;
+                    if constexpr ((t & 1) == 0) {
+                        fb0[q] = frag(stn, 1, q, 0);
+                        nsb[q] = scale_word(stn, 1, q);
+                    } else {
+                        fa0[q] = frag(stn, 0, q, 0);
+                        nsa[q] = scale_word(stn, 0, q);
+                    }
+                }
+                // lanes 32..63 take the odd K blocks: shift their scale
+                // words down one byte, well after the reads were issued
+                // (the empty asm statements pin each update to its slot: the
+                // compiler would otherwise fold it into the loop's back edge)
+                if constexpr (t >= 8) {
+                    constexpr int q = (t - 8) >> 1;
+                    if constexpr ((t & 1) == 0) {
+                        nsb[q] >>= 8 * fh;
+                        asm volatile("" : "+v"(nsb[q]));
+                    } else {
+                        nsa[q] >>= 8 * fh;
+                        asm volatile("" : "+v"(nsa[q]));
+                    }
+                }
+                if constexpr (t >= kDmaPerPhase && t < kDmaPerPhase + 4) advance_ptr(t - kDmaPerPhase, more);
                 __builtin_amdgcn_sched_barrier(0);
-            }
+            });
+            dstep += (int)more;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 sa[i] = nsa[i];
                 sb[i] = nsb[i];
             }
+            const uint32_t o = off_cur;
+            off_cur = off_nxt;
+            off_nxt = off_dma;
+            off_dma = o;
         }
         // the ring is idle: every DMA landed, every wave finished its reads
         wait_and_barrier<0>();
