@@ -41,14 +41,17 @@ typedef int v8i_t __attribute__((ext_vector_type(8)));
 typedef float v16f_t __attribute__((ext_vector_type(16)));
 
 constexpr int kBM = 256, kBN = 256;
-constexpr int kStages = 3;                                  // LDS ring depth (K steps in flight)
+constexpr int kStages = 4;                                  // LDS ring depth (K steps in flight)
 constexpr int kCodeBytes = kBM * 64;                        // one operand's codes per 128-wide K step
 constexpr int kScaleOff = 2 * kCodeBytes;                   // A scales, then B scales (u32 per row)
 constexpr int kStageBytes = 2 * kCodeBytes + (kBM + kBN) * 4;  // 34 KiB
-constexpr int kRingBytes = kStages * kStageBytes;           // 102 KiB
+constexpr int kRingBytes = kStages * kStageBytes;           // 136 KiB
 constexpr int kEpiPitch = 64 * 4 + 16;                      // epilogue staging row: 64 fp32 + 16 bytes of padding
 constexpr int kEpiWaveBytes = 32 * kEpiPitch;               // one wave's epilogue chunk: 32 x 64 fp32
-constexpr int kLdsBytes = kRingBytes + 4 * kEpiWaveBytes;   // 136 KiB
+// The epilogue stages its chunks in the last ring slot, which the next
+// tile's prologue (K steps 0 .. kStages-2) leaves free.
+static_assert(4 * kEpiWaveBytes <= kStageBytes, "epilogue staging must fit in one ring slot");
+constexpr int kLdsBytes = kRingBytes;
 constexpr int kDmaPerStage = 10;                            // DMA instructions per wave per stage
 constexpr int kDmaPerPhase = kDmaPerStage / 2;
 
@@ -265,9 +268,11 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(const uint8_t *__restrict_
     setup(tile);
     prologue();
     for (;;) {
-        // stage 0 of this tile has landed (vmcnt(0) also covers the previous
-        // tile's output stores, which share the counter)
-        wait_and_barrier<0>();
+        // stage 0 of this tile has landed: loads complete in issue order, so
+        // once at most (kStages-2) stages' DMA instructions are outstanding
+        // (the previous tile's output stores share the counter and only
+        // make this wait longer) the oldest stage is in LDS
+        wait_and_barrier<(kStages - 2) * kDmaPerStage>();
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             fa0[i] = frag(lds, 0, i, 0);
@@ -285,16 +290,20 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(const uint8_t *__restrict_
         // matrix cores and every memory instruction is issued between two
         // MFMAs, so LDS reads, DMA issue and MFMAs overlap:
         //   phase A of step ks: MFMAs of half 0 (operands in registers),
-        //     interleaved with half of the DMA of step ks+2 (into the slot of
+        //     interleaved with half of the DMA of step ks+3 (into the slot of
         //     step ks-1, free since the previous barrier) and the LDS reads
         //     of half 1 of step ks;
         //   barrier: step ks+1 has landed in LDS for every wave;
         //   phase B: MFMAs of half 1, interleaved with the rest of the DMA of
-        //     step ks+2 and the LDS reads of half 0 and the scales of ks+1.
-        // Ring slots rotate through three scalar offsets (current step,
-        // next step, DMA target) so that every LDS address is a scalar plus a
+        //     step ks+3 and the LDS reads of half 0 and the scales of ks+1.
+        // The DMA runs three steps ahead: the K slices of all workgroups on
+        // an XCD are requested together, so every one of them waits for the
+        // full HBM latency of the first request of a slice.
+        // Ring slots rotate through four scalar offsets (current step, the
+        // two next steps, DMA target) so that every LDS address is a scalar plus a
         // constant.
-        uint32_t off_cur = 0, off_nxt = kStageBytes, off_dma = 2 * kStageBytes;
+        static_assert(kStages == 4, "the slot rotation below is written for four slots");
+        uint32_t off_cur = 0, off_nxt = kStageBytes, off_n2 = 2 * kStageBytes, off_dma = 3 * kStageBytes;
         for (int ks = 0; ks < nk; ++ks) {
             const uint8_t *st = lds + off_cur;
             const uint8_t *stn = lds + off_nxt;  // a re-read copy past the end
@@ -309,9 +318,10 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(const uint8_t *__restrict_
                 else if constexpr (t < 8) fb1[t - 4] = frag(st, 1, t - 4, 1);
                 __builtin_amdgcn_sched_barrier(0);
             });
-            // step ks+1's DMA was issued one step ago; only this step's first
-            // kDmaPerPhase instructions may still be in flight
-            wait_and_barrier<kDmaPerPhase>();
+            // step ks+1's DMA was issued two steps ago; after it only step
+            // ks+2's DMA and this step's first kDmaPerPhase instructions may
+            // still be in flight
+            wait_and_barrier<(kStages - 3) * kDmaPerStage + kDmaPerPhase>();
             const uint32_t more = dstep < nk - 1 ? 1u : 0u;
             static_for<16>([&](auto t_tag) {
                 constexpr int t = decltype(t_tag)::value;
@@ -357,7 +367,8 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(const uint8_t *__restrict_
             }
             const uint32_t o = off_cur;
             off_cur = off_nxt;
-            off_nxt = off_dma;
+            off_nxt = off_n2;
+            off_n2 = off_dma;
             off_dma = o;
         }
         // the ring is idle: every DMA landed, every wave finished its reads
@@ -380,7 +391,7 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(const uint8_t *__restrict_
         // nearest even) and 16-byte global stores.  Fewest instructions per
         // output: with one wave per SIMD every instruction costs a full issue
         // cycle that nothing else hides.
-        uint8_t *ep = lds + kRingBytes + wave * kEpiWaveBytes;
+        uint8_t *ep = lds + (kStages - 1) * kStageBytes + wave * kEpiWaveBytes;
         const int row_base = tm0 + wm * 128, col_base = tn0 + wn * 128;
         // Lane-derived offsets are recomputed per tile from an opaque copy of
         // the lane index: hoisted out of the tile loop they would stay live
@@ -390,106 +401,129 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(const uint8_t *__restrict_
         asm volatile("v_mov_b32 %0, %1" : "=v"(el) : "v"(lane));
         const int efr = el & 31, efh = el >> 5;
         const bool full = vec_ok && row_base + 128 <= M && col_base + 128 <= N;
-        // alpha == 1 (the common case) skips the multiplies; either way the
-        // chunk loop is branch-free apart from the full-tile test
-        auto epilogue = [&](auto scale_tag) {
+        // specialised on the output type and on alpha == 1 (the common case
+        // skips the multiplies): the chunk loop is branch-free apart from the
+        // full-tile test
+        auto epilogue = [&](auto scale_tag, auto bf16_tag) {
             constexpr bool kScale = decltype(scale_tag)::value;
-            const int esize = c_bf16 ? 2 : 4;
-            // LDS -> registers: one 16-byte output piece (bf16: 8 columns from
-            // two fp32 reads; fp32: 4 columns) of the staged 32 x 64 chunk
-            auto piece_bf16 = [&](int rl, int cp) -> uint4 {
-                float4 lo = *reinterpret_cast<const float4 *>(ep + rl * kEpiPitch + cp * 32);
-                float4 hi = *reinterpret_cast<const float4 *>(ep + rl * kEpiPitch + cp * 32 + 16);
-                if (kScale) {
-                    lo.x *= alpha; lo.y *= alpha; lo.z *= alpha; lo.w *= alpha;
-                    hi.x *= alpha; hi.y *= alpha; hi.z *= alpha; hi.w *= alpha;
+            constexpr bool kBf16 = decltype(bf16_tag)::value;
+            constexpr int esize = kBf16 ? 2 : 4;
+            // A lane's pieces of a staged 32 x 64 chunk: bf16 pieces are
+            // (row el/8 + 8u, 8 columns at 8 (el mod 8)), two fp32 reads each;
+            // fp32 pieces (row el/16 + 4u, 4 columns at 4 (el mod 16)).
+            const int rl0 = kBf16 ? (el >> 3) : (el >> 4);
+            constexpr int rstep = kBf16 ? 8 : 4;
+            const int cpi = kBf16 ? (el & 7) : (el & 15);
+            const uint32_t lds_lane = rl0 * kEpiPitch + cpi * (kBf16 ? 32 : 16);
+            // lane's byte offset inside a chunk of C (the launcher keeps 32
+            // rows of C under 2 GiB)
+            const uint32_t lane_off = ((uint32_t)rl0 * (uint32_t)ldc + cpi * (kBf16 ? 8 : 4)) * esize;
+            // chunk c = (i, jp): rows 32 i, columns 64 jp of the wave's block
+            auto stage = [&](int c) {
+                const int i = c >> 1, jp = c & 1;
+#pragma unroll
+                for (int jj = 0; jj < 2; ++jj) {
+                    const v16f_t &a = acc[i][2 * jp + jj];
+#pragma unroll
+                    for (int g = 0; g < 4; ++g)
+                        *reinterpret_cast<float4 *>(ep + efr * kEpiPitch + (jj * 32 + 8 * g + 4 * efh) * 4) =
+                            make_float4(a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]);
                 }
-                uint4 o;
-                o.x = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo.x, lo.y}, bf16x2_t));
-                o.y = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo.z, lo.w}, bf16x2_t));
-                o.z = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){hi.x, hi.y}, bf16x2_t));
-                o.w = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){hi.z, hi.w}, bf16x2_t));
-                return o;
             };
-            auto piece_f32 = [&](int rl, int cp) -> uint4 {
-                float4 v = *reinterpret_cast<const float4 *>(ep + rl * kEpiPitch + cp * 16);
-                if (kScale) {
-                    v.x *= alpha; v.y *= alpha; v.z *= alpha; v.w *= alpha;
+            // the eight 16-byte LDS reads of a lane's pieces of the staged chunk
+            auto fetch = [&](float4 (&r)[8]) {
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const uint32_t o = kBf16 ? lds_lane + (u >> 1) * rstep * kEpiPitch + (u & 1) * 16
+                                              : lds_lane + u * rstep * kEpiPitch;
+                    r[u] = *reinterpret_cast<const float4 *>(ep + o);
                 }
-                return __builtin_bit_cast(uint4, v);
             };
-            // lane's byte offset inside a chunk: bf16 pieces are (row el/8 + 8u,
-            // 8 columns at 8 (el mod 8)), fp32 pieces (row el/16 + 4u, 4 columns
-            // at 4 (el mod 16)); the launcher keeps 32 rows of C under 2 GiB
-            const uint32_t lane_off = c_bf16 ? ((uint32_t)(el >> 3) * (uint32_t)ldc + (el & 7) * 8) * 2
-                                             : ((uint32_t)(el >> 4) * (uint32_t)ldc + (el & 15) * 4) * 4;
+            auto store = [&](int c, float4 (&r)[8]) {
+                const int i = c >> 1, jp = c & 1;
+                if (kScale) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-#pragma unroll
-                for (int jp = 0; jp < 2; ++jp) {
-#pragma unroll
-                    for (int jj = 0; jj < 2; ++jj) {
-                        const v16f_t &a = acc[i][2 * jp + jj];
-#pragma unroll
-                        for (int g = 0; g < 4; ++g)
-                            *reinterpret_cast<float4 *>(ep + efr * kEpiPitch + (jj * 32 + 8 * g + 4 * efh) * 4) =
-                                make_float4(a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]);
+                    for (int u = 0; u < 8; ++u) {
+                        r[u].x *= alpha; r[u].y *= alpha; r[u].z *= alpha; r[u].w *= alpha;
                     }
-                    const int row0 = row_base + i * 32, col0 = col_base + jp * 64;
-                    if (full) {
-                        // whole chunk inside C and 16-byte aligned: no guards
-                        uint8_t *base = reinterpret_cast<uint8_t *>(C) + ((int64_t)row0 * ldc + col0) * esize;
-                        if (c_bf16) {
+                }
+                const int row0 = row_base + i * 32, col0 = col_base + jp * 64;
+                constexpr int npieces = kBf16 ? 4 : 8;
+                uint4 o[8];
 #pragma unroll
-                            for (int u = 0; u < 4; ++u)
-                                *reinterpret_cast<uint4 *>(base + (int64_t)u * 8 * ldc * 2 + lane_off) =
-                                    piece_bf16((el >> 3) + 8 * u, el & 7);
-                        } else {
-#pragma unroll
-                            for (int u = 0; u < 8; ++u)
-                                *reinterpret_cast<uint4 *>(base + (int64_t)u * 4 * ldc * 4 + lane_off) =
-                                    piece_f32((el >> 4) + 4 * u, el & 15);
-                        }
-                    } else if (c_bf16) {
-#pragma unroll
-                        for (int u = 0; u < 4; ++u) {
-                            const int rl = (el >> 3) + 8 * u, cp = el & 7;
-                            const uint4 o = piece_bf16(rl, cp);
-                            const int row = row0 + rl, col = col0 + cp * 8;
-                            if (row >= M) continue;
-                            uint16_t *dstp = reinterpret_cast<uint16_t *>(C) + (int64_t)row * ldc + col;
-                            if (vec_ok && col + 8 <= N) {
-                                *reinterpret_cast<uint4 *>(dstp) = o;
-                            } else {
-                                const uint16_t *ov = reinterpret_cast<const uint16_t *>(&o);
-                                for (int e = 0; e < 8; ++e)
-                                    if (col + e < N) dstp[e] = ov[e];
-                            }
+                for (int u = 0; u < 8; ++u) {
+                    if constexpr (kBf16) {
+                        if (u < 4) {
+                            const float4 lo = r[2 * u], hi = r[2 * u + 1];
+                            o[u].x = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo.x, lo.y}, bf16x2_t));
+                            o[u].y = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo.z, lo.w}, bf16x2_t));
+                            o[u].z = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){hi.x, hi.y}, bf16x2_t));
+                            o[u].w = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){hi.z, hi.w}, bf16x2_t));
                         }
                     } else {
+                        o[u] = __builtin_bit_cast(uint4, r[u]);
+                    }
+                }
+                if (full) {
+                    // whole chunk inside C and 16-byte aligned: no guards
+                    uint8_t *base = reinterpret_cast<uint8_t *>(C) + ((int64_t)row0 * ldc + col0) * esize;
 #pragma unroll
-                        for (int u = 0; u < 8; ++u) {
-                            const int rl = (el >> 4) + 4 * u, cp = el & 15;
-                            const uint4 o = piece_f32(rl, cp);
-                            const int row = row0 + rl, col = col0 + cp * 4;
-                            if (row >= M) continue;
-                            float *dstp = reinterpret_cast<float *>(C) + (int64_t)row * ldc + col;
-                            if (vec_ok && col + 4 <= N) {
-                                *reinterpret_cast<uint4 *>(dstp) = o;
-                            } else {
-                                const float *vv = reinterpret_cast<const float *>(&o);
-                                for (int e = 0; e < 4; ++e)
-                                    if (col + e < N) dstp[e] = vv[e];
-                            }
+                    for (int u = 0; u < 8; ++u)
+                        if (u < npieces)
+                            *reinterpret_cast<uint4 *>(base + (int64_t)u * rstep * ldc * esize + lane_off) = o[u];
+                } else {
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) {
+                        if (u >= npieces) continue;
+                        const int row = row0 + rl0 + u * rstep, col = col0 + cpi * (kBf16 ? 8 : 4);
+                        if (row >= M) continue;
+                        constexpr int ne = kBf16 ? 8 : 4;
+                        uint8_t *dstp = reinterpret_cast<uint8_t *>(C) + ((int64_t)row * ldc + col) * esize;
+                        if (vec_ok && col + ne <= N) {
+                            *reinterpret_cast<uint4 *>(dstp) = o[u];
+                        } else if constexpr (kBf16) {
+                            const uint16_t *ov = reinterpret_cast<const uint16_t *>(&o[u]);
+                            for (int e = 0; e < 8; ++e)
+                                if (col + e < N) reinterpret_cast<uint16_t *>(dstp)[e] = ov[e];
+                        } else {
+                            const float *ov = reinterpret_cast<const float *>(&o[u]);
+                            for (int e = 0; e < 4; ++e)
+                                if (col + e < N) reinterpret_cast<float *>(dstp)[e] = ov[e];
                         }
                     }
                 }
+            };
+            // Two-deep pipeline over the eight chunks: the LDS writes and
+            // reads of chunk c+1 are issued before chunk c is converted and
+            // stored, so one chunk's LDS latency hides behind the other's
+            // stores.  A wave's LDS operations run in issue order, so chunk
+            // c's reads complete before chunk c+1's writes reuse the area.
+            float4 r0[8], r1[8];
+            stage(0);
+            fetch(r0);
+#pragma unroll
+            for (int c = 0; c < 8; c += 2) {
+                stage(c + 1);
+                fetch(r1);
+                store(c, r0);
+                if (c + 2 < 8) {
+                    stage(c + 2);
+                    fetch(r0);
+                }
+                store(c + 1, r1);
             }
         };
-        if (alpha != 1.0f)
-            epilogue(std::true_type{});
-        else
-            epilogue(std::false_type{});
+        if (c_bf16) {
+            if (alpha != 1.0f)
+                epilogue(std::true_type{}, std::true_type{});
+            else
+                epilogue(std::false_type{}, std::true_type{});
+        } else {
+            if (alpha != 1.0f)
+                epilogue(std::true_type{}, std::false_type{});
+            else
+                epilogue(std::false_type{}, std::false_type{});
+        }
         if (next >= ntiles) break;
         tile = next;
     }
