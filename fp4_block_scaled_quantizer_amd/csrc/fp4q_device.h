@@ -34,23 +34,25 @@ FP4Q_HD uint32_t f32_to_bf16_rne(float f)
 
 // E2M1 stochastic rounding ([Fusion] section "Two Key Numerical Techniques":
 // up or down with probability proportional to the distance).  The grid step
-// is g = 0.5 below 2, 1 in [2, 4), 2 in [4, 6); t = |y| / g is exact, its
-// fractional part f is the distance to the lower neighbour in steps, and the
-// value rounds up iff r16 < f * 2^16 (all exact in binary32).  |y| >= 6
-// saturates.  r16 is uniform on [0, 65535].
+// is g = 0.5 below 2, 1 in [2, 4), 2 in [4, 6); with t = |y| / g, f its
+// fractional part (the distance to the lower neighbour in steps), the value
+// rounds up iff f * 2^16 > r16.  |y| >= 6 saturates.  r16 is uniform on
+// [0, 65535].  Evaluated branch-free and exactly:
+//  - |y| in [1, 6): the binary32 bits of |y| minus those of 0.5 give t on the
+//    code axis in fixed point (code = bits 22 and up, f = the low 22 bits);
+//    adding 2^22 - 1 - 64 r16 carries into the code iff 2^22 f > 64 r16;
+//  - |y| < 1: P = 2^17 |y| (exact) is t in units of 2^-16 steps, and the code
+//    is the number of the thresholds r16 and r16 + 2^16 that P exceeds.
 FP4Q_HD uint32_t e2m1_sr(float y, uint32_t r16)
 {
     const uint32_t b = f2u(y);
-    const float m = u2f(b & 0x7FFFFFFFu);
+    const uint32_t u = b & 0x7FFFFFFFu;
     const uint32_t s = (b >> 28) & 8u;
-    if (m >= 6.0f) return s | 7u;
-    const float ginv = m < 2.0f ? 2.0f : (m < 4.0f ? 1.0f : 0.5f);
-    const float t = m * ginv;
-    const float fl = floorf(t);
-    const float frac = t - fl;
-    const uint32_t up = (float)r16 < frac * 65536.0f ? 1u : 0u;
-    const uint32_t k0 = m < 2.0f ? (uint32_t)fl : (m < 4.0f ? (uint32_t)fl + 2u : 6u);
-    return s | (k0 + up);
+    const uint32_t hi = (u - 0x3F000000u + 0x3FFFFFu - (r16 << 6)) >> 22;
+    const float P = u2f(u) * 131072.0f;
+    const float rf = (float)r16;
+    const uint32_t lo = (P > rf ? 1u : 0u) + (P > rf + 65536.0f ? 1u : 0u);
+    return s | (u >= 0x40C00000u ? 7u : (u >= 0x3F800000u ? hi : lo));
 }
 
 // OCP MX shared exponent byte (E8M0) of a block whose amax has binary32 bits
@@ -105,6 +107,16 @@ FP4Q_HD float nv_inv_decode(uint32_t sb, float S) { return 1.0f / (e4m3_value(sb
 // domain's largest block then maps onto E4M3 448 x E2M1 6 = 2688.
 FP4Q_HD float nv_tensor_scale(float A) { return A == 0.0f ? 1.0f : A / 2688.0f; }
 
+// a ^ b ^ c: one v_bitop3_b32 (truth table 0x96) on gfx950.
+FP4Q_HD uint32_t xor3(uint32_t a, uint32_t b, uint32_t c)
+{
+#if defined(__HIP_DEVICE_COMPILE__)
+    return __builtin_amdgcn_bitop3_b32(a, b, c, 0x96);
+#else
+    return a ^ b ^ c;
+#endif
+}
+
 // Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): ten rounds of two 32x32
 // -> 64-bit multiplies with the published multipliers and Weyl key increments.
 FP4Q_HD void philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3, uint32_t k0, uint32_t k1,
@@ -118,8 +130,8 @@ FP4Q_HD void philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3, u
         }
         const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
         const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
-        const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
-        const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+        const uint32_t n0 = xor3((uint32_t)(p1 >> 32), c1, k0);
+        const uint32_t n2 = xor3((uint32_t)(p0 >> 32), c3, k1);
         c1 = (uint32_t)p1;
         c3 = (uint32_t)p0;
         c0 = n0;

@@ -216,97 +216,130 @@ __global__ __launch_bounds__(kThreads) void quant_mx_rows_kernel(const uint16_t 
 
 // ------------------------------------------------------------------
 // MXFP4 along columns: the logical operand is x^T, blocks run down 32 rows of
-// one column of x.  A lane owns 4 adjacent columns (8-byte loads, so a
-// wavefront reads 512 contiguous bytes of each row) and walks kColBlocks
-// consecutive 32-row blocks.  Each (output row, block) gives 16 bytes of
-// codes, which in the tiled layout is exactly one lane slot of a 1 KiB block:
-// a wavefront's 256 columns fill 512 contiguous bytes of each of 8 blocks,
-// and the 4 scale bytes of the 4 blocks form one 32-bit word per output row.
+// one column of x.  A workgroup owns 128 rows (4 blocks along K) x 128
+// columns.  It reads the tile with row-contiguous 16-byte loads (256 bytes
+// of each row), stages it in LDS, and then each thread quantizes two
+// adjacent columns of one 32-row block, reading them as 32-bit words down
+// the block (a wavefront reads 256 contiguous bytes of one staged row per
+// instruction, so neither phase has bank conflicts).  Each (output row,
+// block) gives 16 bytes of codes: in the tiled layout the thread's two
+// columns are adjacent lane slots of one 1 KiB block, and the 4 scale bytes
+// of an output row form one 32-bit word, assembled in LDS and written 128
+// words at a time.
 // ------------------------------------------------------------------
-constexpr int kColBlocks = 4;
+constexpr int kColTile = 128;            // rows and columns of a workgroup tile
+constexpr int kColPitch = kColTile * 2;  // bytes per staged row
 
 template <bool kSR, bool kHad, bool kTiled>
-__global__ __launch_bounds__(64) void quant_mx_cols_kernel(const uint16_t *__restrict__ x, uint32_t rows,
-                                                           uint32_t cols, uint32_t ld, uint32_t Rp,
-                                                           uint8_t *__restrict__ codes, uint8_t *__restrict__ scales,
-                                                           uint32_t seed_lo, uint32_t seed_hi, uint32_t stream_id,
-                                                           uint32_t sign_mask)
+__global__ __launch_bounds__(kThreads) void quant_mx_cols_kernel(const uint16_t *__restrict__ x, uint32_t rows,
+                                                                 uint32_t cols, uint32_t ld, uint32_t Rp,
+                                                                 uint8_t *__restrict__ codes,
+                                                                 uint8_t *__restrict__ scales, uint32_t seed_lo,
+                                                                 uint32_t seed_hi, uint32_t stream_id,
+                                                                 uint32_t sign_mask)
 {
-    const uint32_t col0 = (blockIdx.x * 64 + threadIdx.x) * 4;  // first of this lane's 4 columns
-    const uint32_t Kb = rows >> 5;                               // blocks per output row
-    const uint32_t j0 = blockIdx.y * kColBlocks;
-    // columns past `cols` exist only as the zero padding rows of the tiled layout
-    if (col0 >= (kTiled ? Rp : cols)) return;  // whole lane idle; no cross-lane work below
-    const bool live = col0 < cols;              // cols % 4 == 0: all 4 columns live or none
-    const uint32_t K2 = rows >> 1;  // bytes of codes per output row
-    uint32_t sword[4] = {0u, 0u, 0u, 0u};
-    for (int jb = 0; jb < kColBlocks; ++jb) {
-        const uint32_t j = j0 + jb;
-        if (j >= Kb) break;
-        uint2 raw[32];
+    __shared__ __attribute__((aligned(16))) uint8_t tile[kColTile * kColPitch];
+    __shared__ __attribute__((aligned(16))) uint8_t sc[kColTile * 4];
+    const uint32_t c0 = blockIdx.x * kColTile, r0 = blockIdx.y * kColTile;
+    const uint32_t span = kTiled ? Rp : cols;  // output rows; the tiled layout pads with zero rows
+    const uint32_t nblk = min(4u, (rows - r0) >> 5);
+    const int t = threadIdx.x;
+    {
+        // 8 passes of 16 rows; thread = (row t / 16, 16-byte chunk t mod 16)
+        const uint32_t ch = t & 15, rr = t >> 4, c = c0 + ch * 8;
+        uint4 q[8];
 #pragma unroll
-        for (int i = 0; i < 32; ++i)
-            raw[i] = live ? load_nt8(x + (size_t)(32 * j + i) * ld + col0) : make_uint2(0u, 0u);
-#pragma unroll
-        for (int cq = 0; cq < 4; ++cq) {
-            const uint32_t col = col0 + cq;
-            float v[32];
-#pragma unroll
-            for (int i = 0; i < 32; ++i) {
-                const uint32_t word = (cq < 2) ? raw[i].x : raw[i].y;
-                v[i] = (cq & 1) ? bf16_hi(word) : bf16_lo(word);
+        for (int p = 0; p < 8; ++p) {
+            const uint32_t r = r0 + p * 16 + rr;
+            q[p] = make_uint4(0u, 0u, 0u, 0u);
+            if (r < rows) {
+                const uint16_t *src = x + (size_t)r * ld + c;
+                if (c + 8 <= cols) {
+                    q[p] = load_nt16(src);
+                } else if (c + 4 <= cols) {  // cols % 4 == 0: a chunk is full, half or empty
+                    const uint2 h = load_nt8(src);
+                    q[p] = make_uint4(h.x, h.y, 0u, 0u);
+                }
             }
+        }
+#pragma unroll
+        for (int p = 0; p < 8; ++p) *reinterpret_cast<uint4 *>(tile + (p * 16 + rr) * kColPitch + ch * 16) = q[p];
+    }
+    __syncthreads();
+    const uint32_t cp = t & 63, jb = t >> 6;
+    const uint32_t col = c0 + 2 * cp;  // first column of the pair; cols % 4 == 0, so both or neither exist
+    if (jb < nblk && col < span) {
+        const uint32_t j = (r0 >> 5) + jb;  // block index along K
+        float v[2][32];
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+            const uint32_t w = *reinterpret_cast<const uint32_t *>(tile + (jb * 32 + i) * kColPitch + cp * 4);
+            v[0][i] = bf16_lo(w);
+            v[1][i] = bf16_hi(w);
+        }
+        uint4 o[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
             if (kHad) {
 #pragma unroll
                 for (int i = 0; i < 32; ++i)
-                    if ((sign_mask >> i) & 1u) v[i] = -v[i];
+                    if ((sign_mask >> i) & 1u) v[h][i] = -v[h][i];
 #pragma unroll
-                for (int h = 1; h < 32; h <<= 1) {
+                for (int st = 1; st < 32; st <<= 1) {
 #pragma unroll
                     for (int i = 0; i < 32; ++i) {
-                        if (i & h) continue;
-                        const float a = v[i], b = v[i + h];
-                        v[i] = a + b;
-                        v[i + h] = a - b;
+                        if (i & st) continue;
+                        const float a = v[h][i], b = v[h][i + st];
+                        v[h][i] = a + b;
+                        v[h][i + st] = a - b;
                     }
                 }
             }
             uint32_t amax = 0;
 #pragma unroll
-            for (int i = 0; i < 32; ++i) amax = max(amax, f2u(v[i]) & 0x7FFFFFFFu);
+            for (int i = 0; i < 32; ++i) amax = max(amax, f2u(v[h][i]) & 0x7FFFFFFFu);
             const uint32_t sbyte = mx_scale_byte(amax);
-            const float inv = mx_inv_scale(sbyte);
-            const float scale = mx_scale_f32(sbyte);
             uint32_t out[4];
+            if (kSR) {
+                const float inv = mx_inv_scale(sbyte);
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                uint32_t packed = 0;
-                if (kSR) {
+                for (int g = 0; g < 4; ++g) {
                     uint32_t w[4];
-                    philox4x32_10(4 * j + g, col, stream_id, 0u, seed_lo, seed_hi, w);
+                    philox4x32_10(4 * j + g, col + h, stream_id, 0u, seed_lo, seed_hi, w);
+                    uint32_t packed = 0;
 #pragma unroll
-                    for (int t = 0; t < 8; ++t) packed |= e2m1_sr(v[8 * g + t] * inv, r16_of(w, t)) << (4 * t);
-                } else {
-                    packed = cvt8_f32(v + 8 * g, scale);
+                    for (int e = 0; e < 8; ++e) packed |= e2m1_sr(v[h][8 * g + e] * inv, r16_of(w, e)) << (4 * e);
+                    out[g] = packed;
                 }
-                out[g] = packed;
-            }
-            const uint4 o = make_uint4(out[0], out[1], out[2], out[3]);
-            if (kTiled) {
-                const size_t blk = (size_t)(col >> 5) * (rows >> 6) + (j >> 1);
-                *reinterpret_cast<uint4 *>(codes + blk * 1024 + ((col & 31) + 32 * (j & 1)) * 16) = o;
-                sword[cq] |= sbyte << (8 * jb);
             } else {
-                *reinterpret_cast<uint4 *>(codes + (size_t)col * K2 + (size_t)j * 16) = o;
-                scales[(size_t)col * Kb + j] = (uint8_t)sbyte;
+                const float scale = mx_scale_f32(sbyte);
+#pragma unroll
+                for (int g = 0; g < 4; ++g) out[g] = cvt8_f32(&v[h][8 * g], scale);
             }
+            o[h] = make_uint4(out[0], out[1], out[2], out[3]);
+            if (kTiled) {
+                sc[(2 * cp + h) * 4 + jb] = (uint8_t)sbyte;
+            } else {
+                scales[(size_t)(col + h) * (rows >> 5) + j] = (uint8_t)sbyte;
+            }
+        }
+        if (kTiled) {
+            // lane slots (col mod 32) + 32 (j mod 2) of block (col / 32, j / 2): the pair is 32 contiguous bytes
+            uint8_t *dst = codes + ((size_t)(col >> 5) * (rows >> 6) + (j >> 1)) * 1024 + ((col & 31) + 32 * (j & 1)) * 16;
+            *reinterpret_cast<uint4 *>(dst) = o[0];
+            *reinterpret_cast<uint4 *>(dst + 16) = o[1];
+        } else {
+            const uint32_t K2 = rows >> 1;
+            *reinterpret_cast<uint4 *>(codes + (size_t)col * K2 + (size_t)j * 16) = o[0];
+            *reinterpret_cast<uint4 *>(codes + (size_t)(col + 1) * K2 + (size_t)j * 16) = o[1];
         }
     }
     if (kTiled) {
-        // K % 128 == 0 in the tiled layout, so j0 / 4 is a whole 128-wide step
-#pragma unroll
-        for (int cq = 0; cq < 4; ++cq)
-            *reinterpret_cast<uint32_t *>(scales + ((size_t)(j0 >> 2) * Rp + col0 + cq) * 4) = sword[cq];
+        // rows % 128 == 0 in the tiled layout: the tile is exactly one 128-wide K step
+        __syncthreads();
+        if ((uint32_t)t < kColTile && c0 + t < span)
+            *reinterpret_cast<uint32_t *>(scales + ((size_t)(r0 >> 7) * Rp + c0 + t) * 4) =
+                *reinterpret_cast<const uint32_t *>(sc + t * 4);
     }
 }
 
@@ -586,13 +619,12 @@ int launch_quant_mx(const QuantArgs &a, hipStream_t st)
     } else {
         const uint32_t rows = (uint32_t)a.rows, cols = (uint32_t)a.cols;
         if (rows == 0 || cols == 0) return 0;
-        const uint32_t Kb = rows >> 5;
         const uint32_t Rp = (cols + 31) / 32 * 32;
         const uint32_t span = a.tiled ? Rp : cols;
-        dim3 grid((span + 255) / 256, (Kb + kColBlocks - 1) / kColBlocks);
+        dim3 grid((span + kColTile - 1) / kColTile, (rows + kColTile - 1) / kColTile);
         auto *codes = reinterpret_cast<uint8_t *>(a.codes);
 #define FP4Q_LAUNCH_COLS(SR, HAD, T)                                                                          \
-    hipLaunchKernelGGL((quant_mx_cols_kernel<SR, HAD, T>), grid, dim3(64), 0, st, x, rows, cols, (uint32_t)a.ld, \
+    hipLaunchKernelGGL((quant_mx_cols_kernel<SR, HAD, T>), grid, dim3(kThreads), 0, st, x, rows, cols, (uint32_t)a.ld, \
                        Rp, codes, scales, seed_lo, seed_hi, a.stream_id, a.sign_mask)
 #define FP4Q_LAUNCH_COLS2(SR, HAD) \
     do { if (a.tiled) FP4Q_LAUNCH_COLS(SR, HAD, true); else FP4Q_LAUNCH_COLS(SR, HAD, false); } while (0)
