@@ -74,6 +74,8 @@ def build_workload(name, dev, copies, layout_name="tiled"):
         cs, ss = B.mx_output_shapes(R, K, L)
         return (torch.empty(cs, dtype=torch.uint8, device=dev), torch.empty(ss, dtype=torch.uint8, device=dev))
 
+    # the kernel each MX row producer launches in this layout
+    qk = "quant_mx_rows_tiled_kernel" if L == B.LAYOUT_TILED else "quant_mx_rows_kernel"
     ops = []
     if name == "copy":
         # a plain copy kernel of known size: 1 GiB read + 1 GiB written per launch
@@ -91,7 +93,6 @@ def build_workload(name, dev, copies, layout_name="tiled"):
         cx, sx = mx_bufs(M, K)
         cw, sw = mx_bufs(N, K)
         C = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-        qk = "quant_mx_rows_tiled_kernel" if L == B.LAYOUT_TILED else "quant_mx_rows_kernel"
         ops = [
             ("quantize X (MXFP4, RNE)", qk,
              lambda s: B.fp4_quantize_mx(X[s % copies], codes=cx, scales=sx, layout=L),
@@ -124,16 +125,16 @@ def build_workload(name, dev, copies, layout_name="tiled"):
         C1 = torch.empty((M, N1), dtype=torch.bfloat16, device=dev)
         C2 = torch.empty((M, N2), dtype=torch.bfloat16, device=dev)
         ops = [
-            ("quantize X", "quant_mx_rows_kernel", q("x", X, M, K1), M * K1 * MX_BYTES_PER_ELEM, "GB/s",
+            ("quantize X", qk, q("x", X, M, K1), M * K1 * MX_BYTES_PER_ELEM, "GB/s",
              HBM_PEAK_GBS, "hbm"),
-            ("quantize W_gate_up", "quant_mx_rows_kernel", q("wg", Wg, N1, K1), N1 * K1 * MX_BYTES_PER_ELEM, "GB/s",
+            ("quantize W_gate_up", qk, q("wg", Wg, N1, K1), N1 * K1 * MX_BYTES_PER_ELEM, "GB/s",
              HBM_PEAK_GBS, "hbm"),
             ("GEMM gate/up", "gemm_mx_kernel",
              lambda s: B.fp4_gemm_mx(*bufs["x"], *bufs["wg"], c=C1, layout=L, m=M, n=N1),
              2.0 * M * N1 * K1, "TFLOP/s", FP4_PEAK_TFLOPS, "mfma"),
-            ("quantize H", "quant_mx_rows_kernel", q("h", H, M, K2), M * K2 * MX_BYTES_PER_ELEM, "GB/s",
+            ("quantize H", qk, q("h", H, M, K2), M * K2 * MX_BYTES_PER_ELEM, "GB/s",
              HBM_PEAK_GBS, "hbm"),
-            ("quantize W_down", "quant_mx_rows_kernel", q("wd", Wd, N2, K2), N2 * K2 * MX_BYTES_PER_ELEM, "GB/s",
+            ("quantize W_down", qk, q("wd", Wd, N2, K2), N2 * K2 * MX_BYTES_PER_ELEM, "GB/s",
              HBM_PEAK_GBS, "hbm"),
             ("GEMM down", "gemm_mx_kernel", lambda s: B.fp4_gemm_mx(*bufs["h"], *bufs["wd"], c=C2, layout=L, m=M, n=N2),
              2.0 * M * N2 * K2, "TFLOP/s", FP4_PEAK_TFLOPS, "mfma"),
@@ -161,7 +162,7 @@ def build_workload(name, dev, copies, layout_name="tiled"):
         dW = torch.empty((O, I), dtype=torch.float32, device=dev)
         seed = synth.SR_SEED
         ops = [
-            ("quantize dY rows (SR)", "quant_mx_rows_kernel",
+            ("quantize dY rows (SR)", qk,
              lambda s: B.fp4_quantize_mx(dY[s % copies], round=B.SR, seed=seed, stream_id=0, codes=bufs["dy_r"][0],
                                          scales=bufs["dy_r"][1], layout=L), T * O * MX_BYTES_PER_ELEM, "GB/s",
              HBM_PEAK_GBS,
