@@ -1,0 +1,240 @@
+// gemm_common.h -- pieces shared by the block-scaled GEMM kernels of libfp4q
+// (gemm_mx.hip, gemm_nv.hip): workgroup -> tile order, LDS DMA issue and
+// waits, a compile-time loop, and the epilogue of a wave's 128 x 128 block.
+// Not installed; not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+namespace fp4q {
+namespace gemm {
+
+typedef float v16f_t __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Epilogue staging of one wave: 32 rows x 64 fp32, rows padded by 16 bytes.
+constexpr int kEpiPitch = 64 * 4 + 16;
+constexpr int kEpiWaveBytes = 32 * kEpiPitch;
+
+// Tile order: XCD-contiguous ranges (workgroup b runs on XCD b mod 8), then
+// groups of 8 tile rows swept column by column inside each range.
+__device__ __forceinline__ void tile_coords(int bid, int tiles_m, int tiles_n, int &tm, int &tn)
+{
+    const int nt = tiles_m * tiles_n;
+    int t = bid;
+    if ((nt & 7) == 0) t = (bid & 7) * (nt >> 3) + (bid >> 3);
+    constexpr int G = 8;
+    const int width = G * tiles_n;
+    const int g = t / width;
+    const int first = g * G;
+    const int gsz = min(tiles_m - first, G);
+    const int w = t - g * width;
+    tm = first + w % gsz;
+    tn = w / gsz;
+}
+
+// Global -> LDS copies that bypass VGPRs (gfx950 LDS DMA): lane i reads
+// base + voff_i (base a 64-bit scalar address, voff a 32-bit per-lane byte
+// offset) and writes its 16 (or 4) bytes to LDS address m0 + 16 i (4 i),
+// m0 = lds_slot + kLdsOff (the add clobbers SCC, declared as such).
+// They are issued from inline assembly so that the only waits on them are
+// the explicit vmcnt waits of the K loop: every vector-memory instruction of
+// the loop is one of these, so the count of DMA instructions issued after a
+// stage is exactly the vmcnt value that guarantees that stage has landed.
+// base and lds_slot must be the same in every lane (scalar operands).
+template <uint32_t kLdsOff>
+__device__ __forceinline__ void dma16(const void *base, uint32_t voff, uint32_t lds_slot)
+{
+    asm volatile("s_add_u32 m0, %2, %3\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "s"(lds_slot),
+                 "n"(kLdsOff)
+                 : "memory", "m0", "scc");
+}
+template <uint32_t kLdsOff>
+__device__ __forceinline__ void dma4(const void *base, uint32_t voff, uint32_t lds_slot)
+{
+    asm volatile("s_add_u32 m0, %2, %3\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(base), "s"(lds_slot),
+                 "n"(kLdsOff)
+                 : "memory", "m0", "scc");
+}
+
+// All of this wave's LDS reads have returned and at most kAhead DMA
+// instructions are still in flight; then the workgroup meets.
+template <int kAhead>
+__device__ __forceinline__ void wait_and_barrier()
+{
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kAhead) : "memory");
+}
+
+// f(integral_constant<int, 0>) ... f(integral_constant<int, N-1>)
+template <int N, int I = 0, typename F>
+__device__ __forceinline__ void static_for(F &&f)
+{
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for<N, I + 1>(f);
+    }
+}
+
+// Epilogue of a wave's 128 x 128 block of C, held as a 4 x 4 grid of 32 x 32
+// accumulator blocks in which the B fragment was the matrix cores' first
+// operand: register r of lane l holds C[row (l mod 32)][col 8 (r/4) +
+// 4 (l/32) + r mod 4] of its block, so each aligned group of four
+// accumulator registers is four consecutive columns of one row.  The block
+// is written in eight chunks of 32 rows x 64 columns: 16-byte LDS writes
+// straight from the accumulator registers into the wave's staging area `ep`
+// (kEpiWaveBytes), then 16-byte LDS reads of row pieces, alpha (skipped when
+// kScale is false), conversion (bf16: v_cvt_pk_bf16_f32, round to nearest
+// even) and 16-byte global stores.  Fewest instructions per output: with one
+// wave per SIMD every instruction costs an issue cycle that nothing hides.
+// Rows >= M and columns >= N are not written; `full` says the whole block is
+// inside C with 16-byte aligned rows (then no guards are evaluated); the
+// lane index `el` is passed in from an opaque copy so that the lane-derived
+// offsets are recomputed here rather than kept live across the K loop.
+template <bool kScale, bool kBf16>
+__device__ __forceinline__ void store_wave_block(const v16f_t (&acc)[4][4], uint8_t *ep, int el, int row_base,
+                                                 int col_base, int M, int N, float alpha, void *C, int64_t ldc,
+                                                 bool vec_ok, bool full)
+{
+    constexpr int esize = kBf16 ? 2 : 4;
+    const int efr = el & 31, efh = el >> 5;
+    // A lane's pieces of a staged chunk: bf16 pieces are (row el/8 + 8u,
+    // 8 columns at 8 (el mod 8)), two fp32 reads each; fp32 pieces
+    // (row el/16 + 4u, 4 columns at 4 (el mod 16)).
+    const int rl0 = kBf16 ? (el >> 3) : (el >> 4);
+    constexpr int rstep = kBf16 ? 8 : 4;
+    const int cpi = kBf16 ? (el & 7) : (el & 15);
+    const uint32_t lds_lane = rl0 * kEpiPitch + cpi * (kBf16 ? 32 : 16);
+    // lane's byte offset inside a chunk of C (the launcher keeps 32 rows of
+    // C under 2 GiB for the unguarded path)
+    const uint32_t lane_off = ((uint32_t)rl0 * (uint32_t)ldc + cpi * (kBf16 ? 8 : 4)) * esize;
+    // chunk c = (i, jp): rows 32 i, columns 64 jp of the wave's block
+    auto stage = [&](int c) {
+        const int i = c >> 1, jp = c & 1;
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+            const v16f_t &a = acc[i][2 * jp + jj];
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+                *reinterpret_cast<float4 *>(ep + efr * kEpiPitch + (jj * 32 + 8 * g + 4 * efh) * 4) =
+                    make_float4(a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]);
+        }
+    };
+    auto fetch = [&](float4 (&r)[8]) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const uint32_t o = kBf16 ? lds_lane + (u >> 1) * rstep * kEpiPitch + (u & 1) * 16
+                                     : lds_lane + u * rstep * kEpiPitch;
+            r[u] = *reinterpret_cast<const float4 *>(ep + o);
+        }
+    };
+    auto store = [&](int c, float4 (&r)[8]) {
+        const int i = c >> 1, jp = c & 1;
+        if (kScale) {
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                r[u].x *= alpha; r[u].y *= alpha; r[u].z *= alpha; r[u].w *= alpha;
+            }
+        }
+        const int row0 = row_base + i * 32, col0 = col_base + jp * 64;
+        constexpr int npieces = kBf16 ? 4 : 8;
+        uint4 o[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            if constexpr (kBf16) {
+                if (u < 4) {
+                    const float4 lo = r[2 * u], hi = r[2 * u + 1];
+                    o[u].x = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo.x, lo.y}, bf16x2_t));
+                    o[u].y = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo.z, lo.w}, bf16x2_t));
+                    o[u].z = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){hi.x, hi.y}, bf16x2_t));
+                    o[u].w = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){hi.z, hi.w}, bf16x2_t));
+                }
+            } else {
+                o[u] = __builtin_bit_cast(uint4, r[u]);
+            }
+        }
+        if (full) {
+            uint8_t *base = reinterpret_cast<uint8_t *>(C) + ((int64_t)row0 * ldc + col0) * esize;
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (u < npieces)
+                    *reinterpret_cast<uint4 *>(base + (int64_t)u * rstep * ldc * esize + lane_off) = o[u];
+        } else {
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                if (u >= npieces) continue;
+                const int row = row0 + rl0 + u * rstep, col = col0 + cpi * (kBf16 ? 8 : 4);
+                if (row >= M) continue;
+                constexpr int ne = kBf16 ? 8 : 4;
+                uint8_t *dstp = reinterpret_cast<uint8_t *>(C) + ((int64_t)row * ldc + col) * esize;
+                if (vec_ok && col + ne <= N) {
+                    *reinterpret_cast<uint4 *>(dstp) = o[u];
+                } else if constexpr (kBf16) {
+                    const uint16_t *ov = reinterpret_cast<const uint16_t *>(&o[u]);
+                    for (int e = 0; e < 8; ++e)
+                        if (col + e < N) reinterpret_cast<uint16_t *>(dstp)[e] = ov[e];
+                } else {
+                    const float *ov = reinterpret_cast<const float *>(&o[u]);
+                    for (int e = 0; e < 4; ++e)
+                        if (col + e < N) reinterpret_cast<float *>(dstp)[e] = ov[e];
+                }
+            }
+        }
+    };
+    // Two-deep pipeline over the eight chunks: the LDS writes and reads of
+    // chunk c+1 are issued before chunk c is converted and stored, so one
+    // chunk's LDS latency hides behind the other's stores.  A wave's LDS
+    // operations run in issue order, so chunk c's reads complete before
+    // chunk c+1's writes reuse the area.
+    float4 r0[8], r1[8];
+    stage(0);
+    fetch(r0);
+#pragma unroll
+    for (int c = 0; c < 8; c += 2) {
+        stage(c + 1);
+        fetch(r1);
+        store(c, r0);
+        if (c + 2 < 8) {
+            stage(c + 2);
+            fetch(r0);
+        }
+        store(c + 1, r1);
+    }
+}
+
+// The epilogue for a runtime output type and alpha.
+__device__ __forceinline__ void store_wave_block_any(const v16f_t (&acc)[4][4], uint8_t *ep, int el, int row_base,
+                                                     int col_base, int M, int N, float alpha, void *C, int64_t ldc,
+                                                     bool c_bf16, bool vec_ok)
+{
+    const bool full = vec_ok && row_base + 128 <= M && col_base + 128 <= N;
+    if (c_bf16) {
+        if (alpha != 1.0f)
+            store_wave_block<true, true>(acc, ep, el, row_base, col_base, M, N, alpha, C, ldc, vec_ok, full);
+        else
+            store_wave_block<false, true>(acc, ep, el, row_base, col_base, M, N, alpha, C, ldc, vec_ok, full);
+    } else {
+        if (alpha != 1.0f)
+            store_wave_block<true, false>(acc, ep, el, row_base, col_base, M, N, alpha, C, ldc, vec_ok, full);
+        else
+            store_wave_block<false, false>(acc, ep, el, row_base, col_base, M, N, alpha, C, ldc, vec_ok, full);
+    }
+}
+
+// C = 0 (the K == 0 product); one thread per element.
+static __global__ void fill_zero_kernel(void *__restrict__ C, int M, int N, int64_t ldc, int c_bf16)
+{
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= (int64_t)M * N) return;
+    const int64_t r = i / N, c = i - r * N;
+    if (c_bf16)
+        reinterpret_cast<uint16_t *>(C)[r * ldc + c] = 0;
+    else
+        reinterpret_cast<float *>(C)[r * ldc + c] = 0.0f;
+}
+
+}  // namespace gemm
+}  // namespace fp4q

@@ -26,6 +26,7 @@
 
 #include "fp4q_device.h"
 #include "fp4q_internal.h"
+#include "gemm_common.h"
 
 namespace fp4q {
 
@@ -69,7 +70,7 @@ __device__ __forceinline__ void dequant32(const uint4 &q, float s0, float s1, ui
 }
 
 template <bool kTile>
-__global__ __launch_bounds__(256) void gemm_nv_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
+__global__ __launch_bounds__(256) void gemm_nv_tile_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
                                                       const float *__restrict__ Ats, const uint8_t *__restrict__ B,
                                                       const uint8_t *__restrict__ Bs, const float *__restrict__ Bts,
                                                       int M, int N, int K, float alpha, void *__restrict__ C,
@@ -186,15 +187,297 @@ __global__ __launch_bounds__(256) void gemm_nv_kernel(const uint8_t *__restrict_
         }
 }
 
-__global__ void nv_fill_zero_kernel(void *__restrict__ C, int M, int N, int64_t ldc, int c_bf16)
+
+// ------------------------------------------------------------------
+// Global domain: persistent kernel on fp16 matrix cores.
+//
+// An E2M1 value times an E4M3 scale has at most 6 significant bits and lies
+// in [2^-10, 2688], so it is exact in fp16 as well as bf16; fp16 has packed
+// multiplies on gfx950 (bf16 has none), so each pair of elements dequantizes
+// in two instructions: v_cvt_scalef32_pk_f16_fp4 (scale 1: the E2M1 values)
+// and v_pk_mul_f16 by the block's E4M3 value.  (The scaled convert itself
+// applies only the exponent of its scale operand, which an E4M3 value with a
+// mantissa would lose.)  Products on v_mfma_f32_32x32x16_f16 are then exact
+// and only the fp32 accumulation rounds; S_A * S_B * alpha is applied in the
+// epilogue.
+//
+// Structure as the MX kernel: one 256-thread workgroup per CU walks
+// 256 x 256 tiles (four waves of 128 x 128, B fragment first so the
+// accumulators hold row pieces), a four-slot LDS ring of 128-wide K steps
+// filled by LDS DMA three steps ahead, and the shared epilogue.  Each wave
+// dequantizes the fragments it multiplies, in registers, one 16-wide K slice
+// ahead of the matrix cores.
+//
+// K order inside a step.  The matrix cores only need A and B to agree on
+// which K a lane position carries, so slice s (0..7) of a 128-wide step
+// gives lanes 0..31 the K values 8s .. 8s+7 and lanes 32..63 the values
+// 64 + 8s .. 64 + 8s + 7.  A lane's 4 slices s = 4q .. 4q+3 are then 16
+// contiguous code bytes (chunk 2h + q of its row's 64 bytes): one 16-byte
+// LDS read per row per 4 slices.  Its 16-element NV block for slice s is
+// 4h + s/2: byte s/2 of the 32-bit word at row offset 4h of the step's 8
+// scale bytes.
+//
+// LDS image of a stage: codes of 256 rows x 64 bytes per operand with the
+// 16-byte chunk c of local row r at r * 64 + 16 (c ^ ((r >> 1) & 3)) (the
+// DMA lane mapping applies the swizzle, so 8 lanes reading one chunk of 8
+// consecutive rows hit 8 distinct bank groups), then 8 scale bytes per row.
+// ------------------------------------------------------------------
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+
+constexpr int gStages = 4;
+constexpr int gCodeBytes = 256 * 64;                     // one operand's codes per K step
+constexpr int gScaleBytes = 256 * 8;                     // one operand's E4M3 bytes per K step
+constexpr int gAS = 2 * gCodeBytes;                      // A scales, then B scales
+constexpr int gBS = gAS + gScaleBytes;
+constexpr int gStageBytes = 2 * gCodeBytes + 2 * gScaleBytes;  // 36 KiB
+constexpr int gLdsBytes = gStages * gStageBytes;               // 144 KiB
+constexpr int gDmaPerStage = 12;  // per wave: 4 A-code, 4 B-code, 2 A-scale, 2 B-scale instructions
+static_assert(4 * gemm::kEpiWaveBytes <= gStageBytes, "epilogue staging must fit in one ring slot");
+
+// 8 codes (one 32-bit word, element 2b in the low nibble of byte b) times a
+// block scale given as two equal fp16 values.
+__device__ __forceinline__ half8_t dequant8(uint32_t w, half2_t s2)
 {
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= (int64_t)M * N) return;
-    const int64_t r = i / N, c = i - r * N;
-    if (c_bf16)
-        reinterpret_cast<uint16_t *>(C)[r * ldc + c] = 0;
-    else
-        reinterpret_cast<float *>(C)[r * ldc + c] = 0.0f;
+    const half2_t p0 = __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0)) * s2;
+    const half2_t p1 = __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1)) * s2;
+    const half2_t p2 = __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2)) * s2;
+    const half2_t p3 = __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3)) * s2;
+    return (half8_t){p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
+// E4M3 byte b of word w as two equal fp16 (exact: every E4M3 value is an
+// fp16 normal).
+template <int b>
+__device__ __forceinline__ half2_t scale2(uint32_t w)
+{
+    const float f = __builtin_amdgcn_cvt_f32_fp8((int)w, b);
+    return __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_pkrtz(f, f));
+}
+
+__global__ __launch_bounds__(256) void gemm_nv_global_kernel(
+    const uint8_t *__restrict__ A, const uint8_t *__restrict__ As, const float *__restrict__ Ats,
+    const uint8_t *__restrict__ B, const uint8_t *__restrict__ Bs, const float *__restrict__ Bts, int M, int N, int K,
+    float alpha, void *__restrict__ C, int64_t ldc, int c_bf16, int vec_ok, int tiles_m, int tiles_n)
+{
+    using namespace gemm;
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[gLdsBytes];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    const int fr = lane & 31, fh = lane >> 5;
+    const uint32_t KB = (uint32_t)K >> 1;  // code bytes per row
+    const uint32_t KS = (uint32_t)K >> 4;  // scale bytes per row
+    const int nk = K >> 7;
+    const uint32_t lds_base = (uint32_t)(uintptr_t)lds;
+    const int ntiles = tiles_m * tiles_n;
+
+    // per-lane DMA sources of the current tile (see the stage image above)
+    uint32_t a_goff[4], b_goff[4], as_goff[2], bs_goff[2];
+    int m0 = 0, n0 = 0;
+    const uint8_t *pa = A, *pb = B, *pas = As, *pbs = Bs;
+    int dstep = 0;
+    auto setup = [&](int tile) {
+        int tm, tn;
+        tile_coords(tile, tiles_m, tiles_n, tm, tn);
+        m0 = tm * 256;
+        n0 = tn * 256;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const uint32_t r = 64 * wave + 16 * t + (lane >> 2);  // local row
+            const uint32_t c = (uint32_t)(lane & 3) ^ ((r >> 1) & 3u);
+            a_goff[t] = (uint32_t)min(m0 + (int)r, M - 1) * KB + c * 16;
+            b_goff[t] = (uint32_t)min(n0 + (int)r, N - 1) * KB + c * 16;
+        }
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const uint32_t r = 64 * wave + 32 * t + (lane >> 1);
+            as_goff[t] = (uint32_t)min(m0 + (int)r, M - 1) * KS + (lane & 1) * 4;
+            bs_goff[t] = (uint32_t)min(n0 + (int)r, N - 1) * KS + (lane & 1) * 4;
+        }
+        pa = A;
+        pb = B;
+        pas = As;
+        pbs = Bs;
+        dstep = 0;
+    };
+    // the d-th of this wave's 12 DMA instructions of a step into the stage at slot_addr
+    auto dma_piece = [&](uint32_t slot_addr, auto d_tag) {
+        constexpr int d = decltype(d_tag)::value;
+        if constexpr (d < 4)
+            dma16<0>(pa, a_goff[d], slot_addr + (64 * wave + 16 * d) * 64);
+        else if constexpr (d < 8)
+            dma16<gCodeBytes>(pb, b_goff[d - 4], slot_addr + (64 * wave + 16 * (d - 4)) * 64);
+        else if constexpr (d < 10)
+            dma4<gAS>(pas, as_goff[d - 8], slot_addr + (64 * wave + 32 * (d - 8)) * 8);
+        else
+            dma4<gBS>(pbs, bs_goff[d - 10], slot_addr + (64 * wave + 32 * (d - 10)) * 8);
+    };
+    auto advance = [&]() {
+        const uint32_t more = dstep < nk - 1 ? 1u : 0u;
+        pa += more * 64u;
+        pb += more * 64u;
+        pas += more * 8u;
+        pbs += more * 8u;
+        dstep += (int)more;
+    };
+    auto prologue = [&]() {
+#pragma unroll
+        for (int s2 = 0; s2 < gStages - 1; ++s2) {
+            const uint32_t slot_addr = lds_base + s2 * gStageBytes;
+            static_for<gDmaPerStage>([&](auto d) { dma_piece(slot_addr, d); });
+            advance();
+        }
+    };
+
+    // fragment sources: local rows of this wave's block rows / columns
+    auto code_chunk = [&](const uint8_t *st, int operand, int i, int q) -> uint4 {
+        const uint32_t r = (operand == 0 ? wm * 128 : wn * 128) + 32 * i + fr;
+        const uint32_t c = (uint32_t)(2 * fh + q) ^ ((r >> 1) & 3u);
+        return *reinterpret_cast<const uint4 *>(st + operand * gCodeBytes + r * 64 + c * 16);
+    };
+    auto scale_word = [&](const uint8_t *st, int operand, int i) -> uint32_t {
+        const uint32_t r = (operand == 0 ? wm * 128 : wn * 128) + 32 * i + fr;
+        return *reinterpret_cast<const uint32_t *>(st + gAS + operand * gScaleBytes + r * 8 + fh * 4);
+    };
+
+    v16f_t acc[4][4];
+    uint4 rawA[4][2], rawB[4][2];   // code chunks of the step (q = 0, 1)
+    uint32_t swA[4], swB[4];        // scale words of the step
+    uint32_t nswA[4], nswB[4];      // scale words of the next step
+    half2_t sA2[4], sB2[4];         // block scales of the current slice pair
+    half8_t fa[4], fb[4];           // fragments of the slice on the matrix cores
+    half8_t na[4], nb[4];           // fragments of the next slice
+
+    auto word_of = [&](const uint4 &q, int d) -> uint32_t {
+        return d == 0 ? q.x : d == 1 ? q.y : d == 2 ? q.z : q.w;
+    };
+
+    int tile = blockIdx.x;
+    setup(tile);
+    prologue();
+    for (;;) {
+        // stages 0 and 1 of this tile have landed (only stage 2's DMA may be
+        // in flight; loads complete in order)
+        wait_and_barrier<gDmaPerStage>();
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            rawA[i][0] = code_chunk(lds, 0, i, 0);
+            rawA[i][1] = code_chunk(lds, 0, i, 1);
+            rawB[i][0] = code_chunk(lds, 1, i, 0);
+            rawB[i][1] = code_chunk(lds, 1, i, 1);
+            swA[i] = scale_word(lds, 0, i);
+            swB[i] = scale_word(lds, 1, i);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            sA2[i] = scale2<0>(swA[i]);
+            sB2[i] = scale2<0>(swB[i]);
+            fa[i] = dequant8(rawA[i][0].x, sA2[i]);
+            fb[i] = dequant8(rawB[i][0].x, sB2[i]);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[i][j] = (v16f_t){};
+
+        uint32_t off_cur = 0, off_nxt = gStageBytes, off_n2 = 2 * gStageBytes, off_dma = 3 * gStageBytes;
+        for (int ks = 0; ks < nk; ++ks) {
+            // stage ks+1 has landed for every wave, and every wave is done
+            // with stage ks-1 (read in steps ks-2 and ks-1): its slot takes
+            // the DMA of step ks+3
+            if (ks > 0) wait_and_barrier<gDmaPerStage>();
+            const uint8_t *stn = lds + off_nxt;
+            const uint32_t dma_addr = lds_base + off_dma;
+            const uint32_t more = dstep < nk - 1 ? 1u : 0u;
+            // 8 slices of 16 MFMAs; slice s+1 is dequantized while slice s runs
+            static_for<8>([&](auto s_tag) {
+                constexpr int s = decltype(s_tag)::value;
+                constexpr int sn = s + 1;  // the slice being prepared (8 = slice 0 of step ks+1)
+                static_for<16>([&](auto t_tag) {
+                    constexpr int t = decltype(t_tag)::value;
+                    constexpr int i = t >> 2, j = t & 3;
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[j], fa[i], acc[i][j], 0, 0, 0);
+                    // DMA of step ks+3: two instructions per slice in slices 0..5
+                    if constexpr (t < 2 && 2 * s + t < gDmaPerStage)
+                        dma_piece(dma_addr, std::integral_constant<int, 2 * s + t>{});
+                    // next step's operands: q = 0 chunks and scale words once
+                    // the current q = 0 chunks are consumed (slice 3 was
+                    // prepared during slice 2), q = 1 chunks at the start of
+                    // the next step (this step's slice 7 was prepared during
+                    // slice 6)
+                    if constexpr (s == 4 && t < 4) {
+                        rawA[t][0] = code_chunk(stn, 0, t, 0);
+                        nswA[t] = scale_word(stn, 0, t);
+                    }
+                    if constexpr (s == 4 && t >= 4 && t < 8) {
+                        rawB[t - 4][0] = code_chunk(stn, 1, t - 4, 0);
+                        nswB[t - 4] = scale_word(stn, 1, t - 4);
+                    }
+                    if constexpr (s == 0 && t >= 8 && t < 12) {
+                        if (ks > 0) rawA[t - 8][1] = code_chunk(lds + off_cur, 0, t - 8, 1);
+                    }
+                    if constexpr (s == 0 && t >= 12) {
+                        if (ks > 0) rawB[t - 12][1] = code_chunk(lds + off_cur, 1, t - 12, 1);
+                    }
+                    // pointer updates after the step's last DMA
+                    if constexpr (s == 6 && t < 4) {
+                        if (t == 0) { pa += more * 64u; asm volatile("" : "+s"(pa)); }
+                        if (t == 1) { pb += more * 64u; asm volatile("" : "+s"(pb)); }
+                        if (t == 2) { pas += more * 8u; asm volatile("" : "+s"(pas)); }
+                        if (t == 3) { pbs += more * 8u; asm volatile("" : "+s"(pbs)); }
+                    }
+                    // dequantize slice sn: fragment t/2 of A (even t) or B (odd t) in slots 0..7,
+                    // block scales of a new slice pair first (slots 0..7 too)
+                    if constexpr (t < 8) {
+                        constexpr int f = t >> 1;
+                        constexpr int ss = sn & 7, q = ss >> 2, d = ss & 3, b = ss >> 1;
+                        if constexpr ((ss & 1) == 0) {
+                            if constexpr ((t & 1) == 0)
+                                sA2[f] = scale2<b>(sn == 8 ? nswA[f] : swA[f]);
+                            else
+                                sB2[f] = scale2<b>(sn == 8 ? nswB[f] : swB[f]);
+                        }
+                        if constexpr ((t & 1) == 0)
+                            na[f] = dequant8(word_of(rawA[f][q], d), sA2[f]);
+                        else
+                            nb[f] = dequant8(word_of(rawB[f][q], d), sB2[f]);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                });
+#pragma unroll
+                for (int f = 0; f < 4; ++f) {
+                    fa[f] = na[f];
+                    fb[f] = nb[f];
+                }
+            });
+            dstep += (int)more;
+#pragma unroll
+            for (int f = 0; f < 4; ++f) {
+                swA[f] = nswA[f];
+                swB[f] = nswB[f];
+            }
+            const uint32_t o = off_cur;
+            off_cur = off_nxt;
+            off_nxt = off_n2;
+            off_n2 = off_dma;
+            off_dma = o;
+        }
+        wait_and_barrier<0>();
+        const int tm0 = m0, tn0 = n0;
+        const int next = tile + (int)gridDim.x;
+        if (next < ntiles) {
+            setup(next);
+            prologue();
+        }
+        uint8_t *ep = lds + (gStages - 1) * gStageBytes + wave * kEpiWaveBytes;
+        int el;
+        asm volatile("v_mov_b32 %0, %1" : "=v"(el) : "v"(lane));
+        store_wave_block_any(acc, ep, el, tm0 + wm * 128, tn0 + wn * 128, M, N, alpha * (Ats[0] * Bts[0]), C, ldc,
+                             c_bf16 != 0, vec_ok != 0);
+        if (next >= ntiles) break;
+        tile = next;
+    }
 }
 
 }  // namespace
@@ -205,21 +488,30 @@ int launch_gemm_nv(const GemmArgs &g, hipStream_t st)
     if (M == 0 || N == 0) return 0;
     if (K == 0) {
         const int64_t n = (int64_t)M * N;
-        hipLaunchKernelGGL(nv_fill_zero_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, g.c, M, N,
+        hipLaunchKernelGGL(gemm::fill_zero_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, g.c, M, N,
                            g.ldc, (int)g.c_bf16);
         return hipGetLastError() == hipSuccess ? 0 : 1;
     }
-    const int tiles_m = (M + kBM - 1) / kBM, tiles_n = (N + kBN - 1) / kBN;
     auto *a = reinterpret_cast<const uint8_t *>(g.a_codes);
     auto *as = reinterpret_cast<const uint8_t *>(g.a_scales);
     auto *b = reinterpret_cast<const uint8_t *>(g.b_codes);
     auto *bs = reinterpret_cast<const uint8_t *>(g.b_scales);
-    if (g.nv_domain == 1)
-        hipLaunchKernelGGL(gemm_nv_kernel<true>, dim3(tiles_m * tiles_n), dim3(256), 0, st, a, as, g.a_ts, b, bs,
+    if (g.nv_domain == 1) {
+        const int tiles_m = (M + kBM - 1) / kBM, tiles_n = (N + kBN - 1) / kBN;
+        hipLaunchKernelGGL(gemm_nv_tile_kernel<true>, dim3(tiles_m * tiles_n), dim3(256), 0, st, a, as, g.a_ts, b, bs,
                            g.b_ts, M, N, K, g.alpha, g.c, g.ldc, (int)g.c_bf16, tiles_n);
-    else
-        hipLaunchKernelGGL(gemm_nv_kernel<false>, dim3(tiles_m * tiles_n), dim3(256), 0, st, a, as, g.a_ts, b, bs,
-                           g.b_ts, M, N, K, g.alpha, g.c, g.ldc, (int)g.c_bf16, tiles_n);
+    } else {
+        const int esize = g.c_bf16 ? 2 : 4;
+        const int vec_ok = ((uintptr_t)g.c % 16 == 0) && (g.ldc % (16 / esize) == 0) && g.ldc <= (int64_t(1) << 26);
+        const int tiles_m = (M + 255) / 256, tiles_n = (N + 255) / 256;
+        int dev = 0, cus = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+            return 1;
+        const int grid = min(tiles_m * tiles_n, cus);
+        hipLaunchKernelGGL(gemm_nv_global_kernel, dim3(grid), dim3(256), 0, st, a, as, g.a_ts, b, bs, g.b_ts, M, N, K,
+                           g.alpha, g.c, g.ldc, (int)g.c_bf16, vec_ok, tiles_m, tiles_n);
+    }
     return hipGetLastError() == hipSuccess ? 0 : 1;
 }
 
