@@ -227,9 +227,8 @@ def build_workload(name, dev, copies, layout_name="tiled"):
 
 def read_traffic(kernel, workload):
     """HBM bytes per launch from a committed rocprofv3 counter summary, if one
-    exists for this kernel and workload and still matches the kernel source."""
-    import hashlib
-
+    exists for this kernel and workload and still matches the kernel source
+    (`source` lists the files, comma-separated)."""
     path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_pmc.txt")
     if not os.path.exists(path):
         return None
@@ -242,10 +241,21 @@ def read_traffic(kernel, workload):
     src = vals.get("source")
     if not src or "traffic_bytes" not in vals:
         return None
-    h = hashlib.sha256(open(os.path.join(ROOT, src), "rb").read()).hexdigest()[:16]
-    if h != vals.get("source_sha256_16"):
+    if source_hash(src.split(",")) != vals.get("source_sha256_16"):
         return None  # kernel changed since the counters were taken
     return float(vals["traffic_bytes"])
+
+
+def source_hash(paths):
+    """SHA-256 (first 16 hex digits) of the kernel's source files, concatenated
+    in the order given."""
+    import hashlib
+
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p.strip()), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def cpu_baseline(workload):
