@@ -216,7 +216,7 @@ def build_workload(name, dev, copies, layout_name="tiled"):
     ops = [
         ("quantize X (NVFP4)", kname, qnv("x", X, M), M * K * bpe, "GB/s", HBM_PEAK_GBS, "hbm"),
         ("quantize W (NVFP4)", kname, qnv("w", W, N), N * K * bpe, "GB/s", HBM_PEAK_GBS, "hbm"),
-        ("GEMM NVFP4 (fp16 MFMA)", "gemm_nv_global_kernel" if domain == B.NV_GLOBAL else "gemm_nv_tile_kernel",
+        ("GEMM NVFP4 (fp16 MFMA)", "gemm_nv_fp16_kernel",
          lambda s: B.fp4_gemm_nv(bufs["x"][0], bufs["x"][1], bufs["x"][2], bufs["w"][0], bufs["w"][1], bufs["w"][2],
                                  domain, c=C), 2.0 * M * N * K, "TFLOP/s", BF16_PEAK_TFLOPS, "mfma"),
     ]

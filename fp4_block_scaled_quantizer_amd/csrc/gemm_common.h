@@ -79,12 +79,12 @@ __device__ __forceinline__ void static_for(F &&f)
     }
 }
 
-// Epilogue of a wave's 128 x 128 block of C, held as a 4 x 4 grid of 32 x 32
-// accumulator blocks in which the B fragment was the matrix cores' first
+// Epilogue of a wave's 128 x 128 (or 128 x 64) block of C, held as a 4 x 4
+// (4 x 2) grid of 32 x 32 accumulator blocks in which the B fragment was the matrix cores' first
 // operand: register r of lane l holds C[row (l mod 32)][col 8 (r/4) +
 // 4 (l/32) + r mod 4] of its block, so each aligned group of four
 // accumulator registers is four consecutive columns of one row.  The block
-// is written in eight chunks of 32 rows x 64 columns: 16-byte LDS writes
+// is written in chunks of 32 rows x 64 columns: 16-byte LDS writes
 // straight from the accumulator registers into the wave's staging area `ep`
 // (kEpiWaveBytes), then 16-byte LDS reads of row pieces, alpha (skipped when
 // kScale is false), conversion (bf16: v_cvt_pk_bf16_f32, round to nearest
@@ -94,11 +94,13 @@ __device__ __forceinline__ void static_for(F &&f)
 // inside C with 16-byte aligned rows (then no guards are evaluated); the
 // lane index `el` is passed in from an opaque copy so that the lane-derived
 // offsets are recomputed here rather than kept live across the K loop.
-template <bool kScale, bool kBf16>
-__device__ __forceinline__ void store_wave_block(const v16f_t (&acc)[4][4], uint8_t *ep, int el, int row_base,
+template <int kNJ, bool kScale, bool kBf16>
+__device__ __forceinline__ void store_wave_block(const v16f_t (&acc)[4][kNJ], uint8_t *ep, int el, int row_base,
                                                  int col_base, int M, int N, float alpha, void *C, int64_t ldc,
                                                  bool vec_ok, bool full)
 {
+    static_assert(kNJ == 2 || kNJ == 4, "a wave block is 128 rows x 64 or 128 columns");
+    constexpr int kChunks = 2 * kNJ;  // 32 x 64 chunks
     constexpr int esize = kBf16 ? 2 : 4;
     const int efr = el & 31, efh = el >> 5;
     // A lane's pieces of a staged chunk: bf16 pieces are (row el/8 + 8u,
@@ -113,7 +115,7 @@ __device__ __forceinline__ void store_wave_block(const v16f_t (&acc)[4][4], uint
     const uint32_t lane_off = ((uint32_t)rl0 * (uint32_t)ldc + cpi * (kBf16 ? 8 : 4)) * esize;
     // chunk c = (i, jp): rows 32 i, columns 64 jp of the wave's block
     auto stage = [&](int c) {
-        const int i = c >> 1, jp = c & 1;
+        const int i = c / (kNJ / 2), jp = c % (kNJ / 2);
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj) {
             const v16f_t &a = acc[i][2 * jp + jj];
@@ -132,7 +134,7 @@ __device__ __forceinline__ void store_wave_block(const v16f_t (&acc)[4][4], uint
         }
     };
     auto store = [&](int c, float4 (&r)[8]) {
-        const int i = c >> 1, jp = c & 1;
+        const int i = c / (kNJ / 2), jp = c % (kNJ / 2);
         if (kScale) {
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
@@ -193,11 +195,11 @@ __device__ __forceinline__ void store_wave_block(const v16f_t (&acc)[4][4], uint
     stage(0);
     fetch(r0);
 #pragma unroll
-    for (int c = 0; c < 8; c += 2) {
+    for (int c = 0; c < kChunks; c += 2) {
         stage(c + 1);
         fetch(r1);
         store(c, r0);
-        if (c + 2 < 8) {
+        if (c + 2 < kChunks) {
             stage(c + 2);
             fetch(r0);
         }
@@ -206,21 +208,22 @@ __device__ __forceinline__ void store_wave_block(const v16f_t (&acc)[4][4], uint
 }
 
 // The epilogue for a runtime output type and alpha.
-__device__ __forceinline__ void store_wave_block_any(const v16f_t (&acc)[4][4], uint8_t *ep, int el, int row_base,
+template <int kNJ>
+__device__ __forceinline__ void store_wave_block_any(const v16f_t (&acc)[4][kNJ], uint8_t *ep, int el, int row_base,
                                                      int col_base, int M, int N, float alpha, void *C, int64_t ldc,
                                                      bool c_bf16, bool vec_ok)
 {
-    const bool full = vec_ok && row_base + 128 <= M && col_base + 128 <= N;
+    const bool full = vec_ok && row_base + 128 <= M && col_base + 32 * kNJ <= N;
     if (c_bf16) {
         if (alpha != 1.0f)
-            store_wave_block<true, true>(acc, ep, el, row_base, col_base, M, N, alpha, C, ldc, vec_ok, full);
+            store_wave_block<kNJ, true, true>(acc, ep, el, row_base, col_base, M, N, alpha, C, ldc, vec_ok, full);
         else
-            store_wave_block<false, true>(acc, ep, el, row_base, col_base, M, N, alpha, C, ldc, vec_ok, full);
+            store_wave_block<kNJ, false, true>(acc, ep, el, row_base, col_base, M, N, alpha, C, ldc, vec_ok, full);
     } else {
         if (alpha != 1.0f)
-            store_wave_block<true, false>(acc, ep, el, row_base, col_base, M, N, alpha, C, ldc, vec_ok, full);
+            store_wave_block<kNJ, true, false>(acc, ep, el, row_base, col_base, M, N, alpha, C, ldc, vec_ok, full);
         else
-            store_wave_block<false, false>(acc, ep, el, row_base, col_base, M, N, alpha, C, ldc, vec_ok, full);
+            store_wave_block<kNJ, false, false>(acc, ep, el, row_base, col_base, M, N, alpha, C, ldc, vec_ok, full);
     }
 }
 

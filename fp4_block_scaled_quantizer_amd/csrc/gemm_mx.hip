@@ -53,7 +53,8 @@ constexpr int kRingBytes = kStages * kStageBytes;           // 136 KiB
 static_assert(4 * kEpiWaveBytes <= kStageBytes, "epilogue staging must fit in one ring slot");
 constexpr int kLdsBytes = kRingBytes;
 constexpr int kDmaPerStage = 10;                            // DMA instructions per wave per stage
-constexpr int kDmaPerPhase = kDmaPerStage / 2;
+constexpr int kDmaA = kDmaPerStage / 2;                    // DMA instructions in phase A; the rest in phase B
+constexpr int kDmaB = kDmaPerStage - kDmaA;
 
 // Persistent kernel: one workgroup per CU walks tiles b, b + G, b + 2G, ...
 // (G = grid size).  Each tile: 256 x 256 outputs, four waves of 128 x 128.
@@ -251,23 +252,23 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(const uint8_t *__restrict_
                 constexpr int i = t >> 2, j = t & 3;
                 acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb0[j], fa0[i], acc[i][j], 4, 4, 0,
                                                                              (int)sb[j], 0, (int)sa[i]);
-                if constexpr (t < kDmaPerPhase) dma_piece(dma_addr, t_tag);
+                if constexpr (t < kDmaA) dma_piece(dma_addr, t_tag);
                 if constexpr (t < 4) fa1[t] = frag(st, 0, t, 1);
                 else if constexpr (t < 8) fb1[t - 4] = frag(st, 1, t - 4, 1);
                 __builtin_amdgcn_sched_barrier(0);
             });
             // step ks+1's DMA was issued two steps ago; after it only step
-            // ks+2's DMA and this step's first kDmaPerPhase instructions may
+            // ks+2's DMA and this step's first kDmaA instructions may
             // still be in flight
-            wait_and_barrier<(kStages - 3) * kDmaPerStage + kDmaPerPhase>();
+            wait_and_barrier<(kStages - 3) * kDmaPerStage + kDmaA>();
             const uint32_t more = dstep < nk - 1 ? 1u : 0u;
             static_for<16>([&](auto t_tag) {
                 constexpr int t = decltype(t_tag)::value;
                 constexpr int i = t >> 2, j = t & 3;
                 acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb1[j], fa1[i], acc[i][j], 4, 4, 2,
                                                                              (int)sb[j], 2, (int)sa[i]);
-                if constexpr (t < kDmaPerPhase)
-                    dma_piece(dma_addr, std::integral_constant<int, kDmaPerPhase + t>{});
+                if constexpr (t < kDmaB)
+                    dma_piece(dma_addr, std::integral_constant<int, kDmaA + t>{});
                 // next step's operands, in the order phase A consumes them,
                 // two per slot so they land well before the phase ends
                 if constexpr (t < 8) {
@@ -294,7 +295,7 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(const uint8_t *__restrict_
                         asm volatile("" : "+v"(nsa[q]));
                     }
                 }
-                if constexpr (t >= kDmaPerPhase && t < kDmaPerPhase + 4) advance_ptr(t - kDmaPerPhase, more);
+                if constexpr (t >= kDmaB && t < kDmaB + 4) advance_ptr(t - kDmaB, more);
                 __builtin_amdgcn_sched_barrier(0);
             });
             dstep += (int)more;

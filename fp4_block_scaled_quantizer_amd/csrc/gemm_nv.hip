@@ -1,5 +1,5 @@
-// gemm_nv.hip -- NVFP4 GEMM: exact dequantization to bf16 in LDS, bf16
-// matrix cores, FP32 tensor scales on the fp32 partial sums.
+// gemm_nv.hip -- NVFP4 GEMM on fp16 matrix cores with in-register exact
+// dequantization; FP32 tensor scales applied to fp32 sums.
 //
 // Pages cited (titles as printed):
 //   [Stack]  "FP4 Is No Longer Just a Hardware Feature -- The NVFP4 Software
@@ -11,16 +11,16 @@
 //            Format-Aware Fusion": global nvfp and CTA-local nvfp domains.
 //
 // gfx950's scaled matrix-core instruction takes one power-of-two (E8M0)
-// scale per 32 elements, which cannot carry an E4M3 scale per 16.  An E2M1
-// value has at most 2 significant bits and an E4M3 value at most 4, so their
-// product has at most 6 and is exact in bf16 (8 significant bits, the binary32
-// exponent range).  The kernel therefore dequantizes each K slice of A and B
-// into bf16 in LDS and multiplies on v_mfma_f32_32x32x16_bf16: every product
-// is exact and only the fp32 accumulation rounds.  The tensor scales are
-// applied to fp32 sums: once in the epilogue for the global domain, and per
-// 128-wide K slice for the per-tile domain (a slice is one tile column of both
-// operands, and a 128-row block of A or B lies in one tile row, so one factor
-// S_A(tm, kt) * S_B(tn, kt) covers a workgroup's whole slice).
+// scale per 32 elements, which cannot carry an E4M3 scale per 16.  The
+// kernel therefore dequantizes the E2M1 codes times their E4M3 block scale
+// exactly into fp16 and multiplies on v_mfma_f32_32x32x16_f16: every
+// product is exact and only the fp32 accumulation rounds.  The tensor scales
+// are applied to fp32 sums: once in the epilogue for the global domain, and
+// per 128-wide K step for the per-tile domain (a step is one tile column of
+// both operands, and a wave's 128-row block of A or 64-row block of B lies in
+// one tile row, so one factor S_A(tm, kt) * S_B(tn, kt) covers a wave's whole
+// partial sum of the step).
+
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -32,164 +32,8 @@ namespace fp4q {
 
 namespace {
 
-typedef short v8s_t __attribute__((ext_vector_type(8)));
-typedef float v16f_t __attribute__((ext_vector_type(16)));
-
-constexpr int kBM = 128, kBN = 128, kBK = 64;
-constexpr int kRowBytes = kBK * 2 + 16;                 // 64 bf16 + 16 pad
-constexpr int kStageBytes = (kBM + kBN) * kRowBytes;    // 36 KiB
-constexpr int kLdsBytes = 2 * kStageBytes;
-
-// E2M1 code (4 bits) -> binary32 bits: exponent field e = (c >> 1) & 3, mantissa
-// bit c & 1; e = 0 is the subnormal 0 / 0.5.
-__device__ __forceinline__ uint32_t e2m1_bits(uint32_t c)
-{
-    const uint32_t e = (c >> 1) & 3u, m = c & 1u, s = (c & 8u) << 28;
-    const uint32_t mag = e ? (((e + 126u) << 23) | (m << 22)) : (m ? 0x3F000000u : 0u);
-    return s | mag;
-}
-
-// Dequantize 32 codes (16 bytes, two 16-element NV blocks with scale values
-// s0, s1) into 32 bf16 and store them as 64 bytes at dst.  Each product is
-// exact, so truncating the binary32 to its upper half is the exact bf16.
-__device__ __forceinline__ void dequant32(const uint4 &q, float s0, float s1, uint8_t *dst)
-{
-    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-        const float sc = d < 2 ? s0 : s1;
-        uint32_t o[4];
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            const float lo = u2f(e2m1_bits((w[d] >> (8 * p)) & 0xFu)) * sc;
-            const float hi = u2f(e2m1_bits((w[d] >> (8 * p + 4)) & 0xFu)) * sc;
-            o[p] = (f2u(lo) >> 16) | (f2u(hi) & 0xFFFF0000u);
-        }
-        *reinterpret_cast<uint4 *>(dst + 16 * d) = make_uint4(o[0], o[1], o[2], o[3]);
-    }
-}
-
-template <bool kTile>
-__global__ __launch_bounds__(256) void gemm_nv_tile_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
-                                                      const float *__restrict__ Ats, const uint8_t *__restrict__ B,
-                                                      const uint8_t *__restrict__ Bs, const float *__restrict__ Bts,
-                                                      int M, int N, int K, float alpha, void *__restrict__ C,
-                                                      int64_t ldc, int c_bf16, int tiles_n)
-{
-    __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
-    const int tm = blockIdx.x / tiles_n, tn = blockIdx.x - tm * tiles_n;
-    const int m0 = tm * kBM, n0 = tn * kBN;
-    const uint32_t KB = (uint32_t)K >> 1, KS = (uint32_t)K >> 4;
-    const int nk = K / kBK;
-    const int TK = (K + 127) >> 7;
-
-    // dequant assignment: thread t handles 32 K-elements (half t & 1) of row
-    // t >> 1 of both operands
-    const int drow = tid >> 1, dh = tid & 1;
-    const int ra = min(m0 + drow, M - 1), rb = min(n0 + drow, N - 1);
-    const uint8_t *a_src = A + (size_t)ra * KB + dh * 16;
-    const uint8_t *b_src = B + (size_t)rb * KB + dh * 16;
-    const uint8_t *as_src = As + (size_t)ra * KS + dh * 2;
-    const uint8_t *bs_src = Bs + (size_t)rb * KS + dh * 2;
-    const int st_off = drow * kRowBytes + dh * 64;
-
-    const int fr = lane & 31, fh = lane >> 5;
-    const int fa_off = (wm * 64 + fr) * kRowBytes + fh * 16;
-    const int fb_off = kBM * kRowBytes + (wn * 64 + fr) * kRowBytes + fh * 16;
-
-    v16f_t acc[2][2], part[2][2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            acc[i][j] = (v16f_t){};
-            part[i][j] = (v16f_t){};
-        }
-
-    auto load_stage = [&](int ks, uint4 &qa, uint4 &qb, uint32_t &sa, uint32_t &sb) {
-        qa = *reinterpret_cast<const uint4 *>(a_src + ks * (kBK / 2));
-        qb = *reinterpret_cast<const uint4 *>(b_src + ks * (kBK / 2));
-        sa = *reinterpret_cast<const uint16_t *>(as_src + ks * (kBK / 16));
-        sb = *reinterpret_cast<const uint16_t *>(bs_src + ks * (kBK / 16));
-    };
-    auto store_stage = [&](int buf, const uint4 &qa, const uint4 &qb, uint32_t sa, uint32_t sb) {
-        uint8_t *base = lds + buf * kStageBytes;
-        dequant32(qa, e4m3_value(sa & 0xFFu), e4m3_value(sa >> 8), base + st_off);
-        dequant32(qb, e4m3_value(sb & 0xFFu), e4m3_value(sb >> 8), base + kBM * kRowBytes + st_off);
-    };
-
-    uint4 qa, qb;
-    uint32_t sa, sb;
-    load_stage(0, qa, qb, sa, sb);
-    store_stage(0, qa, qb, sa, sb);
-    __syncthreads();
-
-    for (int ks = 0; ks < nk; ++ks) {
-        const int buf = ks & 1;
-        load_stage(min(ks + 1, nk - 1), qa, qb, sa, sb);
-        const uint8_t *base = lds + buf * kStageBytes;
-#pragma unroll
-        for (int kk = 0; kk < kBK / 16; ++kk) {
-            v8s_t af[2], bfr[2];
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const uint4 ta = *reinterpret_cast<const uint4 *>(base + fa_off + i * 32 * kRowBytes + kk * 32);
-                const uint4 tb = *reinterpret_cast<const uint4 *>(base + fb_off + i * 32 * kRowBytes + kk * 32);
-                af[i] = __builtin_bit_cast(v8s_t, ta);
-                bfr[i] = __builtin_bit_cast(v8s_t, tb);
-            }
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    if (kTile)
-                        part[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], part[i][j], 0, 0, 0);
-                    else
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-                }
-        }
-        if (kTile && ((ks * kBK + kBK) % 128 == 0 || ks == nk - 1)) {
-            // end of a 128-wide K slice: fold its partial sum with the slice's scales
-            const int kt = (ks * kBK) >> 7;
-            const float s = Ats[tm * TK + kt] * Bts[tn * TK + kt];
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int j = 0; j < 2; ++j) {
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) acc[i][j][r] += s * part[i][j][r];
-                    part[i][j] = (v16f_t){};
-                }
-        }
-        store_stage(buf ^ 1, qa, qb, sa, sb);
-        __syncthreads();
-    }
-
-    const float scale = kTile ? alpha : alpha * (Ats[0] * Bts[0]);
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int col = n0 + wn * 64 + j * 32 + fr;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int row = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * fh + (r & 3);
-                if (row < M && col < N) {
-                    const float v = scale * acc[i][j][r];
-                    if (c_bf16)
-                        reinterpret_cast<uint16_t *>(C)[(int64_t)row * ldc + col] = (uint16_t)f32_to_bf16_rne(v);
-                    else
-                        reinterpret_cast<float *>(C)[(int64_t)row * ldc + col] = v;
-                }
-            }
-        }
-}
-
-
 // ------------------------------------------------------------------
-// Global domain: persistent kernel on fp16 matrix cores.
+// Persistent kernel on fp16 matrix cores.
 //
 // An E2M1 value times an E4M3 scale has at most 6 significant bits and lies
 // in [2^-10, 2688], so it is exact in fp16 as well as bf16; fp16 has packed
@@ -198,15 +42,19 @@ __global__ __launch_bounds__(256) void gemm_nv_tile_kernel(const uint8_t *__rest
 // and v_pk_mul_f16 by the block's E4M3 value.  (The scaled convert itself
 // applies only the exponent of its scale operand, which an E4M3 value with a
 // mantissa would lose.)  Products on v_mfma_f32_32x32x16_f16 are then exact
-// and only the fp32 accumulation rounds; S_A * S_B * alpha is applied in the
-// epilogue.
+// and only the fp32 accumulation rounds.
 //
-// Structure as the MX kernel: one 256-thread workgroup per CU walks
-// 256 x 256 tiles (four waves of 128 x 128, B fragment first so the
-// accumulators hold row pieces), a four-slot LDS ring of 128-wide K steps
-// filled by LDS DMA three steps ahead, and the shared epilogue.  Each wave
-// dequantizes the fragments it multiplies, in registers, one 16-wide K slice
-// ahead of the matrix cores.
+// Structure as the MX kernel: one 256-thread workgroup per CU walks output
+// tiles (B fragment first so the accumulators hold row pieces), a four-slot
+// LDS ring of 128-wide K steps filled by LDS DMA three steps ahead, and the
+// shared epilogue.  Each wave dequantizes the fragments it multiplies, in
+// registers, one 16-wide K slice ahead of the matrix cores.
+//
+// Global domain: 256 x 256 tiles, four waves of 128 x 128; S_A * S_B * alpha
+// scales the sum in the epilogue.  Per-tile domain: 256 x 128 tiles, four
+// waves of 128 x 64, so that a second set of accumulators fits: each step's
+// product starts from zero and is added, times S_A(tm, kt) * S_B(tn, kt),
+// into the running sum.
 //
 // K order inside a step.  The matrix cores only need A and B to agree on
 // which K a lane position carries, so slice s (0..7) of a 128-wide step
@@ -217,7 +65,7 @@ __global__ __launch_bounds__(256) void gemm_nv_tile_kernel(const uint8_t *__rest
 // 4h + s/2: byte s/2 of the 32-bit word at row offset 4h of the step's 8
 // scale bytes.
 //
-// LDS image of a stage: codes of 256 rows x 64 bytes per operand with the
+// LDS image of a stage: codes of up to 256 rows x 64 bytes per operand with the
 // 16-byte chunk c of local row r at r * 64 + 16 (c ^ ((r >> 1) & 3)) (the
 // DMA lane mapping applies the swizzle, so 8 lanes reading one chunk of 8
 // consecutive rows hit 8 distinct bank groups), then 8 scale bytes per row.
@@ -232,7 +80,6 @@ constexpr int gAS = 2 * gCodeBytes;                      // A scales, then B sca
 constexpr int gBS = gAS + gScaleBytes;
 constexpr int gStageBytes = 2 * gCodeBytes + 2 * gScaleBytes;  // 36 KiB
 constexpr int gLdsBytes = gStages * gStageBytes;               // 144 KiB
-constexpr int gDmaPerStage = 12;  // per wave: 4 A-code, 4 B-code, 2 A-scale, 2 B-scale instructions
 static_assert(4 * gemm::kEpiWaveBytes <= gStageBytes, "epilogue staging must fit in one ring slot");
 
 // 8 codes (one 32-bit word, element 2b in the low nibble of byte b) times a
@@ -255,12 +102,19 @@ __device__ __forceinline__ half2_t scale2(uint32_t w)
     return __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_pkrtz(f, f));
 }
 
-__global__ __launch_bounds__(256) void gemm_nv_global_kernel(
+template <bool kTile>
+__global__ __launch_bounds__(256) void gemm_nv_fp16_kernel(
     const uint8_t *__restrict__ A, const uint8_t *__restrict__ As, const float *__restrict__ Ats,
     const uint8_t *__restrict__ B, const uint8_t *__restrict__ Bs, const float *__restrict__ Bts, int M, int N, int K,
     float alpha, void *__restrict__ C, int64_t ldc, int c_bf16, int vec_ok, int tiles_m, int tiles_n)
 {
     using namespace gemm;
+    // global domain: 256 x 256 tiles, wave blocks 128 x 128; per-tile domain:
+    // 256 x 128 tiles, wave blocks 128 x 64 (room for a second accumulator set)
+    constexpr int NJ = kTile ? 2 : 4;             // 32-column blocks per wave
+    constexpr int BN = 64 * NJ;                   // workgroup tile columns (two waves across)
+    constexpr int kBRowsPerWave = BN / 4;         // B rows one wave copies per step
+    constexpr int kDma = 4 + NJ + 2 + NJ / 2;     // DMA instructions per wave per step
     __shared__ __attribute__((aligned(1024))) uint8_t lds[gLdsBytes];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -273,7 +127,7 @@ __global__ __launch_bounds__(256) void gemm_nv_global_kernel(
     const int ntiles = tiles_m * tiles_n;
 
     // per-lane DMA sources of the current tile (see the stage image above)
-    uint32_t a_goff[4], b_goff[4], as_goff[2], bs_goff[2];
+    uint32_t a_goff[4], b_goff[NJ], as_goff[2], bs_goff[NJ / 2];
     int m0 = 0, n0 = 0;
     const uint8_t *pa = A, *pb = B, *pas = As, *pbs = Bs;
     int dstep = 0;
@@ -281,18 +135,27 @@ __global__ __launch_bounds__(256) void gemm_nv_global_kernel(
         int tm, tn;
         tile_coords(tile, tiles_m, tiles_n, tm, tn);
         m0 = tm * 256;
-        n0 = tn * 256;
+        n0 = tn * BN;
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             const uint32_t r = 64 * wave + 16 * t + (lane >> 2);  // local row
             const uint32_t c = (uint32_t)(lane & 3) ^ ((r >> 1) & 3u);
             a_goff[t] = (uint32_t)min(m0 + (int)r, M - 1) * KB + c * 16;
+        }
+#pragma unroll
+        for (int t = 0; t < NJ; ++t) {
+            const uint32_t r = kBRowsPerWave * wave + 16 * t + (lane >> 2);
+            const uint32_t c = (uint32_t)(lane & 3) ^ ((r >> 1) & 3u);
             b_goff[t] = (uint32_t)min(n0 + (int)r, N - 1) * KB + c * 16;
         }
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
             const uint32_t r = 64 * wave + 32 * t + (lane >> 1);
             as_goff[t] = (uint32_t)min(m0 + (int)r, M - 1) * KS + (lane & 1) * 4;
+        }
+#pragma unroll
+        for (int t = 0; t < NJ / 2; ++t) {
+            const uint32_t r = kBRowsPerWave * wave + 32 * t + (lane >> 1);
             bs_goff[t] = (uint32_t)min(n0 + (int)r, N - 1) * KS + (lane & 1) * 4;
         }
         pa = A;
@@ -301,17 +164,17 @@ __global__ __launch_bounds__(256) void gemm_nv_global_kernel(
         pbs = Bs;
         dstep = 0;
     };
-    // the d-th of this wave's 12 DMA instructions of a step into the stage at slot_addr
+    // the d-th of this wave's kDma DMA instructions of a step into the stage at slot_addr
     auto dma_piece = [&](uint32_t slot_addr, auto d_tag) {
         constexpr int d = decltype(d_tag)::value;
         if constexpr (d < 4)
             dma16<0>(pa, a_goff[d], slot_addr + (64 * wave + 16 * d) * 64);
-        else if constexpr (d < 8)
-            dma16<gCodeBytes>(pb, b_goff[d - 4], slot_addr + (64 * wave + 16 * (d - 4)) * 64);
-        else if constexpr (d < 10)
-            dma4<gAS>(pas, as_goff[d - 8], slot_addr + (64 * wave + 32 * (d - 8)) * 8);
+        else if constexpr (d < 4 + NJ)
+            dma16<gCodeBytes>(pb, b_goff[d - 4], slot_addr + (kBRowsPerWave * wave + 16 * (d - 4)) * 64);
+        else if constexpr (d < 6 + NJ)
+            dma4<gAS>(pas, as_goff[d - 4 - NJ], slot_addr + (64 * wave + 32 * (d - 4 - NJ)) * 8);
         else
-            dma4<gBS>(pbs, bs_goff[d - 10], slot_addr + (64 * wave + 32 * (d - 10)) * 8);
+            dma4<gBS>(pbs, bs_goff[d - 6 - NJ], slot_addr + (kBRowsPerWave * wave + 32 * (d - 6 - NJ)) * 8);
     };
     auto advance = [&]() {
         const uint32_t more = dstep < nk - 1 ? 1u : 0u;
@@ -325,29 +188,30 @@ __global__ __launch_bounds__(256) void gemm_nv_global_kernel(
 #pragma unroll
         for (int s2 = 0; s2 < gStages - 1; ++s2) {
             const uint32_t slot_addr = lds_base + s2 * gStageBytes;
-            static_for<gDmaPerStage>([&](auto d) { dma_piece(slot_addr, d); });
+            static_for<kDma>([&](auto d) { dma_piece(slot_addr, d); });
             advance();
         }
     };
 
     // fragment sources: local rows of this wave's block rows / columns
     auto code_chunk = [&](const uint8_t *st, int operand, int i, int q) -> uint4 {
-        const uint32_t r = (operand == 0 ? wm * 128 : wn * 128) + 32 * i + fr;
+        const uint32_t r = (operand == 0 ? wm * 128 : wn * (32 * NJ)) + 32 * i + fr;
         const uint32_t c = (uint32_t)(2 * fh + q) ^ ((r >> 1) & 3u);
         return *reinterpret_cast<const uint4 *>(st + operand * gCodeBytes + r * 64 + c * 16);
     };
     auto scale_word = [&](const uint8_t *st, int operand, int i) -> uint32_t {
-        const uint32_t r = (operand == 0 ? wm * 128 : wn * 128) + 32 * i + fr;
+        const uint32_t r = (operand == 0 ? wm * 128 : wn * (32 * NJ)) + 32 * i + fr;
         return *reinterpret_cast<const uint32_t *>(st + gAS + operand * gScaleBytes + r * 8 + fh * 4);
     };
 
-    v16f_t acc[4][4];
-    uint4 rawA[4][2], rawB[4][2];   // code chunks of the step (q = 0, 1)
-    uint32_t swA[4], swB[4];        // scale words of the step
-    uint32_t nswA[4], nswB[4];      // scale words of the next step
-    half2_t sA2[4], sB2[4];         // block scales of the current slice pair
-    half8_t fa[4], fb[4];           // fragments of the slice on the matrix cores
-    half8_t na[4], nb[4];           // fragments of the next slice
+    v16f_t acc[4][NJ];              // the sum (global) or the current K tile's partial sum (per-tile)
+    v16f_t tot[kTile ? 4 : 1][kTile ? NJ : 1];  // per-tile: the sum of the scaled partials
+    uint4 rawA[4][2], rawB[NJ][2];  // code chunks of the step (q = 0, 1)
+    uint32_t swA[4], swB[NJ];       // scale words of the step
+    uint32_t nswA[4], nswB[NJ];     // scale words of the next step
+    half2_t sA2[4], sB2[NJ];        // block scales of the current slice pair
+    half8_t fa[4], fb[NJ];          // fragments of the slice on the matrix cores
+    half8_t na[4], nb[NJ];          // fragments of the next slice
 
     auto word_of = [&](const uint4 &q, int d) -> uint32_t {
         return d == 0 ? q.x : d == 1 ? q.y : d == 2 ? q.z : q.w;
@@ -359,47 +223,66 @@ __global__ __launch_bounds__(256) void gemm_nv_global_kernel(
     for (;;) {
         // stages 0 and 1 of this tile have landed (only stage 2's DMA may be
         // in flight; loads complete in order)
-        wait_and_barrier<gDmaPerStage>();
+        wait_and_barrier<kDma>();
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             rawA[i][0] = code_chunk(lds, 0, i, 0);
             rawA[i][1] = code_chunk(lds, 0, i, 1);
-            rawB[i][0] = code_chunk(lds, 1, i, 0);
-            rawB[i][1] = code_chunk(lds, 1, i, 1);
             swA[i] = scale_word(lds, 0, i);
-            swB[i] = scale_word(lds, 1, i);
+        }
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            rawB[j][0] = code_chunk(lds, 1, j, 0);
+            rawB[j][1] = code_chunk(lds, 1, j, 1);
+            swB[j] = scale_word(lds, 1, j);
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             sA2[i] = scale2<0>(swA[i]);
-            sB2[i] = scale2<0>(swB[i]);
             fa[i] = dequant8(rawA[i][0].x, sA2[i]);
-            fb[i] = dequant8(rawB[i][0].x, sB2[i]);
+        }
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            sB2[j] = scale2<0>(swB[j]);
+            fb[j] = dequant8(rawB[j][0].x, sB2[j]);
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) acc[i][j] = (v16f_t){};
+            for (int j = 0; j < NJ; ++j) {
+                if (kTile)
+                    tot[kTile ? i : 0][kTile ? j : 0] = (v16f_t){};
+                else
+                    acc[i][j] = (v16f_t){};
+            }
+        // per-tile domain: the 128-row tiles of A and B this wave's block lies in
+        const int mt = (m0 >> 7) + wm, nt = n0 >> 7;
 
         uint32_t off_cur = 0, off_nxt = gStageBytes, off_n2 = 2 * gStageBytes, off_dma = 3 * gStageBytes;
         for (int ks = 0; ks < nk; ++ks) {
             // stage ks+1 has landed for every wave, and every wave is done
             // with stage ks-1 (read in steps ks-2 and ks-1): its slot takes
             // the DMA of step ks+3
-            if (ks > 0) wait_and_barrier<gDmaPerStage>();
+            if (ks > 0) wait_and_barrier<kDma>();
             const uint8_t *stn = lds + off_nxt;
             const uint32_t dma_addr = lds_base + off_dma;
             const uint32_t more = dstep < nk - 1 ? 1u : 0u;
-            // 8 slices of 16 MFMAs; slice s+1 is dequantized while slice s runs
+            // per-tile domain: this K tile's factor S_A(mt, ks) * S_B(nt, ks)
+            const float fold = kTile ? Ats[mt * nk + ks] * Bts[nt * nk + ks] : 1.0f;
+            constexpr int kSlots = 4 * NJ;  // MFMAs per slice
+            // 8 slices of kSlots MFMAs; slice s+1 is dequantized while slice s runs
             static_for<8>([&](auto s_tag) {
                 constexpr int s = decltype(s_tag)::value;
                 constexpr int sn = s + 1;  // the slice being prepared (8 = slice 0 of step ks+1)
-                static_for<16>([&](auto t_tag) {
+                static_for<kSlots>([&](auto t_tag) {
                     constexpr int t = decltype(t_tag)::value;
-                    constexpr int i = t >> 2, j = t & 3;
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[j], fa[i], acc[i][j], 0, 0, 0);
-                    // DMA of step ks+3: two instructions per slice in slices 0..5
-                    if constexpr (t < 2 && 2 * s + t < gDmaPerStage)
+                    constexpr int i = t / NJ, j = t % NJ;
+                    if constexpr (kTile && s == 0)  // a fresh partial sum per K tile
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[j], fa[i], (v16f_t){}, 0, 0, 0);
+                    else
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[j], fa[i], acc[i][j], 0, 0, 0);
+                    // DMA of step ks+3: two instructions per slice from slice 0 on
+                    if constexpr (t < 2 && 2 * s + t < kDma)
                         dma_piece(dma_addr, std::integral_constant<int, 2 * s + t>{});
                     // next step's operands: q = 0 chunks and scale words once
                     // the current q = 0 chunks are consumed (slice 3 was
@@ -410,15 +293,15 @@ __global__ __launch_bounds__(256) void gemm_nv_global_kernel(
                         rawA[t][0] = code_chunk(stn, 0, t, 0);
                         nswA[t] = scale_word(stn, 0, t);
                     }
-                    if constexpr (s == 4 && t >= 4 && t < 8) {
+                    if constexpr (s == 4 && t >= 4 && t < 4 + NJ) {
                         rawB[t - 4][0] = code_chunk(stn, 1, t - 4, 0);
                         nswB[t - 4] = scale_word(stn, 1, t - 4);
                     }
-                    if constexpr (s == 0 && t >= 8 && t < 12) {
-                        if (ks > 0) rawA[t - 8][1] = code_chunk(lds + off_cur, 0, t - 8, 1);
+                    if constexpr (s == 0 && t >= kSlots - 4 - NJ && t < kSlots - NJ) {
+                        if (ks > 0) rawA[t - (kSlots - 4 - NJ)][1] = code_chunk(lds + off_cur, 0, t - (kSlots - 4 - NJ), 1);
                     }
-                    if constexpr (s == 0 && t >= 12) {
-                        if (ks > 0) rawB[t - 12][1] = code_chunk(lds + off_cur, 1, t - 12, 1);
+                    if constexpr (s == 0 && t >= kSlots - NJ) {
+                        if (ks > 0) rawB[t - (kSlots - NJ)][1] = code_chunk(lds + off_cur, 1, t - (kSlots - NJ), 1);
                     }
                     // pointer updates after the step's last DMA
                     if constexpr (s == 6 && t < 4) {
@@ -429,34 +312,39 @@ __global__ __launch_bounds__(256) void gemm_nv_global_kernel(
                     }
                     // dequantize slice sn: fragment t/2 of A (even t) or B (odd t) in slots 0..7,
                     // block scales of a new slice pair first (slots 0..7 too)
-                    if constexpr (t < 8) {
+                    if constexpr (t < 8 && ((t & 1) == 0 || (t >> 1) < NJ)) {
                         constexpr int f = t >> 1;
                         constexpr int ss = sn & 7, q = ss >> 2, d = ss & 3, b = ss >> 1;
-                        if constexpr ((ss & 1) == 0) {
-                            if constexpr ((t & 1) == 0)
-                                sA2[f] = scale2<b>(sn == 8 ? nswA[f] : swA[f]);
-                            else
-                                sB2[f] = scale2<b>(sn == 8 ? nswB[f] : swB[f]);
-                        }
-                        if constexpr ((t & 1) == 0)
+                        if constexpr ((t & 1) == 0) {
+                            if constexpr ((ss & 1) == 0) sA2[f] = scale2<b>(sn == 8 ? nswA[f] : swA[f]);
                             na[f] = dequant8(word_of(rawA[f][q], d), sA2[f]);
-                        else
+                        } else {
+                            if constexpr ((ss & 1) == 0) sB2[f] = scale2<b>(sn == 8 ? nswB[f] : swB[f]);
                             nb[f] = dequant8(word_of(rawB[f][q], d), sB2[f]);
+                        }
                     }
                     __builtin_amdgcn_sched_barrier(0);
                 });
 #pragma unroll
-                for (int f = 0; f < 4; ++f) {
-                    fa[f] = na[f];
-                    fb[f] = nb[f];
-                }
+                for (int f = 0; f < 4; ++f) fa[f] = na[f];
+#pragma unroll
+                for (int f = 0; f < NJ; ++f) fb[f] = nb[f];
             });
+            if constexpr (kTile) {
+                // fold this K tile's partial sum with its factor
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r)
+                            tot[kTile ? i : 0][kTile ? j : 0][r] += fold * acc[i][j][r];
+            }
             dstep += (int)more;
 #pragma unroll
-            for (int f = 0; f < 4; ++f) {
-                swA[f] = nswA[f];
-                swB[f] = nswB[f];
-            }
+            for (int f = 0; f < 4; ++f) swA[f] = nswA[f];
+#pragma unroll
+            for (int f = 0; f < NJ; ++f) swB[f] = nswB[f];
             const uint32_t o = off_cur;
             off_cur = off_nxt;
             off_nxt = off_n2;
@@ -473,8 +361,12 @@ __global__ __launch_bounds__(256) void gemm_nv_global_kernel(
         uint8_t *ep = lds + (gStages - 1) * gStageBytes + wave * kEpiWaveBytes;
         int el;
         asm volatile("v_mov_b32 %0, %1" : "=v"(el) : "v"(lane));
-        store_wave_block_any(acc, ep, el, tm0 + wm * 128, tn0 + wn * 128, M, N, alpha * (Ats[0] * Bts[0]), C, ldc,
-                             c_bf16 != 0, vec_ok != 0);
+        if constexpr (kTile)
+            store_wave_block_any<NJ>(tot, ep, el, tm0 + wm * 128, tn0 + wn * (32 * NJ), M, N, alpha, C, ldc,
+                                     c_bf16 != 0, vec_ok != 0);
+        else
+            store_wave_block_any<NJ>(acc, ep, el, tm0 + wm * 128, tn0 + wn * (32 * NJ), M, N,
+                                     alpha * (Ats[0] * Bts[0]), C, ldc, c_bf16 != 0, vec_ok != 0);
         if (next >= ntiles) break;
         tile = next;
     }
@@ -496,22 +388,21 @@ int launch_gemm_nv(const GemmArgs &g, hipStream_t st)
     auto *as = reinterpret_cast<const uint8_t *>(g.a_scales);
     auto *b = reinterpret_cast<const uint8_t *>(g.b_codes);
     auto *bs = reinterpret_cast<const uint8_t *>(g.b_scales);
-    if (g.nv_domain == 1) {
-        const int tiles_m = (M + kBM - 1) / kBM, tiles_n = (N + kBN - 1) / kBN;
-        hipLaunchKernelGGL(gemm_nv_tile_kernel<true>, dim3(tiles_m * tiles_n), dim3(256), 0, st, a, as, g.a_ts, b, bs,
-                           g.b_ts, M, N, K, g.alpha, g.c, g.ldc, (int)g.c_bf16, tiles_n);
-    } else {
-        const int esize = g.c_bf16 ? 2 : 4;
-        const int vec_ok = ((uintptr_t)g.c % 16 == 0) && (g.ldc % (16 / esize) == 0) && g.ldc <= (int64_t(1) << 26);
-        const int tiles_m = (M + 255) / 256, tiles_n = (N + 255) / 256;
-        int dev = 0, cus = 0;
-        if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-            return 1;
-        const int grid = min(tiles_m * tiles_n, cus);
-        hipLaunchKernelGGL(gemm_nv_global_kernel, dim3(grid), dim3(256), 0, st, a, as, g.a_ts, b, bs, g.b_ts, M, N, K,
-                           g.alpha, g.c, g.ldc, (int)g.c_bf16, vec_ok, tiles_m, tiles_n);
-    }
+    const int esize = g.c_bf16 ? 2 : 4;
+    const int vec_ok = ((uintptr_t)g.c % 16 == 0) && (g.ldc % (16 / esize) == 0) && g.ldc <= (int64_t(1) << 26);
+    const bool tile = g.nv_domain == 1;
+    const int tiles_m = (M + 255) / 256, tiles_n = tile ? (N + 127) / 128 : (N + 255) / 256;
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        return 1;
+    const int grid = min(tiles_m * tiles_n, cus);
+    if (tile)
+        hipLaunchKernelGGL(gemm_nv_fp16_kernel<true>, dim3(grid), dim3(256), 0, st, a, as, g.a_ts, b, bs, g.b_ts, M, N,
+                           K, g.alpha, g.c, g.ldc, (int)g.c_bf16, vec_ok, tiles_m, tiles_n);
+    else
+        hipLaunchKernelGGL(gemm_nv_fp16_kernel<false>, dim3(grid), dim3(256), 0, st, a, as, g.a_ts, b, bs, g.b_ts, M, N,
+                           K, g.alpha, g.c, g.ldc, (int)g.c_bf16, vec_ok, tiles_m, tiles_n);
     return hipGetLastError() == hipSuccess ? 0 : 1;
 }
 
