@@ -369,7 +369,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "e2m1 x e2m1 -> f32 accumulate" if "nvfp4" not in args.workload else "bf16(e2m1*e4m3) -> f32",
+        "dtype": "e2m1 x e2m1 -> f32 accumulate" if "nvfp4" not in args.workload else "fp16(e2m1*e4m3) -> f32",
         "data": "synthetic",
         "config": cfg,
         "roofline": roofline,

@@ -181,9 +181,10 @@ FP4Q_API fp4q_status fp4_gemm_mx(const void *a_codes, const void *a_scales, cons
                         int64_t M, int64_t N, int64_t K, float alpha, int layout, void *c, int c_type,
                         int64_t ldc, void *stream);
 
-/* NVFP4 GEMM: E2M1 x E4M3 is dequantized exactly to bf16 and multiplied on
- * bf16 MFMA; the FP32 tensor scales multiply the fp32 partial sums (once in
- * the epilogue for the global domain, per 128-wide K slice for tile128).
+/* NVFP4 GEMM: E2M1 x E4M3 is dequantized exactly to fp16 and multiplied on
+ * fp16 MFMA with fp32 accumulation; the FP32 tensor scales multiply the fp32
+ * partial sums (once in the epilogue for the global domain, per 128-wide K
+ * slice for tile128).
  * a_tensor_scale / b_tensor_scale as written by fp4_quantize_nv with the same
  * domain.  Requires K % 128 == 0.  FP4Q_EUNSUPPORTED: layout
  * FP4Q_LAYOUT_TILED. */
