@@ -9,10 +9,14 @@ X bf16 8192x4096, W bf16 6144x4096, C = X W^T bf16 8192x6144.
 
 Prints one JSON line.  `value` is quantize+GEMM TFLOP/s = 2MNK / (time per
 step), with inputs resident in HBM (several input copies are rotated so the
-producers read from HBM, not from the 256 MB Infinity Cache).  `roofline`
-describes the dominant kernel (average launch duration from HIP events on the
-launch stream inside the timed region); `kernels` lists every kernel of the
-step; `cpu_baseline` times the CPU oracle on one full step on the host cores.
+producers read from HBM, not from the 256 MB Infinity Cache).  The timed region is
+K steps launched back to back, after the warmup steps and the per-kernel
+passes.  `roofline` describes the dominant kernel: its average launch
+duration from HIP events on the launch stream, in a pass of K steps with an
+event pair around that kernel's launches only (an event marker between two
+kernels costs a few microseconds of GPU time, so the step timing has none);
+`kernels` lists every kernel of the step; `cpu_baseline` times the CPU oracle
+on one full step on the host cores.
 """
 from __future__ import annotations
 
@@ -26,6 +30,7 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
+WARM_S = 0.5                 # minimum warmup time (seconds)
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 FP4_PEAK_TFLOPS = 10100.0    # dense MFMA, fp4/fp6
 BF16_PEAK_TFLOPS = 2500.0    # dense MFMA, bf16
@@ -302,35 +307,38 @@ def main():
     cfg, ops, step_flops = build_workload(args.workload, dev, args.copies, args.layout)
     stream = torch.cuda.current_stream()
 
-    for s in range(args.warmup):
+    # W warmup steps, then more until the GPU has run for WARM_S seconds: the
+    # first ~0.1 s of back-to-back work runs at lower clocks.
+    t0 = time.perf_counter()
+    s = 0
+    while s < args.warmup or time.perf_counter() - t0 < WARM_S:
         for op in ops:
             op[2](s)
+        s += 1
+        if s % 8 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
 
     nops = len(ops)
-    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nops)]
-          for _ in range(args.steps)]
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    t_start.record(stream)
-    for s in range(args.steps):
-        for i, op in enumerate(ops):
-            ev[s][i][0].record(stream)
-            op[2](s)
-            ev[s][i][1].record(stream)
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    gpu_ms = t_start.elapsed_time(t_end)
-    ms_per_step = gpu_ms / args.steps
+    # Per-kernel durations, measured in the step: for each op, K steps with a
+    # HIP event pair around that op's launch only (every event marker between
+    # two kernels costs the GPU a few microseconds, so one op is bracketed per
+    # pass and the step timing below has none).
+    op_ms = []
+    for i in range(nops):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        for s in range(args.steps):
+            for j, op in enumerate(ops):
+                if j == i:
+                    ev[s][0].record(stream)
+                op[2](s)
+                if j == i:
+                    ev[s][1].record(stream)
+        torch.cuda.synchronize()
+        op_ms.append([e0.elapsed_time(e1) for e0, e1 in ev])
 
-    # Per-launch events carry a few microseconds of their own, which matters
-    # for the short producers: each op is also timed as a batch of
-    # back-to-back launches (outside the timed region) and reported as
-    # avg_us_batched; `achieved` uses the in-step events for ops longer than
-    # 100 us and the batched figure otherwise.
+    # Each op also as a batch of back-to-back launches (no markers at all),
+    # for the short producers where even two markers per step matter.
     batch = 20
     batched_ms = []
     for i, op in enumerate(ops):
@@ -342,9 +350,25 @@ def main():
         torch.cuda.synchronize()
         batched_ms.append(b0.elapsed_time(b1) / batch)
 
+    # Timed region: K steps launched back to back.
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for s in range(args.steps):
+        for op in ops:
+            op[2](s)
+    t_end.record(stream)
+    enqueue = time.perf_counter() - wall0
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    gpu_ms = t_start.elapsed_time(t_end)
+    ms_per_step = gpu_ms / args.steps
+
     kernels = []
     for i, (label, kname, _, amount, unit, peak, bound) in enumerate(ops):
-        durs = [ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(args.steps)]
+        durs = op_ms[i]
         avg_ms = sum(durs) / len(durs)
         use_ms = avg_ms if avg_ms > 0.1 else batched_ms[i]
         achieved = amount / (use_ms * 1e-3) / (1e9 if unit == "GB/s" else 1e12)
@@ -375,6 +399,7 @@ def main():
         "roofline": roofline,
         "kernels": kernels,
         "wall_s_timed": round(wall, 4),
+        "host_enqueue_us_per_step": round(enqueue / args.steps * 1e6, 1),
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.workload)
