@@ -84,7 +84,11 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(const uint8_t *__restrict_
     // elements are one 1 KiB block in matrix-core lane order (lane l's 16
     // bytes = row l mod 32, K half l / 32), blocks ordered (row group g, K
     // half kk) -> 2 g + kk.  Wave w copies blocks 4w .. 4w+3 of A and of B
-    // and the scale words of rows 64 w + lane.  In the tiled layout a block is
+    // and 64 scale words of each operand.  The scale words are stored so that
+    // the four a consuming lane needs (rows 32 i + l mod 32 of its 128-row
+    // block, i = 0..3) are one 16-byte read: word 4 f + i of 128-row block c
+    // holds row 128 c + 32 i + f, so lane l of wave w's copy takes row
+    // 128 (w / 2) + 32 (l mod 4) + 16 (w mod 2) + l / 4.  In the tiled layout a block is
     // 1 KiB of contiguous global memory; in the linear layout lane l of block
     // b reads row 32 (b / 2) + l mod 32, bytes 32 (b mod 2) + 16 (l / 32) of
     // the step.  Rows past the operand re-read its last row (linear) or row
@@ -116,14 +120,15 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(const uint8_t *__restrict_
                 b_goff[i] = (uint32_t)min(n0 + r, N - 1) * KB + col;
             }
         }
+        const int srow = 128 * (wave >> 1) + 32 * (lane & 3) + 16 * (wave & 1) + (lane >> 2);
         if (kTiled) {
-            as_goff = min((uint32_t)(m0 + wave * 64 + lane), Mp - 1) * 4;
-            bs_goff = min((uint32_t)(n0 + wave * 64 + lane), Np - 1) * 4;
+            as_goff = min((uint32_t)(m0 + srow), Mp - 1) * 4;
+            bs_goff = min((uint32_t)(n0 + srow), Np - 1) * 4;
             as_step = Mp * 4;
             bs_step = Np * 4;
         } else {
-            as_goff = (uint32_t)min(m0 + wave * 64 + lane, M - 1) * KS;
-            bs_goff = (uint32_t)min(n0 + wave * 64 + lane, N - 1) * KS;
+            as_goff = (uint32_t)min(m0 + srow, M - 1) * KS;
+            bs_goff = (uint32_t)min(n0 + srow, N - 1) * KS;
             as_step = bs_step = 4;
         }
         pa = A;
@@ -194,9 +199,9 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(const uint8_t *__restrict_
     // blocks 0..3; lanes 32..63 feed the matrix cores K blocks 1 and 3, so
     // their word is shifted down one byte and both halves select byte 0
     // (K half 0) or byte 2 (K half 1) with the instruction's byte select.
-    auto scale_word = [&](const uint8_t *st, int operand, int i) -> uint32_t {
-        const int row = (operand == 0 ? wm * 128 : wn * 128) + i * 32 + fr;
-        return *reinterpret_cast<const uint32_t *>(st + kScaleOff + operand * kBM * 4 + row * 4);
+    auto scale_words = [&](const uint8_t *st, int operand) -> uint4 {
+        const int c = operand == 0 ? wm : wn;
+        return *reinterpret_cast<const uint4 *>(st + kScaleOff + operand * kBM * 4 + (c * 128 + fr * 4) * 4);
     };
 
     v16f_t acc[4][4];
@@ -216,8 +221,11 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(const uint8_t *__restrict_
         for (int i = 0; i < 4; ++i) {
             fa0[i] = frag(lds, 0, i, 0);
             fb0[i] = frag(lds, 1, i, 0);
-            sa[i] = scale_word(lds, 0, i) >> (8 * fh);
-            sb[i] = scale_word(lds, 1, i) >> (8 * fh);
+        }
+        {
+            const uint4 wa = scale_words(lds, 0), wb = scale_words(lds, 1);
+            sa[0] = wa.x >> (8 * fh); sa[1] = wa.y >> (8 * fh); sa[2] = wa.z >> (8 * fh); sa[3] = wa.w >> (8 * fh);
+            sb[0] = wb.x >> (8 * fh); sb[1] = wb.y >> (8 * fh); sb[2] = wb.z >> (8 * fh); sb[3] = wb.w >> (8 * fh);
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -273,13 +281,18 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(const uint8_t *__restrict_
                 // two per slot so they land well before the phase ends
                 if constexpr (t < 8) {
                     constexpr int q = t >> 1;
-                    if constexpr ((t & 1) == 0) {
+                    if constexpr ((t & 1) == 0)
                         fb0[q] = frag(stn, 1, q, 0);
-                        nsb[q] = scale_word(stn, 1, q);
-                    } else {
+                    else
                         fa0[q] = frag(stn, 0, q, 0);
-                        nsa[q] = scale_word(stn, 0, q);
-                    }
+                }
+                if constexpr (t == 0) {
+                    const uint4 w = scale_words(stn, 1);
+                    nsb[0] = w.x; nsb[1] = w.y; nsb[2] = w.z; nsb[3] = w.w;
+                }
+                if constexpr (t == 1) {
+                    const uint4 w = scale_words(stn, 0);
+                    nsa[0] = w.x; nsa[1] = w.y; nsa[2] = w.z; nsa[3] = w.w;
                 }
                 // lanes 32..63 take the odd K blocks: shift their scale
                 // words down one byte, well after the reads were issued
