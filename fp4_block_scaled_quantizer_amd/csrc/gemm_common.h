@@ -40,7 +40,8 @@ __device__ __forceinline__ void tile_coords(int bid, int tiles_m, int tiles_n, i
 // Global -> LDS copies that bypass VGPRs (gfx950 LDS DMA): lane i reads
 // base + voff_i (base a 64-bit scalar address, voff a 32-bit per-lane byte
 // offset) and writes its 16 (or 4) bytes to LDS address m0 + 16 i (4 i),
-// m0 = lds_slot + kLdsOff (the add clobbers SCC, declared as such).
+// m0 = lds_slot + kLdsOff (the add clobbers SCC, declared as such; an LDS
+// DMA needs one wait state after an SALU write of M0, hence the s_nop).
 // They are issued from inline assembly so that the only waits on them are
 // the explicit vmcnt waits of the K loop: every vector-memory instruction of
 // the loop is one of these, so the count of DMA instructions issued after a
@@ -49,14 +50,14 @@ __device__ __forceinline__ void tile_coords(int bid, int tiles_m, int tiles_n, i
 template <uint32_t kLdsOff>
 __device__ __forceinline__ void dma16(const void *base, uint32_t voff, uint32_t lds_slot)
 {
-    asm volatile("s_add_u32 m0, %2, %3\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "s"(lds_slot),
+    asm volatile("s_add_u32 m0, %2, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "s"(lds_slot),
                  "n"(kLdsOff)
                  : "memory", "m0", "scc");
 }
 template <uint32_t kLdsOff>
 __device__ __forceinline__ void dma4(const void *base, uint32_t voff, uint32_t lds_slot)
 {
-    asm volatile("s_add_u32 m0, %2, %3\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(base), "s"(lds_slot),
+    asm volatile("s_add_u32 m0, %2, %3\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(base), "s"(lds_slot),
                  "n"(kLdsOff)
                  : "memory", "m0", "scc");
 }

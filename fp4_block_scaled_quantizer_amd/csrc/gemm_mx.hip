@@ -279,20 +279,19 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(const uint8_t *__restrict_
                     dma_piece(dma_addr, std::integral_constant<int, kDmaA + t>{});
                 // next step's operands, in the order phase A consumes them,
                 // two per slot so they land well before the phase ends
+                // the scale words first: LDS reads return in order, so the
+                // shifts below then wait on these two reads only
+                if constexpr (t == 0) {
+                    const uint4 wb = scale_words(stn, 1), wa = scale_words(stn, 0);
+                    nsb[0] = wb.x; nsb[1] = wb.y; nsb[2] = wb.z; nsb[3] = wb.w;
+                    nsa[0] = wa.x; nsa[1] = wa.y; nsa[2] = wa.z; nsa[3] = wa.w;
+                }
                 if constexpr (t < 8) {
                     constexpr int q = t >> 1;
                     if constexpr ((t & 1) == 0)
                         fb0[q] = frag(stn, 1, q, 0);
                     else
                         fa0[q] = frag(stn, 0, q, 0);
-                }
-                if constexpr (t == 0) {
-                    const uint4 w = scale_words(stn, 1);
-                    nsb[0] = w.x; nsb[1] = w.y; nsb[2] = w.z; nsb[3] = w.w;
-                }
-                if constexpr (t == 1) {
-                    const uint4 w = scale_words(stn, 0);
-                    nsa[0] = w.x; nsa[1] = w.y; nsa[2] = w.z; nsa[3] = w.w;
                 }
                 // lanes 32..63 take the odd K blocks: shift their scale
                 // words down one byte, well after the reads were issued
