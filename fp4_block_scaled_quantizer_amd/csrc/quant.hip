@@ -344,35 +344,42 @@ __global__ __launch_bounds__(kThreads) void quant_mx_cols_kernel(const uint16_t 
 }
 
 // ------------------------------------------------------------------
-// MXFP4 along rows into the tiled layout.  A workgroup owns 32 rows x 512 K
-// (up to 4 K steps): wavefront w reads row 4 i + w of the group, i < 8, with
-// contiguous 1 KiB loads (lane = 8-element chunk), quantizes exactly like the
-// linear kernel, assembles the group's eight 1 KiB lane-order code blocks and
-// its step-major scale words in LDS, then writes both out contiguously.
+// MXFP4 along rows into the tiled layout.  A workgroup owns 32 rows x kWin K
+// (kWin = 512 or 256: up to kWin / 128 K steps).  Each load instruction of a
+// wavefront covers 512 contiguous elements: one row of a 512-wide window, or
+// two rows of a 256-wide one (lane = 8-element chunk); the rows are
+// quantized exactly like the linear kernel, the group's 1 KiB lane-order
+// code blocks and its step-major scale words are assembled in LDS, then
+// written out contiguously.
 // ------------------------------------------------------------------
-template <bool kSR, bool kHad>
+template <bool kSR, bool kHad, int kWin>
 __global__ __launch_bounds__(kThreads) void quant_mx_rows_tiled_kernel(
     const uint16_t *__restrict__ x, uint32_t R, uint32_t K, uint32_t ld, uint32_t Rp, uint8_t *__restrict__ codes,
     uint8_t *__restrict__ scales, uint32_t seed_lo, uint32_t seed_hi, uint32_t stream_id, uint32_t sign_mask)
 {
-    __shared__ __attribute__((aligned(16))) uint8_t tile[8192 + 512];
+    static_assert(kWin == 512 || kWin == 256 || kWin == 128, "window of 4, 2 or 1 K steps");
+    constexpr int kRowsPerLoad = 512 / kWin;       // rows one load instruction covers
+    constexpr int kLoads = 8 / kRowsPerLoad;       // load instructions per thread
+    constexpr int kCodeTile = kWin * 16;           // 32 rows x kWin codes, bytes
+    __shared__ __attribute__((aligned(16))) uint8_t tile[kCodeTile + kWin];
     const uint32_t g = blockIdx.y;         // 32-row group
-    const uint32_t k0 = blockIdx.x * 512;  // first K of this workgroup
-    const uint32_t nsteps = min(4u, (K - k0) >> 7);
+    const uint32_t k0 = blockIdx.x * kWin; // first K of this workgroup
+    const uint32_t nsteps = min((uint32_t)(kWin / 128), (K - k0) >> 7);
     const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
     const int quad_lane = lane & 3;
-    const uint32_t c8 = lane;  // 8-element chunk within the 512-wide window
+    const uint32_t c8 = lane % (kWin / 8);  // 8-element chunk within the window
+    const uint32_t sub = lane / (kWin / 8); // which row of the load instruction
     const bool kvalid = (c8 >> 4) < nsteps;
-    uint4 q[8];
+    uint4 q[kLoads];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const uint32_t row = g * 32 + i * 4 + wave;
+    for (int i = 0; i < kLoads; ++i) {
+        const uint32_t row = g * 32 + (i * 4 + wave) * kRowsPerLoad + sub;
         q[i] = make_uint4(0u, 0u, 0u, 0u);
         if (row < R && kvalid) q[i] = load_nt16(x + (size_t)row * ld + k0 + 8 * c8);
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const uint32_t rl = i * 4 + wave, row = g * 32 + rl;
+    for (int i = 0; i < kLoads; ++i) {
+        const uint32_t rl = (i * 4 + wave) * kRowsPerLoad + sub, row = g * 32 + rl;
         uint32_t packed = 0, sbyte;
         if (!kHad && !kSR) {
             uint32_t amax = amax8_bf16(q[i]);
@@ -404,8 +411,8 @@ __global__ __launch_bounds__(kThreads) void quant_mx_rows_tiled_kernel(
         *reinterpret_cast<uint32_t *>(tile + (c8 >> 3) * 1024 + (rl + 32 * ((c8 >> 2) & 1)) * 16 + (c8 & 3) * 4) =
             packed;
         if (quad_lane == 0) {
-            const uint32_t jb = c8 >> 2;  // MX block within the window, 0..15
-            tile[8192 + (jb >> 2) * 128 + rl * 4 + (jb & 3)] = (uint8_t)sbyte;
+            const uint32_t jb = c8 >> 2;  // MX block within the window
+            tile[kCodeTile + (jb >> 2) * 128 + rl * 4 + (jb & 3)] = (uint8_t)sbyte;
         }
     }
     __syncthreads();
@@ -415,7 +422,7 @@ __global__ __launch_bounds__(kThreads) void quant_mx_rows_tiled_kernel(
     if ((uint32_t)t < 8 * nsteps) {
         const uint32_t s = t >> 3, part = t & 7;
         *reinterpret_cast<uint4 *>(scales + ((size_t)((k0 >> 7) + s) * Rp + 32 * g) * 4 + part * 16) =
-            *reinterpret_cast<const uint4 *>(tile + 8192 + s * 128 + part * 16);
+            *reinterpret_cast<const uint4 *>(tile + kCodeTile + s * 128 + part * 16);
     }
 }
 
@@ -590,11 +597,12 @@ int launch_quant_mx(const QuantArgs &a, hipStream_t st)
         const uint32_t R = (uint32_t)a.rows, K = (uint32_t)a.cols;
         if (R == 0 || K == 0) return 0;
         const uint32_t Rp = (R + 31) / 32 * 32;
-        dim3 grid((K + 511) / 512, Rp / 32);
+        constexpr int kWin = 256;  // two K steps per workgroup: 4096 workgroups for an 8192 x 4096 input
+        dim3 grid((K + kWin - 1) / kWin, Rp / 32);
         auto *codes = reinterpret_cast<uint8_t *>(a.codes);
-#define FP4Q_LAUNCH_ROWS_T(SR, HAD)                                                                            \
-    hipLaunchKernelGGL((quant_mx_rows_tiled_kernel<SR, HAD>), grid, dim3(kThreads), 0, st, x, R, K, (uint32_t)a.ld, \
-                       Rp, codes, scales, seed_lo, seed_hi, a.stream_id, a.sign_mask)
+#define FP4Q_LAUNCH_ROWS_T(SR, HAD)                                                                                  \
+    hipLaunchKernelGGL((quant_mx_rows_tiled_kernel<SR, HAD, kWin>), grid, dim3(kThreads), 0, st, x, R, K,            \
+                       (uint32_t)a.ld, Rp, codes, scales, seed_lo, seed_hi, a.stream_id, a.sign_mask)
         if (a.sr) { if (a.hadamard) FP4Q_LAUNCH_ROWS_T(true, true); else FP4Q_LAUNCH_ROWS_T(true, false); }
         else { if (a.hadamard) FP4Q_LAUNCH_ROWS_T(false, true); else FP4Q_LAUNCH_ROWS_T(false, false); }
 #undef FP4Q_LAUNCH_ROWS_T
