@@ -37,6 +37,7 @@ BF16_PEAK_TFLOPS = 2500.0    # dense MFMA, bf16
 
 # algorithmic bytes per element (payload + block scales + tensor scales, logical rows)
 MX_BYTES_PER_ELEM = 2 + 0.5 + 1 / 32
+MX_DUAL_BYTES_PER_ELEM = 2 + 2 * (0.5 + 1 / 32)  # one read, two operands written
 NV_TILE_BYTES_PER_ELEM = 2 + 0.5 + 1 / 16 + 4 / (128 * 128)
 NV_GLOBAL_BYTES_PER_ELEM = 2 + 2 + 0.5 + 1 / 16   # includes the amax pre-pass read
 
@@ -47,7 +48,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="qkv",
-                    choices=["qkv", "mlp", "backward", "nvfp4_global", "nvfp4_tile", "copy"],
+                    choices=["qkv", "mlp", "backward", "backward_dual", "dual_x", "nvfp4_global", "nvfp4_tile",
+                             "copy"],
                     help="copy = a plain 1 GiB device copy: the HBM reference for counter scaling")
     ap.add_argument("--copies", type=int, default=4, help="input copies rotated across steps (cold producers)")
     ap.add_argument("--layout", default="tiled", choices=["tiled", "linear"],
@@ -147,7 +149,23 @@ def build_workload(name, dev, copies, layout_name="tiled"):
         cfg = {"workload": "Llama-3-8B MLP forward (gate/up + down), MXFP4 RNE",
                "gemms_mnk": [[M, N1, K1], [M, N2, K2]], "out": "bf16", "layout": layout_name, "input_copies": copies}
         return cfg, ops, 2.0 * M * N1 * K1 + 2.0 * M * N2 * K2
-    if name == "backward":
+    if name == "dual_x":
+        # the forward activation's two operands from one read: X along rows (RNE,
+        # for fprop) and the Hadamard X^T along tokens (RNE, kept for wgrad)
+        X = gen("qkv", "X", copies)
+        T, I = X[0].shape
+        mask = synth.sign_mask(synth.HADAMARD_MASK_SEED)
+        xr, xc = mx_bufs(T, I), mx_bufs(I, T)
+        ops = [("dual-quantize X: rows + Hadamard X^T (RNE)", "quant_mx_cols_kernel",
+                lambda s: B.fp4_quantize_mx_dual(X[s % copies], hadamard_cols=True, sign_mask=mask, layout=L,
+                                                 codes_rows=xr[0], scales_rows=xr[1], codes_cols=xc[0],
+                                                 scales_cols=xc[1]),
+                T * I * MX_DUAL_BYTES_PER_ELEM, "GB/s", HBM_PEAK_GBS, "hbm")]
+        cfg = {"workload": "Llama-3-8B activation X 8192x4096, MXFP4 rows + Hadamard columns from one read",
+               "shape": [T, I], "layout": layout_name, "input_copies": copies}
+        return cfg, ops, 0.0
+    if name in ("backward", "backward_dual"):
+        dual = name == "backward_dual"
         dY = gen("backward", "dY", copies)
         W = gen("backward", "W", copies)
         X = gen("backward", "X", copies)
@@ -193,7 +211,18 @@ def build_workload(name, dev, copies, layout_name="tiled"):
              lambda s: B.fp4_gemm_mx(*bufs["dy_c"], *bufs["x_c"], alpha=1.0 / 32, c=dW, layout=L, m=O, n=I),
              2.0 * O * I * T, "TFLOP/s", FP4_PEAK_TFLOPS, "mfma"),
         ]
-        cfg = {"workload": "Llama-3-8B o_proj backward, MXFP4: SR on dY, fixed-sign Hadamard-32 on wgrad",
+        if dual:
+            # one read of dY for both of its operands (dgrad rows, wgrad Hadamard columns)
+            ops = [("dual-quantize dY: rows (SR) + Hadamard dY^T (SR)", "quant_mx_cols_kernel",
+                    lambda s: B.fp4_quantize_mx_dual(dY[s % copies], round_rows=B.SR, stream_id_rows=0,
+                                                     hadamard_cols=True, sign_mask=mask, round_cols=B.SR,
+                                                     stream_id_cols=1, seed=seed, layout=L,
+                                                     codes_rows=bufs["dy_r"][0], scales_rows=bufs["dy_r"][1],
+                                                     codes_cols=bufs["dy_c"][0], scales_cols=bufs["dy_c"][1]),
+                    T * O * MX_DUAL_BYTES_PER_ELEM, "GB/s", HBM_PEAK_GBS, "hbm")] + \
+                [op for op in ops if not op[0].startswith(("quantize dY", "Hadamard-quantize dY"))]
+        cfg = {"workload": "Llama-3-8B o_proj backward, MXFP4: SR on dY, fixed-sign Hadamard-32 on wgrad" +
+                           (", dY's two operands from one read (dual producer)" if dual else ""),
                "dgrad_mnk": [T, I, O], "wgrad_mnk": [O, I, T], "layout": layout_name, "input_copies": copies}
         return cfg, ops, 2.0 * T * I * O * 2
     # NVFP4
@@ -381,11 +410,13 @@ def main():
     roofline = {"bound": dk["bound"], "achieved": dk["achieved"], "peak": dk["peak"], "unit": dk["unit"],
                 "frac": dk["frac"], "traffic": read_traffic(dk["kernel"], args.workload), "kernel": dk["kernel"],
                 "op": dk["op"], "avg_us": dk["avg_us"]}
+    # workloads without a GEMM (a producer alone, the copy calibration) report
+    # the dominant kernel's rate
     value = step_flops / (ms_per_step * 1e-3) / 1e12 if step_flops else dk["achieved"]
     out = {
-        "metric": "quantize+FP4 GEMM TFLOP/s (Llama-3-8B shapes)",
+        "metric": "quantize+FP4 GEMM TFLOP/s (Llama-3-8B shapes)" if step_flops else f"{dk['op']} {dk['unit']}",
         "value": round(value, 1),
-        "unit": "TFLOP/s",
+        "unit": "TFLOP/s" if step_flops else dk["unit"],
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -393,7 +424,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "e2m1 x e2m1 -> f32 accumulate" if "nvfp4" not in args.workload else "fp16(e2m1*e4m3) -> f32",
+        "dtype": ("fp16(e2m1*e4m3) -> f32" if "nvfp4" in args.workload else
+                  "e2m1 x e2m1 -> f32 accumulate" if step_flops else
+                  "bf16" if args.workload == "copy" else "bf16 -> e2m1 + e8m0"),
         "data": "synthetic",
         "config": cfg,
         "roofline": roofline,

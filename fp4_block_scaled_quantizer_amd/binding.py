@@ -55,13 +55,16 @@ def lib() -> ctypes.CDLL:
                                    ctypes.c_int, ctypes.c_float)
     L.fp4_quantize_mx.argtypes = [vp, i64, i64, i64, i32, i32, u64, u32, vp, vp, i32, vp]
     L.fp4_hadamard32_quantize.argtypes = [vp, i64, i64, i64, i32, u32, i32, u64, u32, vp, vp, i32, vp]
+    L.fp4_quantize_mx_dual.argtypes = [vp, i64, i64, i64, i32, u32, vp, vp, i32, u32, i32, u32, vp, vp, u64, i32,
+                                       vp]
     L.fp4q_nv_workspace_bytes.argtypes = [i64, i64, i32, i32]
     L.fp4q_nv_workspace_bytes.restype = ctypes.c_size_t
     L.fp4_quantize_nv.argtypes = [vp, i64, i64, i64, i32, i32, u64, u32, i32, vp, vp, vp, vp, ctypes.c_size_t,
                                   i32, vp]
     L.fp4_gemm_mx.argtypes = [vp, vp, vp, vp, i64, i64, i64, f32, i32, vp, i32, i64, vp]
     L.fp4_gemm_nv.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, i64, i64, f32, i32, vp, i32, i64, vp]
-    for fn in ("fp4_quantize_mx", "fp4_hadamard32_quantize", "fp4_quantize_nv", "fp4_gemm_mx", "fp4_gemm_nv"):
+    for fn in ("fp4_quantize_mx", "fp4_hadamard32_quantize", "fp4_quantize_mx_dual", "fp4_quantize_nv",
+               "fp4_gemm_mx", "fp4_gemm_nv"):
         getattr(L, fn).restype = i32
     L.fp4q_status_str.argtypes = [i32]
     L.fp4q_status_str.restype = ctypes.c_char_p
@@ -133,6 +136,25 @@ def fp4_quantize_mx(x: torch.Tensor, *, cols: Optional[int] = None, axis: int = 
     _check("fp4_quantize_mx", lib().fp4_quantize_mx(x.data_ptr(), rows, cols, ld, axis, round, seed, stream_id,
                                                     codes.data_ptr(), scales.data_ptr(), layout, _stream(stream)))
     return codes, scales
+
+
+def fp4_quantize_mx_dual(x: torch.Tensor, *, round_rows: int = RNE, stream_id_rows: int = 0,
+                         hadamard_cols: bool = True, sign_mask: int = 0, round_cols: int = RNE,
+                         stream_id_cols: int = 0, seed: int = 0, layout: int = LAYOUT_LINEAR,
+                         codes_rows: Optional[torch.Tensor] = None, scales_rows: Optional[torch.Tensor] = None,
+                         codes_cols: Optional[torch.Tensor] = None, scales_cols: Optional[torch.Tensor] = None,
+                         stream=None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor, torch.Tensor]:
+    """x along rows and x^T along columns (optionally Hadamard) from one read
+    of x: (codes_rows, scales_rows, codes_cols, scales_cols)."""
+    rows, cols, ld = _input(x, None)
+    codes_rows, scales_rows = _mx_outputs(rows, cols, layout, codes_rows, scales_rows, x.device)
+    codes_cols, scales_cols = _mx_outputs(cols, rows, layout, codes_cols, scales_cols, x.device)
+    _check("fp4_quantize_mx_dual",
+           lib().fp4_quantize_mx_dual(x.data_ptr(), rows, cols, ld, round_rows, stream_id_rows, codes_rows.data_ptr(),
+                                      scales_rows.data_ptr(), int(bool(hadamard_cols)), sign_mask & 0xFFFFFFFF,
+                                      round_cols, stream_id_cols, codes_cols.data_ptr(), scales_cols.data_ptr(),
+                                      seed, layout, _stream(stream)))
+    return codes_rows, scales_rows, codes_cols, scales_cols
 
 
 def fp4_hadamard32_quantize(x: torch.Tensor, sign_mask: int, *, cols: Optional[int] = None, axis: int = ALONG_COLS,

@@ -134,6 +134,48 @@ fp4q_status fp4_hadamard32_quantize(const void *x, int64_t rows, int64_t cols, i
                            stream);
 }
 
+fp4q_status fp4_quantize_mx_dual(const void *x, int64_t rows, int64_t cols, int64_t ld_x, int round_rows,
+                                 uint32_t stream_id_rows, void *codes_rows, void *scales_rows, int hadamard_cols,
+                                 uint32_t sign_mask, int round_cols, uint32_t stream_id_cols, void *codes_cols,
+                                 void *scales_cols, uint64_t seed, int layout, void *stream)
+{
+    if (hadamard_cols != 0 && hadamard_cols != 1) return FP4Q_EINVAL;
+    bool empty = false;
+    fp4q_status st = check_mx_producer(x, rows, cols, ld_x, FP4Q_ALONG_ROWS, round_rows, codes_rows, scales_rows,
+                                       layout, &empty);
+    if (st != FP4Q_OK) return st;
+    st = check_mx_producer(x, rows, cols, ld_x, FP4Q_ALONG_COLS, round_cols, codes_cols, scales_cols, layout, &empty);
+    if (st != FP4Q_OK || empty) return st;
+    // K % 32 (or 128) of both operands makes rows and cols multiples of the
+    // block, so neither operand has padding rows
+    const uint64_t n = (uint64_t)rows * (uint64_t)cols;
+    const Range outs[4] = {bytes(codes_rows, n / 2), bytes(scales_rows, n / 32), bytes(codes_cols, n / 2),
+                           bytes(scales_cols, n / 32)};
+    for (int i = 0; i < 4; ++i)
+        for (int j = i + 1; j < 4; ++j)
+            if (overlap(outs[i], outs[j])) return FP4Q_EINVAL;
+    fp4q::QuantArgs a{};
+    a.x = x;
+    a.rows = rows;
+    a.cols = cols;
+    a.ld = ld_x;
+    a.axis = FP4Q_ALONG_COLS;
+    a.sr = round_cols == FP4Q_SR;
+    a.hadamard = hadamard_cols != 0;
+    a.tiled = layout == FP4Q_LAYOUT_TILED;
+    a.seed = seed;
+    a.stream_id = stream_id_cols;
+    a.sign_mask = sign_mask;
+    a.codes = codes_cols;
+    a.scales = scales_cols;
+    a.rows_round = round_rows == FP4Q_SR ? 2 : 1;
+    a.stream_id_rows = stream_id_rows;
+    a.codes_rows = codes_rows;
+    a.scales_rows = scales_rows;
+    (void)hipGetLastError();
+    return launched(fp4q::launch_quant_mx(a, as_stream(stream)));
+}
+
 size_t fp4q_nv_workspace_bytes(int64_t rows, int64_t cols, int axis, int domain)
 {
     (void)rows;

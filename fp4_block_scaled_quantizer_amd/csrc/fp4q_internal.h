@@ -20,6 +20,12 @@ struct QuantArgs {
     uint32_t sign_mask;
     void *codes;
     void *scales;
+    // dual output (axis 1 only): x along rows as well, rounded per rows_round
+    // (0 none, 1 RNE, 2 SR) with its own stream id
+    int rows_round;
+    uint32_t stream_id_rows;
+    void *codes_rows;
+    void *scales_rows;
 };
 
 struct GemmArgs {

@@ -214,6 +214,40 @@ __global__ __launch_bounds__(kThreads) void quant_mx_rows_kernel(const uint16_t 
     }
 }
 
+// One 8-element chunk of an MX operand along rows, encoded by a quad of lanes
+// (the four chunks of a 32-element block sit in lanes 4m .. 4m+3): returns
+// the packed codes of the chunk and sets the block's scale byte.  Every lane
+// of the wavefront must call it (the block amax is a quad shuffle).  `chunk`
+// is the chunk's index along K and `row` its row in the logical operand (the
+// SR counter), as in the row kernels.
+template <bool kSR>
+__device__ __forceinline__ uint32_t encode_row_chunk(const uint4 &q, uint32_t row, uint32_t chunk, uint32_t stream_id,
+                                                     uint32_t seed_lo, uint32_t seed_hi, uint32_t &sbyte)
+{
+    if (!kSR) {
+        uint32_t amax = amax8_bf16(q);
+        amax = xor_max<1>(amax);
+        amax = xor_max<2>(amax);
+        sbyte = mx_scale_byte(amax << 16);
+        return cvt8_bf16(q, mx_scale_f32(sbyte));
+    }
+    float f[8];
+    unpack8(q, f);
+    uint32_t amax = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) amax = max(amax, f2u(f[j]) & 0x7FFFFFFFu);
+    amax = xor_max<1>(amax);
+    amax = xor_max<2>(amax);
+    sbyte = mx_scale_byte(amax);
+    const float inv = mx_inv_scale(sbyte);
+    uint32_t w[4];
+    philox4x32_10(chunk, row, stream_id, 0u, seed_lo, seed_hi, w);
+    uint32_t packed = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) packed |= e2m1_sr(f[j] * inv, r16_of(w, j)) << (4 * j);
+    return packed;
+}
+
 // ------------------------------------------------------------------
 // MXFP4 along columns: the logical operand is x^T, blocks run down 32 rows of
 // one column of x.  A workgroup owns 128 rows (4 blocks along K) x 128
@@ -230,13 +264,21 @@ __global__ __launch_bounds__(kThreads) void quant_mx_rows_kernel(const uint16_t 
 constexpr int kColTile = 128;            // rows and columns of a workgroup tile
 constexpr int kColPitch = kColTile * 2;  // bytes per staged row
 
-template <bool kSR, bool kHad, bool kTiled>
+// Dual output (kRowsOut = 1: RNE, 2: SR): while the tile is in registers
+// the kernel also writes x along rows ([rows x cols], no Hadamard) to
+// codes_r / scales_r, bit-identical to the row producers, so one read of x
+// yields both operands a training step needs from it.  The dual launch
+// requires rows and cols to be multiples of 32 (linear) or 128 (tiled).
+template <bool kSR, bool kHad, bool kTiled, int kRowsOut = 0>
 __global__ __launch_bounds__(kThreads) void quant_mx_cols_kernel(const uint16_t *__restrict__ x, uint32_t rows,
                                                                  uint32_t cols, uint32_t ld, uint32_t Rp,
                                                                  uint8_t *__restrict__ codes,
                                                                  uint8_t *__restrict__ scales, uint32_t seed_lo,
                                                                  uint32_t seed_hi, uint32_t stream_id,
-                                                                 uint32_t sign_mask)
+                                                                 uint32_t sign_mask,
+                                                                 uint8_t *__restrict__ codes_r = nullptr,
+                                                                 uint8_t *__restrict__ scales_r = nullptr,
+                                                                 uint32_t stream_id_r = 0)
 {
     __shared__ __attribute__((aligned(16))) uint8_t tile[kColTile * kColPitch];
     __shared__ __attribute__((aligned(16))) uint8_t sc[kColTile * 4];
@@ -264,6 +306,28 @@ __global__ __launch_bounds__(kThreads) void quant_mx_cols_kernel(const uint16_t 
         }
 #pragma unroll
         for (int p = 0; p < 8; ++p) *reinterpret_cast<uint4 *>(tile + (p * 16 + rr) * kColPitch + ch * 16) = q[p];
+        if constexpr (kRowsOut != 0) {
+            // x along rows: chunk c / 8 of row r; lanes 4m .. 4m+3 hold one
+            // 32-element block
+#pragma unroll
+            for (int p = 0; p < 8; ++p) {
+                const uint32_t r = r0 + p * 16 + rr;
+                uint32_t sbyte;
+                const uint32_t packed =
+                    encode_row_chunk<kRowsOut == 2>(q[p], r, c >> 3, stream_id_r, seed_lo, seed_hi, sbyte);
+                if (r < rows && c < cols) {
+                    if (kTiled) {
+                        *reinterpret_cast<uint32_t *>(codes_r + ((size_t)(r >> 5) * (cols >> 6) + (c >> 6)) * 1024 +
+                                                      ((r & 31) + 32 * ((c >> 5) & 1)) * 16 + ((c >> 3) & 3) * 4) =
+                            packed;
+                        if ((ch & 3) == 0) scales_r[((size_t)(c >> 7) * rows + r) * 4 + ((c >> 5) & 3)] = (uint8_t)sbyte;
+                    } else {
+                        *reinterpret_cast<uint32_t *>(codes_r + (size_t)r * (cols >> 1) + (c >> 1)) = packed;
+                        if ((ch & 3) == 0) scales_r[(size_t)r * (cols >> 5) + (c >> 5)] = (uint8_t)sbyte;
+                    }
+                }
+            }
+        }
     }
     __syncthreads();
     const uint32_t cp = t & 63, jb = t >> 6;
@@ -631,14 +695,24 @@ int launch_quant_mx(const QuantArgs &a, hipStream_t st)
         const uint32_t span = a.tiled ? Rp : cols;
         dim3 grid((span + kColTile - 1) / kColTile, (rows + kColTile - 1) / kColTile);
         auto *codes = reinterpret_cast<uint8_t *>(a.codes);
-#define FP4Q_LAUNCH_COLS(SR, HAD, T)                                                                          \
-    hipLaunchKernelGGL((quant_mx_cols_kernel<SR, HAD, T>), grid, dim3(kThreads), 0, st, x, rows, cols, (uint32_t)a.ld, \
-                       Rp, codes, scales, seed_lo, seed_hi, a.stream_id, a.sign_mask)
+        auto *codes_r = reinterpret_cast<uint8_t *>(a.codes_rows);
+        auto *scales_r = reinterpret_cast<uint8_t *>(a.scales_rows);
+#define FP4Q_LAUNCH_COLS(SR, HAD, T, RO)                                                                          \
+    hipLaunchKernelGGL((quant_mx_cols_kernel<SR, HAD, T, RO>), grid, dim3(kThreads), 0, st, x, rows, cols,          \
+                       (uint32_t)a.ld, Rp, codes, scales, seed_lo, seed_hi, a.stream_id, a.sign_mask, codes_r,      \
+                       scales_r, a.stream_id_rows)
+#define FP4Q_LAUNCH_COLS1(SR, HAD, T)                                       \
+    do {                                                                    \
+        if (a.rows_round == 1) FP4Q_LAUNCH_COLS(SR, HAD, T, 1);             \
+        else if (a.rows_round == 2) FP4Q_LAUNCH_COLS(SR, HAD, T, 2);        \
+        else FP4Q_LAUNCH_COLS(SR, HAD, T, 0);                               \
+    } while (0)
 #define FP4Q_LAUNCH_COLS2(SR, HAD) \
-    do { if (a.tiled) FP4Q_LAUNCH_COLS(SR, HAD, true); else FP4Q_LAUNCH_COLS(SR, HAD, false); } while (0)
+    do { if (a.tiled) FP4Q_LAUNCH_COLS1(SR, HAD, true); else FP4Q_LAUNCH_COLS1(SR, HAD, false); } while (0)
         if (a.sr) { if (a.hadamard) FP4Q_LAUNCH_COLS2(true, true); else FP4Q_LAUNCH_COLS2(true, false); }
         else { if (a.hadamard) FP4Q_LAUNCH_COLS2(false, true); else FP4Q_LAUNCH_COLS2(false, false); }
 #undef FP4Q_LAUNCH_COLS2
+#undef FP4Q_LAUNCH_COLS1
 #undef FP4Q_LAUNCH_COLS
     }
     return hipGetLastError() == hipSuccess ? 0 : 1;

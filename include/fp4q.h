@@ -154,6 +154,28 @@ FP4Q_API fp4q_status fp4_hadamard32_quantize(const void *x, int64_t rows, int64_
                                     uint32_t sign_mask, int round, uint64_t seed, uint32_t stream_id,
                                     void *codes, void *scales, int layout, void *stream);
 
+/* One read of x, both MXFP4 operands a training step takes from it: x along
+ * rows (the forward / dgrad operand, [rows x cols], no Hadamard) and x^T
+ * along columns with an optional fixed-sign Hadamard (the wgrad operand,
+ * [cols x rows]).  Saving the second one at forward time keeps the backward
+ * pass from reading x again ([Fusion] section "Why FP4 Speedups Often Remain
+ * Theoretical": the state kept for backpropagation is one of the overheads;
+ * section "The Design Philosophy of Format-Aware Fusion": each producer is
+ * bound to the layout its consumer loads).
+ * Outputs: codes_rows / scales_rows exactly as fp4_quantize_mx(x, rows, cols,
+ * ld_x, FP4Q_ALONG_ROWS, round_rows, seed, stream_id_rows, ...) writes them,
+ * and codes_cols / scales_cols exactly as fp4_hadamard32_quantize (when
+ * hadamard_cols = 1, with sign_mask) or fp4_quantize_mx (hadamard_cols = 0)
+ * with FP4Q_ALONG_COLS, round_cols, seed, stream_id_cols; every byte is
+ * identical to those calls'.  Requires rows and cols to be multiples of 32
+ * (linear) or 128 (tiled); both outputs in `layout`.  Errors as the two
+ * producers, plus FP4Q_EINVAL for hadamard_cols other than 0 or 1 and for
+ * outputs that overlap each other. */
+FP4Q_API fp4q_status fp4_quantize_mx_dual(const void *x, int64_t rows, int64_t cols, int64_t ld_x, int round_rows,
+                                 uint32_t stream_id_rows, void *codes_rows, void *scales_rows, int hadamard_cols,
+                                 uint32_t sign_mask, int round_cols, uint32_t stream_id_cols, void *codes_cols,
+                                 void *scales_cols, uint64_t seed, int layout, void *stream);
+
 /* Bytes of device workspace fp4_quantize_nv needs (the global domain's
  * partial maxima; 0 for the tile domain). */
 FP4Q_API size_t fp4q_nv_workspace_bytes(int64_t rows, int64_t cols, int axis, int domain);

@@ -25,8 +25,8 @@ def lib():
 
 def test_exports_every_declared_function():
     names = B.declared_functions()
-    assert set(names) >= {"fp4_quantize_mx", "fp4_quantize_nv", "fp4_hadamard32_quantize", "fp4_gemm_mx",
-                          "fp4_gemm_nv"}
+    assert set(names) >= {"fp4_quantize_mx", "fp4_quantize_nv", "fp4_hadamard32_quantize", "fp4_quantize_mx_dual",
+                          "fp4_gemm_mx", "fp4_gemm_nv"}
     for n in names:
         assert hasattr(L, n), n
     assert B.abi_version() == 1
@@ -135,3 +135,36 @@ def test_tiled_layout_status_codes():
     assert L.fp4_quantize_nv(X, 64, 64, 64, 0, 0, 0, 0, 0, CODES, SCALES, TS, WS, 4096, 1, None) == B.EUNSUPPORTED
     assert g_mx(layout=1, K=96) == B.ESHAPE
     assert g_mx(layout=3) == B.EINVAL
+
+
+CODES2 = 0x7F6000000000
+SCALES2 = 0x7F7000000000
+
+
+def q_dual(x=X, rows=64, cols=64, ld=64, rr=0, had=1, rc=0, codes_r=CODES, scales_r=SCALES, codes_c=CODES2,
+           scales_c=SCALES2, layout=0):
+    return L.fp4_quantize_mx_dual(x, rows, cols, ld, rr, 0, codes_r, scales_r, had, 0xF0F0F0F0, rc, 1, codes_c,
+                                  scales_c, 7, layout, None)
+
+
+def test_quantize_mx_dual_status_codes():
+    assert q_dual(rr=2) == B.EINVAL
+    assert q_dual(rc=3) == B.EINVAL
+    assert q_dual(had=2) == B.EINVAL
+    assert q_dual(layout=2) == B.EINVAL
+    assert q_dual(x=None) == B.EINVAL
+    assert q_dual(codes_r=None) == B.EINVAL
+    assert q_dual(scales_c=None) == B.EINVAL
+    assert q_dual(cols=48, ld=48) == B.ESHAPE            # K of the row operand % 32
+    assert q_dual(rows=48) == B.ESHAPE                   # K of the column operand % 32
+    assert q_dual(rows=96, layout=1) == B.ESHAPE         # tiled: rows % 128
+    assert q_dual(rows=128, cols=96, ld=96, layout=1) == B.ESHAPE
+    assert q_dual(ld=32) == B.ESHAPE
+    assert q_dual(rows=-1) == B.ESHAPE
+    assert q_dual(x=X + 8) == B.EALIGN
+    assert q_dual(codes_c=CODES2 + 4) == B.EALIGN
+    assert q_dual(codes_c=CODES + 512) == B.EINVAL       # the two operands' codes overlap
+    assert q_dual(scales_c=SCALES + 16) == B.EINVAL      # the two operands' scales overlap
+    assert q_dual(codes_r=X + 64) == B.EINVAL            # output overlaps input
+    assert q_dual(rows=0) == B.OK                        # empty: nothing enqueued
+    assert q_dual(cols=0, ld=0) == B.OK
