@@ -49,7 +49,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="qkv",
                     choices=["qkv", "mlp", "backward", "backward_dual", "dual_x", "nvfp4_global", "nvfp4_tile",
-                             "copy"],
+                             "nvfp4_chain", "nvfp4_chain_2pass", "copy"],
                     help="copy = a plain 1 GiB device copy: the HBM reference for counter scaling")
     ap.add_argument("--copies", type=int, default=4, help="input copies rotated across steps (cold producers)")
     ap.add_argument("--layout", default="tiled", choices=["tiled", "linear"],
@@ -225,6 +225,62 @@ def build_workload(name, dev, copies, layout_name="tiled"):
                            (", dY's two operands from one read (dual producer)" if dual else ""),
                "dgrad_mnk": [T, I, O], "wgrad_mnk": [O, I, T], "layout": layout_name, "input_copies": copies}
         return cfg, ops, 2.0 * T * I * O * 2
+    if name in ("nvfp4_chain", "nvfp4_chain_2pass"):
+        # two NVFP4 GEMMs in a row (Llama-3-8B MLP up and down shapes, global
+        # domain): the first GEMM's output is the second's A operand.  In
+        # nvfp4_chain the first GEMM also reports max |C1| and C1 is quantized
+        # in one pass with it; nvfp4_chain_2pass runs the amax pass instead.
+        one_pass = name == "nvfp4_chain"
+        X = gen("nvfp4", "X", copies)
+        W1 = gen("nvfp4", "W", copies)
+        W2 = gen("mlp_down", "W", copies)
+        M, K = X[0].shape
+        N1 = W1[0].shape[0]
+        N2 = W2[0].shape[0]
+        G = B.NV_GLOBAL
+
+        def nvbufs(R, Kc):
+            return (torch.empty((R, Kc // 2), dtype=torch.uint8, device=dev),
+                    torch.empty((R, Kc // 16), dtype=torch.uint8, device=dev),
+                    torch.empty((1,), dtype=torch.float32, device=dev),
+                    torch.empty((max(1, B.fp4q_nv_workspace_bytes(R, Kc, 0, G)),), dtype=torch.uint8, device=dev))
+
+        bx, bw1, bc1, bw2 = nvbufs(M, K), nvbufs(N1, K), nvbufs(M, N1), nvbufs(N2, N1)
+        C1 = torch.empty((M, N1), dtype=torch.bfloat16, device=dev)
+        C2 = torch.empty((M, N2), dtype=torch.bfloat16, device=dev)
+        amax = torch.zeros((1,), dtype=torch.float32, device=dev)
+
+        def q(src, b, **kw):
+            return B.fp4_quantize_nv(src, G, codes=b[0], scales=b[1], tensor_scale=b[2], workspace=b[3], **kw)
+
+        def gemm1(s):
+            if one_pass:
+                amax.zero_()
+                B.fp4_gemm_nv(*bx[:3], *bw1[:3], G, out_dtype=torch.bfloat16, c=C1, c_amax=amax)
+            else:
+                B.fp4_gemm_nv(*bx[:3], *bw1[:3], G, out_dtype=torch.bfloat16, c=C1)
+
+        ops = [
+            ("quantize X (NVFP4)", "nv_quant_global (amax + quantize)", lambda s: q(X[s % copies], bx),
+             M * K * NV_GLOBAL_BYTES_PER_ELEM, "GB/s", HBM_PEAK_GBS, "hbm"),
+            ("quantize W1 (NVFP4)", "nv_quant_global (amax + quantize)", lambda s: q(W1[s % copies], bw1),
+             N1 * K * NV_GLOBAL_BYTES_PER_ELEM, "GB/s", HBM_PEAK_GBS, "hbm"),
+            ("GEMM1 X W1^T" + (" (+ max |C1|)" if one_pass else ""), "gemm_nv_fp16_kernel", gemm1,
+             2.0 * M * N1 * K, "TFLOP/s", BF16_PEAK_TFLOPS, "mfma"),
+            ("quantize C1 (NVFP4, " + ("one pass, GEMM1's amax)" if one_pass else "amax pass + quantize)"),
+             "nv_quant_global_kernel" if one_pass else "nv_quant_global (amax + quantize)",
+             (lambda s: q(C1, bc1, amax=amax)) if one_pass else (lambda s: q(C1, bc1)),
+             M * N1 * (NV_GLOBAL_BYTES_PER_ELEM - (2 if one_pass else 0)), "GB/s", HBM_PEAK_GBS, "hbm"),
+            ("quantize W2 (NVFP4)", "nv_quant_global (amax + quantize)", lambda s: q(W2[s % copies], bw2),
+             N2 * N1 * NV_GLOBAL_BYTES_PER_ELEM, "GB/s", HBM_PEAK_GBS, "hbm"),
+            ("GEMM2 C1 W2^T", "gemm_nv_fp16_kernel",
+             lambda s: B.fp4_gemm_nv(*bc1[:3], *bw2[:3], G, out_dtype=torch.bfloat16, c=C2),
+             2.0 * M * N2 * N1, "TFLOP/s", BF16_PEAK_TFLOPS, "mfma"),
+        ]
+        cfg = {"workload": "NVFP4 global, two chained GEMMs (MLP up then down shapes), C1 quantized " +
+                           ("in one pass with GEMM1's fused amax" if one_pass else "with its own amax pass"),
+               "gemm1_mnk": [M, N1, K], "gemm2_mnk": [M, N2, N1], "out": "bf16", "input_copies": copies}
+        return cfg, ops, 2.0 * M * N1 * K + 2.0 * M * N2 * N1
     # NVFP4
     domain = B.NV_GLOBAL if name == "nvfp4_global" else B.NV_TILE128
     X = gen("nvfp4", "X", copies)

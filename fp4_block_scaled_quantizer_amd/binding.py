@@ -63,8 +63,11 @@ def lib() -> ctypes.CDLL:
                                   i32, vp]
     L.fp4_gemm_mx.argtypes = [vp, vp, vp, vp, i64, i64, i64, f32, i32, vp, i32, i64, vp]
     L.fp4_gemm_nv.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, i64, i64, f32, i32, vp, i32, i64, vp]
+    L.fp4_gemm_mx_amax.argtypes = [vp, vp, vp, vp, i64, i64, i64, f32, i32, vp, i32, i64, vp, vp]
+    L.fp4_gemm_nv_amax.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, i64, i64, f32, i32, vp, i32, i64, vp, vp]
+    L.fp4_quantize_nv_amax.argtypes = [vp, i64, i64, i64, i32, u64, u32, vp, vp, vp, vp, vp]
     for fn in ("fp4_quantize_mx", "fp4_hadamard32_quantize", "fp4_quantize_mx_dual", "fp4_quantize_nv",
-               "fp4_gemm_mx", "fp4_gemm_nv"):
+               "fp4_quantize_nv_amax", "fp4_gemm_mx", "fp4_gemm_nv", "fp4_gemm_mx_amax", "fp4_gemm_nv_amax"):
         getattr(L, fn).restype = i32
     L.fp4q_status_str.argtypes = [i32]
     L.fp4q_status_str.restype = ctypes.c_char_p
@@ -89,6 +92,12 @@ def _check(fn: str, status: int):
 
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
     return None if t is None else t.data_ptr()
+
+
+def _amax_ptr(t: torch.Tensor) -> int:
+    if t.dtype != torch.float32 or t.numel() < 1:
+        raise ValueError("c_amax must be a float32 tensor with at least one element")
+    return t.data_ptr()
 
 
 def _stream(stream) -> int:
@@ -181,7 +190,9 @@ def nv_tensor_scale_shape(R: int, K: int, domain: int):
 def fp4_quantize_nv(x: torch.Tensor, domain: int = NV_GLOBAL, *, cols: Optional[int] = None, axis: int = ALONG_ROWS,
                     round: int = RNE, seed: int = 0, stream_id: int = 0, codes: Optional[torch.Tensor] = None,
                     scales: Optional[torch.Tensor] = None, tensor_scale: Optional[torch.Tensor] = None,
-                    workspace: Optional[torch.Tensor] = None, stream=None):
+                    workspace: Optional[torch.Tensor] = None, amax: Optional[torch.Tensor] = None, stream=None):
+    """NVFP4; with `amax` (a device float32 tensor holding max |x|, global
+    domain only) the producer runs in one pass (fp4_quantize_nv_amax)."""
     rows, cols, ld = _input(x, cols)
     R, K = _logical(rows, cols, axis)
     if codes is None:
@@ -190,6 +201,14 @@ def fp4_quantize_nv(x: torch.Tensor, domain: int = NV_GLOBAL, *, cols: Optional[
         scales = torch.empty((R, K // 16), dtype=torch.uint8, device=x.device)
     if tensor_scale is None:
         tensor_scale = torch.empty(nv_tensor_scale_shape(R, K, domain), dtype=torch.float32, device=x.device)
+    if amax is not None:
+        if domain != NV_GLOBAL or axis != ALONG_ROWS or amax.dtype != torch.float32:
+            raise ValueError("a given amax is a float32 tensor for the global domain along rows")
+        _check("fp4_quantize_nv_amax",
+               lib().fp4_quantize_nv_amax(x.data_ptr(), rows, cols, ld, round, seed, stream_id, amax.data_ptr(),
+                                          codes.data_ptr(), scales.data_ptr(), tensor_scale.data_ptr(),
+                                          _stream(stream)))
+        return codes, scales, tensor_scale
     need = fp4q_nv_workspace_bytes(rows, cols, axis, domain)
     if workspace is None and need > 0:
         workspace = torch.empty((need,), dtype=torch.uint8, device=x.device)
@@ -213,15 +232,22 @@ def _gemm_out(M: int, N: int, out_dtype, device, c: Optional[torch.Tensor]):
 def fp4_gemm_mx(a_codes: torch.Tensor, a_scales: torch.Tensor, b_codes: torch.Tensor, b_scales: torch.Tensor, *,
                 alpha: float = 1.0, out_dtype=torch.float32, c: Optional[torch.Tensor] = None,
                 layout: int = LAYOUT_LINEAR, m: Optional[int] = None, n: Optional[int] = None,
-                stream=None) -> torch.Tensor:
+                c_amax: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """C = alpha * A B^T.  In the tiled layout the code tensors carry rows
-    padded to a multiple of 32, so pass the logical m and n."""
+    padded to a multiple of 32, so pass the logical m and n.  With `c_amax`
+    (a device float32 tensor) max |C| is folded into it (fp4_gemm_mx_amax)."""
     M = a_codes.shape[0] if m is None else m
     N = b_codes.shape[0] if n is None else n
     K = a_codes.shape[1] * 2
     if b_codes.shape[1] * 2 != K:
         raise ValueError("A and B must have the same K")
     c, ctype, ldc = _gemm_out(M, N, out_dtype, a_codes.device, c)
+    if c_amax is not None:
+        _check("fp4_gemm_mx_amax",
+               lib().fp4_gemm_mx_amax(a_codes.data_ptr(), a_scales.data_ptr(), b_codes.data_ptr(), b_scales.data_ptr(),
+                                      M, N, K, float(alpha), layout, c.data_ptr(), ctype, ldc, _amax_ptr(c_amax),
+                                      _stream(stream)))
+        return c
     _check("fp4_gemm_mx", lib().fp4_gemm_mx(a_codes.data_ptr(), a_scales.data_ptr(), b_codes.data_ptr(),
                                             b_scales.data_ptr(), M, N, K, float(alpha), layout,
                                             c.data_ptr(), ctype, ldc, _stream(stream)))
@@ -230,11 +256,21 @@ def fp4_gemm_mx(a_codes: torch.Tensor, a_scales: torch.Tensor, b_codes: torch.Te
 
 def fp4_gemm_nv(a_codes: torch.Tensor, a_scales: torch.Tensor, a_tensor_scale: torch.Tensor, b_codes: torch.Tensor,
                 b_scales: torch.Tensor, b_tensor_scale: torch.Tensor, domain: int = NV_GLOBAL, *, alpha: float = 1.0,
-                out_dtype=torch.float32, c: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+                out_dtype=torch.float32, c: Optional[torch.Tensor] = None, c_amax: Optional[torch.Tensor] = None,
+                stream=None) -> torch.Tensor:
+    """With `c_amax` (a device float32 tensor) max |C| is folded into it
+    (fp4_gemm_nv_amax)."""
     M, N, K = a_codes.shape[0], b_codes.shape[0], a_codes.shape[1] * 2
     if b_codes.shape[1] * 2 != K:
         raise ValueError("A and B must have the same K")
     c, ctype, ldc = _gemm_out(M, N, out_dtype, a_codes.device, c)
+    if c_amax is not None:
+        _check("fp4_gemm_nv_amax",
+               lib().fp4_gemm_nv_amax(a_codes.data_ptr(), a_scales.data_ptr(), a_tensor_scale.data_ptr(),
+                                      b_codes.data_ptr(), b_scales.data_ptr(), b_tensor_scale.data_ptr(), domain, M, N,
+                                      K, float(alpha), LAYOUT_LINEAR, c.data_ptr(), ctype, ldc, _amax_ptr(c_amax),
+                                      _stream(stream)))
+        return c
     _check("fp4_gemm_nv", lib().fp4_gemm_nv(a_codes.data_ptr(), a_scales.data_ptr(), a_tensor_scale.data_ptr(),
                                             b_codes.data_ptr(), b_scales.data_ptr(), b_tensor_scale.data_ptr(),
                                             domain, M, N, K, float(alpha), LAYOUT_LINEAR, c.data_ptr(), ctype, ldc,

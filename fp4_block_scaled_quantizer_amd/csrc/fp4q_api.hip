@@ -115,6 +115,135 @@ fp4q_status check_gemm_common(const void *a_codes, const void *a_scales, const v
     return FP4Q_OK;
 }
 
+// An optional output amax: one 4-byte aligned float outside C.
+bool amax_ok(const float *c_amax, const void *c, int64_t M, int64_t N, int64_t ldc, int c_type)
+{
+    if (!aligned(c_amax, 4)) return false;
+    const uint64_t esize = c_type == FP4Q_OUT_F32 ? 4 : 2;
+    return !overlap(bytes(c_amax, 4), bytes(c, ((uint64_t)(M - 1) * (uint64_t)ldc + (uint64_t)N) * esize));
+}
+
+fp4q_status run_gemm_mx(const void *a_codes, const void *a_scales, const void *b_codes, const void *b_scales,
+                        int64_t M, int64_t N, int64_t K, float alpha, int layout, void *c, int c_type, int64_t ldc,
+                        float *c_amax, void *stream)
+{
+    bool empty = false;
+    const fp4q_status st =
+        check_gemm_common(a_codes, a_scales, b_codes, b_scales, M, N, K, layout, c, c_type, ldc, 32, &empty);
+    if (st != FP4Q_OK || empty) return st;
+    if (c_amax && !amax_ok(c_amax, c, M, N, ldc, c_type)) return aligned(c_amax, 4) ? FP4Q_EINVAL : FP4Q_EALIGN;
+    fp4q::GemmArgs g{};
+    g.a_codes = a_codes;
+    g.a_scales = a_scales;
+    g.b_codes = b_codes;
+    g.b_scales = b_scales;
+    g.M = M;
+    g.N = N;
+    g.K = K;
+    g.alpha = alpha;
+    g.c = c;
+    g.c_bf16 = c_type == FP4Q_OUT_BF16;
+    g.ldc = ldc;
+    g.tiled = layout == FP4Q_LAYOUT_TILED;
+    g.c_amax = reinterpret_cast<uint32_t *>(c_amax);
+    (void)hipGetLastError();
+    return launched(fp4q::launch_gemm_mx(g, as_stream(stream)));
+}
+
+fp4q_status run_gemm_nv(const void *a_codes, const void *a_scales, const float *a_tensor_scale, const void *b_codes,
+                        const void *b_scales, const float *b_tensor_scale, int domain, int64_t M, int64_t N,
+                        int64_t K, float alpha, int layout, void *c, int c_type, int64_t ldc, float *c_amax,
+                        void *stream)
+{
+    if (domain != FP4Q_NV_GLOBAL && domain != FP4Q_NV_TILE128) return FP4Q_EINVAL;
+    if (layout == FP4Q_LAYOUT_TILED) return FP4Q_EUNSUPPORTED;
+    bool empty = false;
+    const fp4q_status st =
+        check_gemm_common(a_codes, a_scales, b_codes, b_scales, M, N, K, layout, c, c_type, ldc, 16, &empty);
+    if (st != FP4Q_OK || empty) return st;
+    if (c_amax && !amax_ok(c_amax, c, M, N, ldc, c_type)) return aligned(c_amax, 4) ? FP4Q_EINVAL : FP4Q_EALIGN;
+    if (K > 0) {
+        if (!a_tensor_scale || !b_tensor_scale) return FP4Q_EINVAL;
+        if (!aligned(a_tensor_scale, 4) || !aligned(b_tensor_scale, 4)) return FP4Q_EALIGN;
+        const uint64_t TK = (uint64_t)(K + 127) / 128;
+        const uint64_t na = domain == FP4Q_NV_GLOBAL ? 1 : (uint64_t)((M + 127) / 128) * TK;
+        const uint64_t nb = domain == FP4Q_NV_GLOBAL ? 1 : (uint64_t)((N + 127) / 128) * TK;
+        const uint64_t esize = c_type == FP4Q_OUT_F32 ? 4 : 2;
+        const Range rc = bytes(c, ((uint64_t)(M - 1) * (uint64_t)ldc + (uint64_t)N) * esize);
+        if (overlap(rc, bytes(a_tensor_scale, na * 4)) || overlap(rc, bytes(b_tensor_scale, nb * 4)))
+            return FP4Q_EINVAL;
+    }
+    fp4q::GemmArgs g{};
+    g.a_codes = a_codes;
+    g.a_scales = a_scales;
+    g.b_codes = b_codes;
+    g.b_scales = b_scales;
+    g.a_ts = a_tensor_scale;
+    g.b_ts = b_tensor_scale;
+    g.nv_domain = domain;
+    g.M = M;
+    g.N = N;
+    g.K = K;
+    g.alpha = alpha;
+    g.c = c;
+    g.c_bf16 = c_type == FP4Q_OUT_BF16;
+    g.ldc = ldc;
+    g.c_amax = reinterpret_cast<uint32_t *>(c_amax);
+    (void)hipGetLastError();
+    return launched(fp4q::launch_gemm_nv(g, as_stream(stream)));
+}
+
+
+fp4q_status run_quantize_nv(const void *x, int64_t rows, int64_t cols, int64_t ld_x, int axis, int round,
+                            uint64_t seed, uint32_t stream_id, int domain, void *codes, void *scales,
+                            float *tensor_scale, void *workspace, size_t workspace_bytes, int layout,
+                            const float *given_amax, void *stream)
+{
+    if ((axis != FP4Q_ALONG_ROWS && axis != FP4Q_ALONG_COLS) || (round != FP4Q_RNE && round != FP4Q_SR) ||
+        (domain != FP4Q_NV_GLOBAL && domain != FP4Q_NV_TILE128) ||
+        (layout != FP4Q_LAYOUT_LINEAR && layout != FP4Q_LAYOUT_TILED))
+        return FP4Q_EINVAL;
+    if (layout == FP4Q_LAYOUT_TILED) return FP4Q_EUNSUPPORTED;
+    if (rows < 0 || cols < 0 || ld_x < cols || rows > kMaxDim || cols > kMaxDim || ld_x > kMaxDim)
+        return FP4Q_ESHAPE;
+    if (axis == FP4Q_ALONG_COLS) return FP4Q_EUNSUPPORTED;
+    const int64_t R = rows, K = cols;
+    if (K % 16 != 0) return FP4Q_ESHAPE;
+    if ((uint64_t)R * (uint64_t)(K / 8) >= (1ull << 32)) return FP4Q_ESHAPE;
+    const bool empty = R == 0 || K == 0;
+    if (empty && domain == FP4Q_NV_TILE128) return FP4Q_OK;  // no tiles, no tensor scales
+    if (!tensor_scale) return FP4Q_EINVAL;
+    if (!empty && (!x || !codes || !scales)) return FP4Q_EINVAL;
+    if (!empty && (!aligned(x, 16) || !aligned(codes, 16) || ld_x % 8 != 0)) return FP4Q_EALIGN;
+    if (!aligned(tensor_scale, 4)) return FP4Q_EALIGN;
+    const size_t need = given_amax ? 0 : fp4q_nv_workspace_bytes(rows, cols, axis, domain);
+    if (need > 0 && (!workspace || workspace_bytes < need)) return FP4Q_EINVAL;
+    if (need > 0 && !aligned(workspace, 4)) return FP4Q_EALIGN;
+    const uint64_t nts = domain == FP4Q_NV_GLOBAL ? 1 : (uint64_t)((R + 127) / 128) * (uint64_t)((K + 127) / 128);
+    const Range rx = bytes(x, input_span(rows, cols, ld_x));
+    const Range outs[4] = {bytes(codes, (uint64_t)R * K / 2), bytes(scales, (uint64_t)R * K / 16),
+                           bytes(tensor_scale, nts * 4), bytes(workspace, need)};
+    for (int i = 0; i < 4; ++i) {
+        if (overlap(rx, outs[i])) return FP4Q_EINVAL;
+        if (given_amax && overlap(bytes(given_amax, 4), outs[i])) return FP4Q_EINVAL;
+        for (int j = i + 1; j < 4; ++j)
+            if (overlap(outs[i], outs[j])) return FP4Q_EINVAL;
+    }
+    fp4q::QuantArgs a{};
+    a.x = x;
+    a.rows = rows;
+    a.cols = cols;
+    a.ld = ld_x;
+    a.axis = axis;
+    a.sr = round == FP4Q_SR;
+    a.seed = seed;
+    a.stream_id = stream_id;
+    a.codes = codes;
+    a.scales = scales;
+    (void)hipGetLastError();
+    return launched(fp4q::launch_quant_nv(a, domain, tensor_scale, workspace, given_amax, as_stream(stream)));
+}
+
 }  // namespace
 
 extern "C" {
@@ -188,113 +317,51 @@ fp4q_status fp4_quantize_nv(const void *x, int64_t rows, int64_t cols, int64_t l
                             uint64_t seed, uint32_t stream_id, int domain, void *codes, void *scales,
                             float *tensor_scale, void *workspace, size_t workspace_bytes, int layout, void *stream)
 {
-    if ((axis != FP4Q_ALONG_ROWS && axis != FP4Q_ALONG_COLS) || (round != FP4Q_RNE && round != FP4Q_SR) ||
-        (domain != FP4Q_NV_GLOBAL && domain != FP4Q_NV_TILE128) ||
-        (layout != FP4Q_LAYOUT_LINEAR && layout != FP4Q_LAYOUT_TILED))
-        return FP4Q_EINVAL;
-    if (layout == FP4Q_LAYOUT_TILED) return FP4Q_EUNSUPPORTED;
-    if (rows < 0 || cols < 0 || ld_x < cols || rows > kMaxDim || cols > kMaxDim || ld_x > kMaxDim)
-        return FP4Q_ESHAPE;
-    if (axis == FP4Q_ALONG_COLS) return FP4Q_EUNSUPPORTED;
-    const int64_t R = rows, K = cols;
-    if (K % 16 != 0) return FP4Q_ESHAPE;
-    if ((uint64_t)R * (uint64_t)(K / 8) >= (1ull << 32)) return FP4Q_ESHAPE;
-    const bool empty = R == 0 || K == 0;
-    if (empty && domain == FP4Q_NV_TILE128) return FP4Q_OK;  // no tiles, no tensor scales
-    if (!tensor_scale) return FP4Q_EINVAL;
-    if (!empty && (!x || !codes || !scales)) return FP4Q_EINVAL;
-    if (!empty && (!aligned(x, 16) || !aligned(codes, 16) || ld_x % 8 != 0)) return FP4Q_EALIGN;
-    if (!aligned(tensor_scale, 4)) return FP4Q_EALIGN;
-    const size_t need = fp4q_nv_workspace_bytes(rows, cols, axis, domain);
-    if (need > 0 && (!workspace || workspace_bytes < need)) return FP4Q_EINVAL;
-    if (need > 0 && !aligned(workspace, 4)) return FP4Q_EALIGN;
-    const uint64_t nts = domain == FP4Q_NV_GLOBAL ? 1 : (uint64_t)((R + 127) / 128) * (uint64_t)((K + 127) / 128);
-    const Range rx = bytes(x, input_span(rows, cols, ld_x));
-    const Range outs[4] = {bytes(codes, (uint64_t)R * K / 2), bytes(scales, (uint64_t)R * K / 16),
-                           bytes(tensor_scale, nts * 4), bytes(workspace, need)};
-    for (int i = 0; i < 4; ++i) {
-        if (overlap(rx, outs[i])) return FP4Q_EINVAL;
-        for (int j = i + 1; j < 4; ++j)
-            if (overlap(outs[i], outs[j])) return FP4Q_EINVAL;
-    }
-    fp4q::QuantArgs a{};
-    a.x = x;
-    a.rows = rows;
-    a.cols = cols;
-    a.ld = ld_x;
-    a.axis = axis;
-    a.sr = round == FP4Q_SR;
-    a.seed = seed;
-    a.stream_id = stream_id;
-    a.codes = codes;
-    a.scales = scales;
-    (void)hipGetLastError();
-    return launched(fp4q::launch_quant_nv(a, domain, tensor_scale, workspace, as_stream(stream)));
+    return run_quantize_nv(x, rows, cols, ld_x, axis, round, seed, stream_id, domain, codes, scales, tensor_scale,
+                           workspace, workspace_bytes, layout, nullptr, stream);
 }
 
 fp4q_status fp4_gemm_mx(const void *a_codes, const void *a_scales, const void *b_codes, const void *b_scales,
                         int64_t M, int64_t N, int64_t K, float alpha, int layout, void *c, int c_type, int64_t ldc,
                         void *stream)
 {
-    bool empty = false;
-    const fp4q_status st =
-        check_gemm_common(a_codes, a_scales, b_codes, b_scales, M, N, K, layout, c, c_type, ldc, 32, &empty);
-    if (st != FP4Q_OK || empty) return st;
-    fp4q::GemmArgs g{};
-    g.a_codes = a_codes;
-    g.a_scales = a_scales;
-    g.b_codes = b_codes;
-    g.b_scales = b_scales;
-    g.M = M;
-    g.N = N;
-    g.K = K;
-    g.alpha = alpha;
-    g.c = c;
-    g.c_bf16 = c_type == FP4Q_OUT_BF16;
-    g.ldc = ldc;
-    g.tiled = layout == FP4Q_LAYOUT_TILED;
-    (void)hipGetLastError();
-    return launched(fp4q::launch_gemm_mx(g, as_stream(stream)));
+    return run_gemm_mx(a_codes, a_scales, b_codes, b_scales, M, N, K, alpha, layout, c, c_type, ldc, nullptr, stream);
+}
+
+fp4q_status fp4_gemm_mx_amax(const void *a_codes, const void *a_scales, const void *b_codes, const void *b_scales,
+                             int64_t M, int64_t N, int64_t K, float alpha, int layout, void *c, int c_type,
+                             int64_t ldc, float *c_amax, void *stream)
+{
+    if (!c_amax) return FP4Q_EINVAL;
+    return run_gemm_mx(a_codes, a_scales, b_codes, b_scales, M, N, K, alpha, layout, c, c_type, ldc, c_amax, stream);
 }
 
 fp4q_status fp4_gemm_nv(const void *a_codes, const void *a_scales, const float *a_tensor_scale, const void *b_codes,
                         const void *b_scales, const float *b_tensor_scale, int domain, int64_t M, int64_t N,
                         int64_t K, float alpha, int layout, void *c, int c_type, int64_t ldc, void *stream)
 {
-    if (domain != FP4Q_NV_GLOBAL && domain != FP4Q_NV_TILE128) return FP4Q_EINVAL;
-    if (layout == FP4Q_LAYOUT_TILED) return FP4Q_EUNSUPPORTED;
-    bool empty = false;
-    const fp4q_status st =
-        check_gemm_common(a_codes, a_scales, b_codes, b_scales, M, N, K, layout, c, c_type, ldc, 16, &empty);
-    if (st != FP4Q_OK || empty) return st;
-    if (K > 0) {
-        if (!a_tensor_scale || !b_tensor_scale) return FP4Q_EINVAL;
-        if (!aligned(a_tensor_scale, 4) || !aligned(b_tensor_scale, 4)) return FP4Q_EALIGN;
-        const uint64_t TK = (uint64_t)(K + 127) / 128;
-        const uint64_t na = domain == FP4Q_NV_GLOBAL ? 1 : (uint64_t)((M + 127) / 128) * TK;
-        const uint64_t nb = domain == FP4Q_NV_GLOBAL ? 1 : (uint64_t)((N + 127) / 128) * TK;
-        const uint64_t esize = c_type == FP4Q_OUT_F32 ? 4 : 2;
-        const Range rc = bytes(c, ((uint64_t)(M - 1) * (uint64_t)ldc + (uint64_t)N) * esize);
-        if (overlap(rc, bytes(a_tensor_scale, na * 4)) || overlap(rc, bytes(b_tensor_scale, nb * 4)))
-            return FP4Q_EINVAL;
-    }
-    fp4q::GemmArgs g{};
-    g.a_codes = a_codes;
-    g.a_scales = a_scales;
-    g.b_codes = b_codes;
-    g.b_scales = b_scales;
-    g.a_ts = a_tensor_scale;
-    g.b_ts = b_tensor_scale;
-    g.nv_domain = domain;
-    g.M = M;
-    g.N = N;
-    g.K = K;
-    g.alpha = alpha;
-    g.c = c;
-    g.c_bf16 = c_type == FP4Q_OUT_BF16;
-    g.ldc = ldc;
-    (void)hipGetLastError();
-    return launched(fp4q::launch_gemm_nv(g, as_stream(stream)));
+    return run_gemm_nv(a_codes, a_scales, a_tensor_scale, b_codes, b_scales, b_tensor_scale, domain, M, N, K, alpha,
+                       layout, c, c_type, ldc, nullptr, stream);
+}
+
+fp4q_status fp4_gemm_nv_amax(const void *a_codes, const void *a_scales, const float *a_tensor_scale,
+                             const void *b_codes, const void *b_scales, const float *b_tensor_scale, int domain,
+                             int64_t M, int64_t N, int64_t K, float alpha, int layout, void *c, int c_type,
+                             int64_t ldc, float *c_amax, void *stream)
+{
+    if (!c_amax) return FP4Q_EINVAL;
+    return run_gemm_nv(a_codes, a_scales, a_tensor_scale, b_codes, b_scales, b_tensor_scale, domain, M, N, K, alpha,
+                       layout, c, c_type, ldc, c_amax, stream);
+}
+
+fp4q_status fp4_quantize_nv_amax(const void *x, int64_t rows, int64_t cols, int64_t ld_x, int round, uint64_t seed,
+                                 uint32_t stream_id, const float *amax, void *codes, void *scales,
+                                 float *tensor_scale, void *stream)
+{
+    if (!amax) return FP4Q_EINVAL;
+    if (!aligned(amax, 4)) return FP4Q_EALIGN;
+    return run_quantize_nv(x, rows, cols, ld_x, FP4Q_ALONG_ROWS, round, seed, stream_id, FP4Q_NV_GLOBAL, codes,
+                           scales, tensor_scale, nullptr, 0, FP4Q_LAYOUT_LINEAR, amax, stream);
 }
 
 const char *fp4q_status_str(int status)

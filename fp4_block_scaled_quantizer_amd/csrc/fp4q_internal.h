@@ -38,10 +38,14 @@ struct GemmArgs {
     void *c;
     bool c_bf16;
     int64_t ldc;
+    uint32_t *c_amax;  // optional: max |C| as stored, folded in as binary32 bits
 };
 
 int launch_quant_mx(const QuantArgs &a, hipStream_t st);
-int launch_quant_nv(const QuantArgs &a, int domain, float *tensor_scale, void *workspace, hipStream_t st);
+// given_amax: optional device pointer to the global domain's amax (skips the
+// amax pass); null for the two-pass global path and the tile domain
+int launch_quant_nv(const QuantArgs &a, int domain, float *tensor_scale, void *workspace, const float *given_amax,
+                    hipStream_t st);
 size_t nv_workspace_bytes(int domain);
 int launch_gemm_mx(const GemmArgs &g, hipStream_t st);
 int launch_gemm_nv(const GemmArgs &g, hipStream_t st);

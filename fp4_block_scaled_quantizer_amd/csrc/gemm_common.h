@@ -95,11 +95,19 @@ __device__ __forceinline__ void static_for(F &&f)
 // inside C with 16-byte aligned rows (then no guards are evaluated); the
 // lane index `el` is passed in from an opaque copy so that the lane-derived
 // offsets are recomputed here rather than kept live across the K loop.
+//
+// amax_out (optional): max |C| over the values this wave stores, as they are
+// stored, folded into *amax_out as binary32 bits with one atomic max per
+// wave (the bits of non-negative floats order like the values).  The maximum
+// is taken over the fp32 values and rounded to bf16 once at the end: round
+// to nearest even is monotonic, so that is the maximum of the rounded values.
+
 template <int kNJ, bool kScale, bool kBf16>
 __device__ __forceinline__ void store_wave_block(const v16f_t (&acc)[4][kNJ], uint8_t *ep, int el, int row_base,
                                                  int col_base, int M, int N, float alpha, void *C, int64_t ldc,
-                                                 bool vec_ok, bool full)
+                                                 bool vec_ok, bool full, uint32_t *amax_out)
 {
+    float amx = 0.0f;
     static_assert(kNJ == 2 || kNJ == 4, "a wave block is 128 rows x 64 or 128 columns");
     constexpr int kChunks = 2 * kNJ;  // 32 x 64 chunks
     constexpr int esize = kBf16 ? 2 : 4;
@@ -159,19 +167,31 @@ __device__ __forceinline__ void store_wave_block(const v16f_t (&acc)[4][kNJ], ui
                 o[u] = __builtin_bit_cast(uint4, r[u]);
             }
         }
+        constexpr int ne = kBf16 ? 8 : 4;  // elements per piece
         if (full) {
             uint8_t *base = reinterpret_cast<uint8_t *>(C) + ((int64_t)row0 * ldc + col0) * esize;
 #pragma unroll
             for (int u = 0; u < 8; ++u)
                 if (u < npieces)
                     *reinterpret_cast<uint4 *>(base + (int64_t)u * rstep * ldc * esize + lane_off) = o[u];
+            if (amax_out) {
+#pragma unroll
+                for (int u = 0; u < 8; ++u)
+                    amx = fmaxf(amx, fmaxf(fmaxf(fabsf(r[u].x), fabsf(r[u].y)), fmaxf(fabsf(r[u].z), fabsf(r[u].w))));
+            }
         } else {
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
                 if (u >= npieces) continue;
                 const int row = row0 + rl0 + u * rstep, col = col0 + cpi * (kBf16 ? 8 : 4);
                 if (row >= M) continue;
-                constexpr int ne = kBf16 ? 8 : 4;
+                if (amax_out) {
+                    // the piece's ne values: r[2u], r[2u+1] (bf16) or r[u] (fp32)
+                    const float *rv = reinterpret_cast<const float *>(&r[kBf16 ? 2 * u : u]);
+#pragma unroll
+                    for (int e = 0; e < ne; ++e)
+                        if (col + e < N) amx = fmaxf(amx, fabsf(rv[e]));
+                }
                 uint8_t *dstp = reinterpret_cast<uint8_t *>(C) + ((int64_t)row * ldc + col) * esize;
                 if (vec_ok && col + ne <= N) {
                     *reinterpret_cast<uint4 *>(dstp) = o[u];
@@ -206,25 +226,40 @@ __device__ __forceinline__ void store_wave_block(const v16f_t (&acc)[4][kNJ], ui
         }
         store(c + 1, r1);
     }
+    if (amax_out) {
+        uint32_t bits;
+        if constexpr (kBf16)
+            bits = (__builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){amx, 0.0f}, bf16x2_t)) & 0xFFFFu)
+                   << 16;
+        else
+            bits = __builtin_bit_cast(uint32_t, amx);
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1) bits = max(bits, (uint32_t)__shfl_xor((int)bits, m, 64));
+        if ((el & 63) == 0) atomicMax(amax_out, bits);
+    }
 }
 
 // The epilogue for a runtime output type and alpha.
 template <int kNJ>
 __device__ __forceinline__ void store_wave_block_any(const v16f_t (&acc)[4][kNJ], uint8_t *ep, int el, int row_base,
                                                      int col_base, int M, int N, float alpha, void *C, int64_t ldc,
-                                                     bool c_bf16, bool vec_ok)
+                                                     bool c_bf16, bool vec_ok, uint32_t *amax_out)
 {
     const bool full = vec_ok && row_base + 128 <= M && col_base + 32 * kNJ <= N;
     if (c_bf16) {
         if (alpha != 1.0f)
-            store_wave_block<kNJ, true, true>(acc, ep, el, row_base, col_base, M, N, alpha, C, ldc, vec_ok, full);
+            store_wave_block<kNJ, true, true>(acc, ep, el, row_base, col_base, M, N, alpha, C, ldc, vec_ok, full,
+                                              amax_out);
         else
-            store_wave_block<kNJ, false, true>(acc, ep, el, row_base, col_base, M, N, alpha, C, ldc, vec_ok, full);
+            store_wave_block<kNJ, false, true>(acc, ep, el, row_base, col_base, M, N, alpha, C, ldc, vec_ok, full,
+                                               amax_out);
     } else {
         if (alpha != 1.0f)
-            store_wave_block<kNJ, true, false>(acc, ep, el, row_base, col_base, M, N, alpha, C, ldc, vec_ok, full);
+            store_wave_block<kNJ, true, false>(acc, ep, el, row_base, col_base, M, N, alpha, C, ldc, vec_ok, full,
+                                              amax_out);
         else
-            store_wave_block<kNJ, false, false>(acc, ep, el, row_base, col_base, M, N, alpha, C, ldc, vec_ok, full);
+            store_wave_block<kNJ, false, false>(acc, ep, el, row_base, col_base, M, N, alpha, C, ldc, vec_ok, full,
+                                                amax_out);
     }
 }
 

@@ -65,7 +65,8 @@ template <bool kTiled>
 __global__ __launch_bounds__(256) void gemm_mx_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
                                                       const uint8_t *__restrict__ B, const uint8_t *__restrict__ Bs,
                                                       int M, int N, int K, float alpha, void *__restrict__ C,
-                                                      int64_t ldc, int c_bf16, int vec_ok, int tiles_m, int tiles_n)
+                                                      int64_t ldc, int c_bf16, int vec_ok, int tiles_m, int tiles_n,
+                                                      uint32_t *__restrict__ c_amax)
 {
     __shared__ __attribute__((aligned(1024))) uint8_t lds[kLdsBytes];
     const int tid = threadIdx.x, lane = tid & 63;
@@ -342,7 +343,7 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(const uint8_t *__restrict_
         // whole vector-memory counter (the next tile's DMA included).
         int el;
         asm volatile("v_mov_b32 %0, %1" : "=v"(el) : "v"(lane));
-        store_wave_block_any(acc, ep, el, row_base, col_base, M, N, alpha, C, ldc, c_bf16 != 0, vec_ok != 0);
+        store_wave_block_any(acc, ep, el, row_base, col_base, M, N, alpha, C, ldc, c_bf16 != 0, vec_ok != 0, c_amax);
         if (next >= ntiles) break;
         tile = next;
     }
@@ -378,10 +379,10 @@ int launch_gemm_mx(const GemmArgs &g, hipStream_t st)
     const int grid = min(tiles_m * tiles_n, cus);
     if (g.tiled)
         hipLaunchKernelGGL(gemm_mx_kernel<true>, dim3(grid), dim3(256), 0, st, a, as, b, bs, M, N, K, g.alpha, g.c,
-                           g.ldc, (int)g.c_bf16, vec_ok, tiles_m, tiles_n);
+                           g.ldc, (int)g.c_bf16, vec_ok, tiles_m, tiles_n, g.c_amax);
     else
         hipLaunchKernelGGL(gemm_mx_kernel<false>, dim3(grid), dim3(256), 0, st, a, as, b, bs, M, N, K, g.alpha, g.c,
-                           g.ldc, (int)g.c_bf16, vec_ok, tiles_m, tiles_n);
+                           g.ldc, (int)g.c_bf16, vec_ok, tiles_m, tiles_n, g.c_amax);
     return hipGetLastError() == hipSuccess ? 0 : 1;
 }
 

@@ -106,7 +106,8 @@ template <bool kTile>
 __global__ __launch_bounds__(256) void gemm_nv_fp16_kernel(
     const uint8_t *__restrict__ A, const uint8_t *__restrict__ As, const float *__restrict__ Ats,
     const uint8_t *__restrict__ B, const uint8_t *__restrict__ Bs, const float *__restrict__ Bts, int M, int N, int K,
-    float alpha, void *__restrict__ C, int64_t ldc, int c_bf16, int vec_ok, int tiles_m, int tiles_n)
+    float alpha, void *__restrict__ C, int64_t ldc, int c_bf16, int vec_ok, int tiles_m, int tiles_n,
+    uint32_t *__restrict__ c_amax)
 {
     using namespace gemm;
     // global domain: 256 x 256 tiles, wave blocks 128 x 128; per-tile domain:
@@ -363,10 +364,10 @@ __global__ __launch_bounds__(256) void gemm_nv_fp16_kernel(
         asm volatile("v_mov_b32 %0, %1" : "=v"(el) : "v"(lane));
         if constexpr (kTile)
             store_wave_block_any<NJ>(tot, ep, el, tm0 + wm * 128, tn0 + wn * (32 * NJ), M, N, alpha, C, ldc,
-                                     c_bf16 != 0, vec_ok != 0);
+                                     c_bf16 != 0, vec_ok != 0, c_amax);
         else
             store_wave_block_any<NJ>(acc, ep, el, tm0 + wm * 128, tn0 + wn * (32 * NJ), M, N,
-                                     alpha * (Ats[0] * Bts[0]), C, ldc, c_bf16 != 0, vec_ok != 0);
+                                     alpha * (Ats[0] * Bts[0]), C, ldc, c_bf16 != 0, vec_ok != 0, c_amax);
         if (next >= ntiles) break;
         tile = next;
     }
@@ -399,10 +400,10 @@ int launch_gemm_nv(const GemmArgs &g, hipStream_t st)
     const int grid = min(tiles_m * tiles_n, cus);
     if (tile)
         hipLaunchKernelGGL(gemm_nv_fp16_kernel<true>, dim3(grid), dim3(256), 0, st, a, as, g.a_ts, b, bs, g.b_ts, M, N,
-                           K, g.alpha, g.c, g.ldc, (int)g.c_bf16, vec_ok, tiles_m, tiles_n);
+                           K, g.alpha, g.c, g.ldc, (int)g.c_bf16, vec_ok, tiles_m, tiles_n, g.c_amax);
     else
         hipLaunchKernelGGL(gemm_nv_fp16_kernel<false>, dim3(grid), dim3(256), 0, st, a, as, g.a_ts, b, bs, g.b_ts, M, N,
-                           K, g.alpha, g.c, g.ldc, (int)g.c_bf16, vec_ok, tiles_m, tiles_n);
+                           K, g.alpha, g.c, g.ldc, (int)g.c_bf16, vec_ok, tiles_m, tiles_n, g.c_amax);
     return hipGetLastError() == hipSuccess ? 0 : 1;
 }
 

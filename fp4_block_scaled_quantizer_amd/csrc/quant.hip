@@ -720,7 +720,8 @@ int launch_quant_mx(const QuantArgs &a, hipStream_t st)
 
 size_t nv_workspace_bytes(int domain) { return domain == 0 ? (size_t)kAmaxBlocks * sizeof(uint32_t) : 0; }
 
-int launch_quant_nv(const QuantArgs &a, int domain, float *tensor_scale, void *workspace, hipStream_t st)
+int launch_quant_nv(const QuantArgs &a, int domain, float *tensor_scale, void *workspace, const float *given_amax,
+                    hipStream_t st)
 {
     const uint32_t seed_lo = (uint32_t)a.seed, seed_hi = (uint32_t)(a.seed >> 32);
     const uint32_t R = (uint32_t)a.rows, K = (uint32_t)a.cols;
@@ -729,13 +730,23 @@ int launch_quant_nv(const QuantArgs &a, int domain, float *tensor_scale, void *w
     auto *scales = reinterpret_cast<uint8_t *>(a.scales);
     if (domain == 0) {
         const uint64_t nchunks = (uint64_t)R * (K >> 3);
-        auto *partial = reinterpret_cast<uint32_t *>(workspace);
-        uint32_t np = (uint32_t)((nchunks + kThreads - 1) / kThreads);
-        if (np > (uint32_t)kAmaxBlocks) np = kAmaxBlocks;
-        if (np == 0) np = 1;
-        // pass 1 (also runs for an empty operand so that S = 1 is written)
-        hipLaunchKernelGGL(nv_amax_partial_kernel, dim3(np), dim3(kThreads), 0, st, x, K, (uint32_t)a.ld,
-                           (uint32_t)nchunks, partial);
+        const uint32_t *partial;
+        uint32_t np;
+        if (given_amax) {
+            // single pass: the caller supplies the domain amax (binary32; its
+            // bits are the one "partial maximum")
+            partial = reinterpret_cast<const uint32_t *>(given_amax);
+            np = 1;
+        } else {
+            auto *part = reinterpret_cast<uint32_t *>(workspace);
+            np = (uint32_t)((nchunks + kThreads - 1) / kThreads);
+            if (np > (uint32_t)kAmaxBlocks) np = kAmaxBlocks;
+            if (np == 0) np = 1;
+            // pass 1 (also runs for an empty operand so that S = 1 is written)
+            hipLaunchKernelGGL(nv_amax_partial_kernel, dim3(np), dim3(kThreads), 0, st, x, K, (uint32_t)a.ld,
+                               (uint32_t)nchunks, part);
+            partial = part;
+        }
         const uint32_t grid = (uint32_t)((nchunks + kThreads * kChunksPerThread - 1) / (kThreads * kChunksPerThread));
         const uint32_t g = grid == 0 ? 1 : grid;
         if (a.sr)

@@ -215,6 +215,37 @@ FP4Q_API fp4q_status fp4_gemm_nv(const void *a_codes, const void *a_scales, cons
                         int64_t M, int64_t N, int64_t K, float alpha, int layout, void *c, int c_type,
                         int64_t ldc, void *stream);
 
+/* The GEMMs above, also reporting max |C| for a following NVFP4 "global
+ * nvfp" quantization of C, so that it needs no amax pass over C (the amax is
+ * produced by the op before the quantizer: [Fusion] section "The Design
+ * Philosophy of Format-Aware Fusion", the global nvfp scenario; [Stack]
+ * section "NVFP4 is more than a 4-bit value": the FP32 tensor scale comes
+ * from the tensor's amax).  c_amax: one device float, 4-byte aligned, not
+ * inside C; the epilogue folds max |C| over the values it stores, as stored
+ * (after the bf16 rounding), into *c_amax with an atomic max: initialize it
+ * to 0 (or to a running maximum) before the call.  The result is then
+ * exactly the amax fp4_quantize_nv computes for a bf16 C.  NaN or Inf in C
+ * give an unspecified *c_amax.  Otherwise identical to fp4_gemm_mx /
+ * fp4_gemm_nv; FP4Q_EINVAL if c_amax is null or overlaps C. */
+FP4Q_API fp4q_status fp4_gemm_mx_amax(const void *a_codes, const void *a_scales, const void *b_codes,
+                             const void *b_scales, int64_t M, int64_t N, int64_t K, float alpha, int layout,
+                             void *c, int c_type, int64_t ldc, float *c_amax, void *stream);
+FP4Q_API fp4q_status fp4_gemm_nv_amax(const void *a_codes, const void *a_scales, const float *a_tensor_scale,
+                             const void *b_codes, const void *b_scales, const float *b_tensor_scale, int domain,
+                             int64_t M, int64_t N, int64_t K, float alpha, int layout, void *c, int c_type,
+                             int64_t ldc, float *c_amax, void *stream);
+
+/* NVFP4 "global nvfp" producer in one pass: the domain amax is read from
+ * `amax` (a device float, e.g. written by fp4_gemm_*_amax for this x)
+ * instead of being computed from x.  With *amax == max |x| every output byte
+ * equals fp4_quantize_nv(..., FP4Q_NV_GLOBAL, ...)'s; another finite value >= 0 gives
+ * the codes of the tensor scale S = *amax / 2688.  Along rows, linear layout;
+ * requires cols % 16 == 0.  Errors as fp4_quantize_nv, plus FP4Q_EINVAL for
+ * a null or overlapping `amax`, FP4Q_EALIGN if it is not 4-byte aligned. */
+FP4Q_API fp4q_status fp4_quantize_nv_amax(const void *x, int64_t rows, int64_t cols, int64_t ld_x, int round,
+                                 uint64_t seed, uint32_t stream_id, const float *amax, void *codes, void *scales,
+                                 float *tensor_scale, void *stream);
+
 /* Human-readable text for a status code (static storage). */
 FP4Q_API const char *fp4q_status_str(int status);
 

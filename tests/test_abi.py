@@ -26,7 +26,8 @@ def lib():
 def test_exports_every_declared_function():
     names = B.declared_functions()
     assert set(names) >= {"fp4_quantize_mx", "fp4_quantize_nv", "fp4_hadamard32_quantize", "fp4_quantize_mx_dual",
-                          "fp4_gemm_mx", "fp4_gemm_nv"}
+                          "fp4_quantize_nv_amax", "fp4_gemm_mx", "fp4_gemm_nv", "fp4_gemm_mx_amax",
+                          "fp4_gemm_nv_amax"}
     for n in names:
         assert hasattr(L, n), n
     assert B.abi_version() == 1
@@ -168,3 +169,27 @@ def test_quantize_mx_dual_status_codes():
     assert q_dual(codes_r=X + 64) == B.EINVAL            # output overlaps input
     assert q_dual(rows=0) == B.OK                        # empty: nothing enqueued
     assert q_dual(cols=0, ld=0) == B.OK
+
+
+AMAX = 0x7F8000000000
+
+
+def test_amax_entry_points_status_codes():
+    def g_mx(amax=AMAX, c=C):
+        return L.fp4_gemm_mx_amax(CODES, SCALES, CODES2, SCALES2, 64, 64, 128, 1.0, 0, c, 1, 64, amax, None)
+
+    def g_nv(amax=AMAX, c=C):
+        return L.fp4_gemm_nv_amax(CODES, SCALES, TS, CODES2, SCALES2, TS + 64, 0, 64, 64, 128, 1.0, 0, c, 1, 64,
+                                  amax, None)
+
+    def q_nv1(amax=AMAX, cols=64):
+        return L.fp4_quantize_nv_amax(X, 64, cols, 64, 0, 7, 0, amax, CODES, SCALES, TS, None)
+
+    for g in (g_mx, g_nv):
+        assert g(amax=None) == B.EINVAL
+        assert g(amax=AMAX + 2) == B.EALIGN
+        assert g(amax=C + 64) == B.EINVAL        # inside C
+    assert q_nv1(amax=None) == B.EINVAL
+    assert q_nv1(amax=AMAX + 1) == B.EALIGN
+    assert q_nv1(amax=CODES + 16) == B.EINVAL    # overlaps an output
+    assert q_nv1(cols=24) == B.ESHAPE            # K % 16
