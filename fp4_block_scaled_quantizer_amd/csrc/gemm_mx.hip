@@ -13,18 +13,22 @@
 // 32 x 32 x 64 block per instruction and applies one E8M0 scale per lane:
 // lane l supplies row (l mod 32), K elements 32*(l/32) .. +31 (16 bytes, low
 // nibble = lower K) and the scale byte of exactly that 32-element block.  An
-// MX block of the linear layout is therefore one lane's operand, and its
-// scale byte is that lane's scale.  The accumulator holds
-// D[8*(i/4) + 4*(l/32) + i%4][l mod 32] in register i of lane l.
+// MX block is therefore one lane's operand, and its scale byte is that
+// lane's scale.  The B fragment is passed as the instruction's first
+// operand, so register i of lane l holds C[row l mod 32][column
+// 8*(i/4) + 4*(l/32) + i%4] of its 32 x 32 block: each group of four
+// registers is four consecutive columns of one row.
 //
-// Tiling: a 256-thread workgroup owns a 256 x 256 tile of C (four waves, each
-// 128 x 128 = 4 x 4 instructions, 256 fp32 accumulators per lane), walks K in
-// steps of 128 and double-buffers the A and B code slices in LDS (rows padded
-// from 64 to 80 bytes so the 16-byte fragment reads of 16 consecutive rows hit
-// distinct banks).  Scales go straight from global memory to registers (one
-// 32-bit load covers the 4 blocks of a 128-wide step).  Tiles are numbered so
-// that each of the 8 XCDs works on a contiguous group of tile rows and shares
-// A and B slices through its own L2.
+// Structure: one 256-thread workgroup per CU (a persistent grid) walks
+// 256 x 256 tiles of C in an XCD-aware order; each wave owns 128 x 128
+// (4 x 4 instructions, 256 fp32 accumulators per lane).  K runs in 128-wide
+// steps through a four-slot LDS ring filled by LDS DMA (global_load_lds)
+// three steps ahead: in the tiled layout every 1 KiB block of codes is one
+// instruction's operand in lane order, copied as is, and the scale words are
+// copied with rows permuted so that a wave reads its four words of a step in
+// one 16-byte LDS read.  The next tile's first steps are put in flight
+// before the finished tile's epilogue (gemm_common.h) runs.  The linear
+// layout takes the same kernel with per-lane DMA addresses.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 

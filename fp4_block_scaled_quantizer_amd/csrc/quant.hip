@@ -1,5 +1,6 @@
 // quant.hip -- FP4 quantization producers for gfx950 (MXFP4, MXFP4 with the
-// fixed-sign Hadamard-32, NVFP4 global and per-128x128-tile domains).
+// fixed-sign Hadamard-32, the dual-output MX producer, NVFP4 global -- two
+// passes, or one with a given amax -- and per-128x128-tile domains).
 //
 // Pages cited (titles as printed):
 //   [Fusion] "Format-Aware Fusion: The Engineering Practice That Doubles FP4
@@ -17,7 +18,10 @@
 // load of bf16, one 4-byte store of codes).  Four lanes make an MX block of 32
 // and two lanes an NV block of 16; block maxima are combined with cross-lane
 // exchanges inside the wavefront.  Consecutive lanes read consecutive 16-byte
-// chunks, so every wavefront load is a contiguous 1 KiB.
+// chunks, so every wavefront load is a contiguous 1 KiB.  In the tiled
+// (consumer) layout a workgroup assembles whole 1 KiB matrix-core blocks in
+// LDS and writes them out contiguously; along columns a 128 x 128 tile is
+// staged in LDS and transposed there.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
