@@ -338,13 +338,18 @@ def read_traffic(kernel, workload):
 
 def source_hash(paths):
     """SHA-256 (first 16 hex digits) of the kernel's source files, concatenated
-    in the order given."""
+    in the order given, with comments, blank lines and indentation removed
+    (a change to the comments does not invalidate the counters)."""
     import hashlib
+    import re
 
     h = hashlib.sha256()
     for p in paths:
-        with open(os.path.join(ROOT, p.strip()), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, p.strip())) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        h.update("\n".join(ln.strip() for ln in text.splitlines() if ln.strip()).encode())
     return h.hexdigest()[:16]
 
 
