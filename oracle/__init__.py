@@ -69,6 +69,7 @@ def _load():
     sig("oc_nv_tensor_scale", ctypes.c_float, ctypes.c_float)
     sig("oc_nv_block_scale", ctypes.c_uint8, ctypes.c_float, ctypes.c_float)
     sig("oc_quantize_nv", i32, u16p, i64, i64, i64, i32, i32, u64, u32, i32, u8p, u8p, f32p)
+    sig("oc_hadamard32_quantize_nv", i32, u16p, i64, i64, i64, i32, u32, i32, u64, u32, i32, u8p, u8p, f32p)
     sig("oc_dequant_mx", None, u8p, u8p, i64, i64, f64p)
     sig("oc_dequant_nv", None, u8p, u8p, f32p, i32, i64, i64, f64p)
     sig("oc_gemm_bruteforce", None, f64p, f64p, i64, i64, i64, ctypes.c_double, f64p, f64p)
@@ -205,6 +206,24 @@ def quantize_nv(x, cols=None, axis=AXIS_ROWS, sr=False, seed=0, stream=0, domain
                                 _ptr(ts, ctypes.c_float))
     if st != 0:
         raise OracleInputError(f"oc_quantize_nv status {st}")
+    return codes, scales, ts
+
+
+def hadamard32_quantize_nv(x, sign_mask, cols=None, axis=AXIS_COLS, sr=False, seed=0, stream=0, domain=NV_GLOBAL):
+    """Fixed-sign Hadamard-32 along K, then NVFP4 (K % 32 == 0); outputs as
+    quantize_nv."""
+    x = _as_bf16_bits(x)
+    rows, ld = x.shape
+    cols = ld if cols is None else cols
+    R, K = _logical_shape(x, cols, axis)
+    codes = np.zeros((R, K // 2), dtype=np.uint8)
+    scales = np.zeros((R, K // 16), dtype=np.uint8)
+    ts = np.zeros(nv_tensor_scale_shape(R, K, domain), dtype=np.float32)
+    st = _load().oc_hadamard32_quantize_nv(_ptr(x, ctypes.c_uint16), rows, cols, ld, axis, sign_mask & 0xFFFFFFFF,
+                                           int(bool(sr)), seed, stream, domain, _ptr(codes, ctypes.c_uint8),
+                                           _ptr(scales, ctypes.c_uint8), _ptr(ts, ctypes.c_float))
+    if st != 0:
+        raise OracleInputError(f"oc_hadamard32_quantize_nv status {st}")
     return codes, scales, ts
 
 

@@ -352,31 +352,40 @@ static void nv_block(const float v[16], uint8_t sb, float S, int sr, uint64_t se
         codes_out[t] = (uint8_t)(c[2 * t] | (c[2 * t + 1] << 4));
 }
 
-/* domain: 0 = one tensor scale for the whole operand ("global nvfp");
+/* Shared driver for oc_quantize_nv and oc_hadamard32_quantize_nv.
+ * domain: 0 = one tensor scale for the whole operand ("global nvfp");
  *         1 = one tensor scale per 128 x 128 tile of the logical [R x K]
  *             operand ("CTA-local nvfp"); edge tiles are their own domains.
  * tensor_scale receives 1 float (global) or ceil(R/128) x ceil(K/128) floats
- * (row-major). */
-int oc_quantize_nv(const uint16_t *x, int64_t rows, int64_t cols, int64_t ld, int axis, int sr,
-                   uint64_t seed, uint32_t stream, int domain, uint8_t *codes, uint8_t *scales,
-                   float *tensor_scale)
+ * (row-major).  The logical operand is first materialized in binary32 (the
+ * bf16 values widened, exactly; with hadamard set, each 32-element block
+ * along K then transformed by oc_hadamard32), so that the domain amax, the
+ * block amax and the codes all see the same values. */
+static int quantize_nv_impl(const uint16_t *x, int64_t rows, int64_t cols, int64_t ld, int axis, int hadamard,
+                            uint32_t sign_mask, int sr, uint64_t seed, uint32_t stream, int domain,
+                            uint8_t *codes, uint8_t *scales, float *tensor_scale)
 {
     int64_t R = axis == 0 ? rows : cols;
     int64_t K = axis == 0 ? cols : rows;
-    if (K % 16 != 0) return 2;
-    for (int64_t r = 0; r < R; ++r)
-        for (int64_t k = 0; k < K; ++k)
-            if (!isfinite(fetch(x, ld, axis, r, k))) return 1;
+    if (K % (hadamard ? 32 : 16) != 0) return 2;
+    float *v = (float *)malloc((size_t)(R * K > 0 ? R * K : 1) * sizeof(float));
+    if (!v) return 3;
+    for (int64_t r = 0; r < R; ++r) {
+        for (int64_t k = 0; k < K; ++k) v[r * K + k] = fetch(x, ld, axis, r, k);
+        if (hadamard)
+            for (int64_t j = 0; j < K / 32; ++j) oc_hadamard32(v + r * K + 32 * j, sign_mask);
+    }
+    for (int64_t i = 0; i < R * K; ++i)
+        if (!isfinite(v[i])) { free(v); return 1; }
     int64_t TR = (R + 127) / 128, TK = (K + 127) / 128;
     /* domain amax, then the domain's tensor scale */
     if (domain == 0) {
         float A = 0.0f;
-        for (int64_t r = 0; r < R; ++r)
-            for (int64_t k = 0; k < K; ++k) {
-                float a = fabsf(fetch(x, ld, axis, r, k));
-                if (a > A) A = a;
-            }
-        if (A != 0.0f && A < 0x1p-100f) return 1; /* degenerate domain, outside the contract */
+        for (int64_t i = 0; i < R * K; ++i) {
+            float a = fabsf(v[i]);
+            if (a > A) A = a;
+        }
+        if (A != 0.0f && A < 0x1p-100f) { free(v); return 1; } /* degenerate domain, outside the contract */
         tensor_scale[0] = oc_nv_tensor_scale(A);
     } else {
         for (int64_t tr = 0; tr < TR; ++tr)
@@ -384,29 +393,48 @@ int oc_quantize_nv(const uint16_t *x, int64_t rows, int64_t cols, int64_t ld, in
                 float A = 0.0f;
                 for (int64_t r = 128 * tr; r < R && r < 128 * tr + 128; ++r)
                     for (int64_t k = 128 * tk; k < K && k < 128 * tk + 128; ++k) {
-                        float a = fabsf(fetch(x, ld, axis, r, k));
+                        float a = fabsf(v[r * K + k]);
                         if (a > A) A = a;
                     }
-                if (A != 0.0f && A < 0x1p-100f) return 1;
+                if (A != 0.0f && A < 0x1p-100f) { free(v); return 1; }
                 tensor_scale[tr * TK + tk] = oc_nv_tensor_scale(A);
             }
     }
     for (int64_t r = 0; r < R; ++r) {
         for (int64_t j = 0; j < K / 16; ++j) {
             float S = domain == 0 ? tensor_scale[0] : tensor_scale[(r / 128) * TK + (16 * j) / 128];
-            float v[16];
+            const float *blk = v + r * K + 16 * j;
             float b = 0.0f;
             for (int i = 0; i < 16; ++i) {
-                v[i] = fetch(x, ld, axis, r, 16 * j + i);
-                float a = fabsf(v[i]);
+                float a = fabsf(blk[i]);
                 if (a > b) b = a;
             }
             uint8_t sb = oc_nv_block_scale(b, S);
             scales[r * (K / 16) + j] = sb;
-            nv_block(v, sb, S, sr, seed, stream, (uint32_t)r, (uint32_t)(16 * j), codes + r * (K / 2) + 8 * j);
+            nv_block(blk, sb, S, sr, seed, stream, (uint32_t)r, (uint32_t)(16 * j), codes + r * (K / 2) + 8 * j);
         }
     }
+    free(v);
     return 0;
+}
+
+int oc_quantize_nv(const uint16_t *x, int64_t rows, int64_t cols, int64_t ld, int axis, int sr,
+                   uint64_t seed, uint32_t stream, int domain, uint8_t *codes, uint8_t *scales,
+                   float *tensor_scale)
+{
+    return quantize_nv_impl(x, rows, cols, ld, axis, 0, 0u, sr, seed, stream, domain, codes, scales, tensor_scale);
+}
+
+/* The fixed-sign Hadamard-32 ([Fusion], section "Two Key Numerical
+ * Techniques") ahead of NVFP4: the transform runs along K in 32-element
+ * blocks (two NV blocks each), as on the MX path, and the NV steps then apply
+ * to the transformed values (K % 32 == 0). */
+int oc_hadamard32_quantize_nv(const uint16_t *x, int64_t rows, int64_t cols, int64_t ld, int axis,
+                              uint32_t sign_mask, int sr, uint64_t seed, uint32_t stream, int domain,
+                              uint8_t *codes, uint8_t *scales, float *tensor_scale)
+{
+    return quantize_nv_impl(x, rows, cols, ld, axis, 1, sign_mask, sr, seed, stream, domain, codes, scales,
+                            tensor_scale);
 }
 
 /* ------------------------------------------------------------------ */

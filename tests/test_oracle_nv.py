@@ -114,3 +114,48 @@ def test_nv_rejects_out_of_contract():
         oracle.quantize_nv(x)
     with pytest.raises(oracle.OracleInputError):
         oracle.quantize_nv(np.zeros((1, 24), dtype=np.uint16))
+
+
+def _small_int_bf16(rows, cols, seed):
+    """bf16 bits of integers in [-3, 3]: every Hadamard-32 output is an
+    integer of magnitude <= 96, exact in bf16."""
+    rng = np.random.default_rng(seed)
+    v = rng.integers(-3, 4, size=(rows, cols)).astype(np.float32)
+    return sf.f32_to_bf16_bits_rne(v)
+
+
+@pytest.mark.parametrize("axis", [0, 1])
+@pytest.mark.parametrize("domain", [0, 1])
+@pytest.mark.parametrize("sr", [False, True])
+def test_hadamard_nv_equals_explicit_transform_then_nv(axis, domain, sr):
+    # the transform through the explicit Sylvester matrix (float64, exact on
+    # these inputs), the result as bf16 rows of the logical operand, then the
+    # plain NVFP4 oracle: same codes, block scales and tensor scales
+    rows, cols = (160, 96) if axis == 0 else (96, 160)
+    x = _small_int_bf16(rows, cols, 30 + axis)
+    mask = synth.sign_mask(11)
+    codes, scales, ts = oracle.hadamard32_quantize_nv(x, mask, axis=axis, sr=sr, seed=5, stream=3, domain=domain)
+    logical = sf.bf16_to_f32(x if axis == 0 else np.ascontiguousarray(x.T)).astype(np.float64)
+    H = sf.sylvester_hadamard(32).astype(np.float64)
+    d = np.array([-1.0 if (mask >> i) & 1 else 1.0 for i in range(32)])
+    R, K = logical.shape
+    blocks = logical.reshape(R, K // 32, 32) * d
+    t = np.einsum("ij,rbj->rbi", H, blocks).reshape(R, K)
+    assert np.array_equal(t, np.round(t)) and np.abs(t).max() <= 256
+    tb = sf.f32_to_bf16_bits_rne(t.astype(np.float32))
+    c2, s2, t2 = oracle.quantize_nv(tb, sr=sr, seed=5, stream=3, domain=domain)
+    assert np.array_equal(codes, c2) and np.array_equal(scales, s2)
+    assert np.array_equal(ts.view(np.uint32), t2.view(np.uint32))
+
+
+def test_hadamard_nv_mask_flip_negates_and_needs_k32():
+    x = synth.bf16_bits(synth.grad_student_t3(64, 96, 33))
+    for domain in (0, 1):
+        c0, s0, t0 = oracle.hadamard32_quantize_nv(x, 0, axis=oracle.AXIS_COLS, domain=domain)
+        c1, s1, t1 = oracle.hadamard32_quantize_nv(x, 0xFFFFFFFF, axis=oracle.AXIS_COLS, domain=domain)
+        assert np.array_equal(s0, s1) and np.array_equal(t0, t1)
+        d0 = oracle.dequant_nv(c0, s0, t0, domain)
+        d1 = oracle.dequant_nv(c1, s1, t1, domain)
+        assert np.array_equal(d1, -d0)
+    with pytest.raises(oracle.OracleInputError):
+        oracle.hadamard32_quantize_nv(np.zeros((16, 48), dtype=np.uint16), 0, axis=oracle.AXIS_ROWS)
