@@ -49,7 +49,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="qkv",
                     choices=["qkv", "mlp", "backward", "backward_dual", "dual_x", "nvfp4_global", "nvfp4_tile",
-                             "nvfp4_chain", "nvfp4_chain_2pass", "copy"],
+                             "nvfp4_chain", "nvfp4_chain_2pass", "nvfp4_wgrad", "copy"],
                     help="copy = a plain 1 GiB device copy: the HBM reference for counter scaling")
     ap.add_argument("--copies", type=int, default=4, help="input copies rotated across steps (cold producers)")
     ap.add_argument("--layout", default="tiled", choices=["tiled", "linear"],
@@ -225,6 +225,41 @@ def build_workload(name, dev, copies, layout_name="tiled"):
                            (", dY's two operands from one read (dual producer)" if dual else ""),
                "dgrad_mnk": [T, I, O], "wgrad_mnk": [O, I, T], "layout": layout_name, "input_copies": copies}
         return cfg, ops, 2.0 * T * I * O * 2
+    if name == "nvfp4_wgrad":
+        # the o_proj weight gradient in NVFP4 (per-tile domain): dY^T and X^T
+        # quantized along tokens with the fixed-sign Hadamard (SR on dY), then
+        # dW = (1/32) dY^T X
+        dY = gen("backward", "dY", copies)
+        X = gen("backward", "X", copies)
+        T, O = dY[0].shape
+        I = X[0].shape[1]
+        mask = synth.sign_mask(synth.HADAMARD_MASK_SEED)
+        D = B.NV_TILE128
+
+        def nvbufs(R, Kc):
+            return (torch.empty((R, Kc // 2), dtype=torch.uint8, device=dev),
+                    torch.empty((R, Kc // 16), dtype=torch.uint8, device=dev),
+                    torch.empty(B.nv_tensor_scale_shape(R, Kc, D), dtype=torch.float32, device=dev))
+
+        bd, bx = nvbufs(O, T), nvbufs(I, T)
+        dW = torch.empty((O, I), dtype=torch.float32, device=dev)
+        ops = [
+            ("Hadamard-quantize dY^T (NVFP4 tile, SR)", "nv_quant_cols_kernel",
+             lambda s: B.fp4_quantize_nv(dY[s % copies], D, axis=B.ALONG_COLS, round=B.SR, seed=synth.SR_SEED,
+                                         stream_id=1, hadamard_mask=mask, codes=bd[0], scales=bd[1],
+                                         tensor_scale=bd[2]),
+             T * O * NV_TILE_BYTES_PER_ELEM, "GB/s", HBM_PEAK_GBS, "hbm"),
+            ("Hadamard-quantize X^T (NVFP4 tile)", "nv_quant_cols_kernel",
+             lambda s: B.fp4_quantize_nv(X[s % copies], D, axis=B.ALONG_COLS, hadamard_mask=mask, codes=bx[0],
+                                         scales=bx[1], tensor_scale=bx[2]),
+             T * I * NV_TILE_BYTES_PER_ELEM, "GB/s", HBM_PEAK_GBS, "hbm"),
+            ("GEMM NVFP4 wgrad dY^T X (alpha 1/32)", "gemm_nv_fp16_kernel",
+             lambda s: B.fp4_gemm_nv(*bd, *bx, D, alpha=1.0 / 32, c=dW), 2.0 * O * I * T, "TFLOP/s",
+             BF16_PEAK_TFLOPS, "mfma"),
+        ]
+        cfg = {"workload": "Llama-3-8B o_proj weight gradient, NVFP4 per-128x128-tile domain, fixed-sign Hadamard-32 "
+                           "along tokens, SR on dY", "wgrad_mnk": [O, I, T], "input_copies": copies}
+        return cfg, ops, 2.0 * O * I * T
     if name in ("nvfp4_chain", "nvfp4_chain_2pass"):
         # two NVFP4 GEMMs in a row (Llama-3-8B MLP up and down shapes, global
         # domain): the first GEMM's output is the second's A operand.  In

@@ -66,8 +66,11 @@ def lib() -> ctypes.CDLL:
     L.fp4_gemm_mx_amax.argtypes = [vp, vp, vp, vp, i64, i64, i64, f32, i32, vp, i32, i64, vp, vp]
     L.fp4_gemm_nv_amax.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, i64, i64, f32, i32, vp, i32, i64, vp, vp]
     L.fp4_quantize_nv_amax.argtypes = [vp, i64, i64, i64, i32, u64, u32, vp, vp, vp, vp, vp]
+    L.fp4_hadamard32_quantize_nv.argtypes = [vp, i64, i64, i64, i32, u32, i32, u64, u32, i32, vp, vp, vp, vp,
+                                             ctypes.c_size_t, i32, vp]
     for fn in ("fp4_quantize_mx", "fp4_hadamard32_quantize", "fp4_quantize_mx_dual", "fp4_quantize_nv",
-               "fp4_quantize_nv_amax", "fp4_gemm_mx", "fp4_gemm_nv", "fp4_gemm_mx_amax", "fp4_gemm_nv_amax"):
+               "fp4_quantize_nv_amax", "fp4_hadamard32_quantize_nv", "fp4_gemm_mx", "fp4_gemm_nv",
+               "fp4_gemm_mx_amax", "fp4_gemm_nv_amax"):
         getattr(L, fn).restype = i32
     L.fp4q_status_str.argtypes = [i32]
     L.fp4q_status_str.restype = ctypes.c_char_p
@@ -190,9 +193,12 @@ def nv_tensor_scale_shape(R: int, K: int, domain: int):
 def fp4_quantize_nv(x: torch.Tensor, domain: int = NV_GLOBAL, *, cols: Optional[int] = None, axis: int = ALONG_ROWS,
                     round: int = RNE, seed: int = 0, stream_id: int = 0, codes: Optional[torch.Tensor] = None,
                     scales: Optional[torch.Tensor] = None, tensor_scale: Optional[torch.Tensor] = None,
-                    workspace: Optional[torch.Tensor] = None, amax: Optional[torch.Tensor] = None, stream=None):
+                    workspace: Optional[torch.Tensor] = None, amax: Optional[torch.Tensor] = None,
+                    hadamard_mask: Optional[int] = None, stream=None):
     """NVFP4; with `amax` (a device float32 tensor holding max |x|, global
-    domain only) the producer runs in one pass (fp4_quantize_nv_amax)."""
+    domain only) the producer runs in one pass (fp4_quantize_nv_amax); with
+    `hadamard_mask` the fixed-sign Hadamard-32 runs first
+    (fp4_hadamard32_quantize_nv, along columns)."""
     rows, cols, ld = _input(x, cols)
     R, K = _logical(rows, cols, axis)
     if codes is None:
@@ -213,6 +219,13 @@ def fp4_quantize_nv(x: torch.Tensor, domain: int = NV_GLOBAL, *, cols: Optional[
     if workspace is None and need > 0:
         workspace = torch.empty((need,), dtype=torch.uint8, device=x.device)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if hadamard_mask is not None:
+        _check("fp4_hadamard32_quantize_nv",
+               lib().fp4_hadamard32_quantize_nv(x.data_ptr(), rows, cols, ld, axis, hadamard_mask & 0xFFFFFFFF, round,
+                                                seed, stream_id, domain, codes.data_ptr(), scales.data_ptr(),
+                                                tensor_scale.data_ptr(), _ptr(workspace), wbytes, LAYOUT_LINEAR,
+                                                _stream(stream)))
+        return codes, scales, tensor_scale
     _check("fp4_quantize_nv",
            lib().fp4_quantize_nv(x.data_ptr(), rows, cols, ld, axis, round, seed, stream_id, domain,
                                  codes.data_ptr(), scales.data_ptr(), tensor_scale.data_ptr(), _ptr(workspace),

@@ -197,7 +197,7 @@ fp4q_status run_gemm_nv(const void *a_codes, const void *a_scales, const float *
 fp4q_status run_quantize_nv(const void *x, int64_t rows, int64_t cols, int64_t ld_x, int axis, int round,
                             uint64_t seed, uint32_t stream_id, int domain, void *codes, void *scales,
                             float *tensor_scale, void *workspace, size_t workspace_bytes, int layout,
-                            const float *given_amax, void *stream)
+                            const float *given_amax, bool hadamard, uint32_t sign_mask, void *stream)
 {
     if ((axis != FP4Q_ALONG_ROWS && axis != FP4Q_ALONG_COLS) || (round != FP4Q_RNE && round != FP4Q_SR) ||
         (domain != FP4Q_NV_GLOBAL && domain != FP4Q_NV_TILE128) ||
@@ -206,9 +206,10 @@ fp4q_status run_quantize_nv(const void *x, int64_t rows, int64_t cols, int64_t l
     if (layout == FP4Q_LAYOUT_TILED) return FP4Q_EUNSUPPORTED;
     if (rows < 0 || cols < 0 || ld_x < cols || rows > kMaxDim || cols > kMaxDim || ld_x > kMaxDim)
         return FP4Q_ESHAPE;
-    if (axis == FP4Q_ALONG_COLS) return FP4Q_EUNSUPPORTED;
-    const int64_t R = rows, K = cols;
-    if (K % 16 != 0) return FP4Q_ESHAPE;
+    if (hadamard && axis == FP4Q_ALONG_ROWS) return FP4Q_EUNSUPPORTED;
+    const int64_t R = axis == FP4Q_ALONG_ROWS ? rows : cols, K = axis == FP4Q_ALONG_ROWS ? cols : rows;
+    if (K % (hadamard ? 32 : 16) != 0) return FP4Q_ESHAPE;
+    if (axis == FP4Q_ALONG_COLS && cols % 4 != 0) return FP4Q_ESHAPE;
     if ((uint64_t)R * (uint64_t)(K / 8) >= (1ull << 32)) return FP4Q_ESHAPE;
     const bool empty = R == 0 || K == 0;
     if (empty && domain == FP4Q_NV_TILE128) return FP4Q_OK;  // no tiles, no tensor scales
@@ -238,6 +239,8 @@ fp4q_status run_quantize_nv(const void *x, int64_t rows, int64_t cols, int64_t l
     a.sr = round == FP4Q_SR;
     a.seed = seed;
     a.stream_id = stream_id;
+    a.hadamard = hadamard;
+    a.sign_mask = sign_mask;
     a.codes = codes;
     a.scales = scales;
     (void)hipGetLastError();
@@ -318,7 +321,16 @@ fp4q_status fp4_quantize_nv(const void *x, int64_t rows, int64_t cols, int64_t l
                             float *tensor_scale, void *workspace, size_t workspace_bytes, int layout, void *stream)
 {
     return run_quantize_nv(x, rows, cols, ld_x, axis, round, seed, stream_id, domain, codes, scales, tensor_scale,
-                           workspace, workspace_bytes, layout, nullptr, stream);
+                           workspace, workspace_bytes, layout, nullptr, false, 0u, stream);
+}
+
+fp4q_status fp4_hadamard32_quantize_nv(const void *x, int64_t rows, int64_t cols, int64_t ld_x, int axis,
+                                       uint32_t sign_mask, int round, uint64_t seed, uint32_t stream_id, int domain,
+                                       void *codes, void *scales, float *tensor_scale, void *workspace,
+                                       size_t workspace_bytes, int layout, void *stream)
+{
+    return run_quantize_nv(x, rows, cols, ld_x, axis, round, seed, stream_id, domain, codes, scales, tensor_scale,
+                           workspace, workspace_bytes, layout, nullptr, true, sign_mask, stream);
 }
 
 fp4q_status fp4_gemm_mx(const void *a_codes, const void *a_scales, const void *b_codes, const void *b_scales,
@@ -361,7 +373,7 @@ fp4q_status fp4_quantize_nv_amax(const void *x, int64_t rows, int64_t cols, int6
     if (!amax) return FP4Q_EINVAL;
     if (!aligned(amax, 4)) return FP4Q_EALIGN;
     return run_quantize_nv(x, rows, cols, ld_x, FP4Q_ALONG_ROWS, round, seed, stream_id, FP4Q_NV_GLOBAL, codes,
-                           scales, tensor_scale, nullptr, 0, FP4Q_LAYOUT_LINEAR, amax, stream);
+                           scales, tensor_scale, nullptr, 0, FP4Q_LAYOUT_LINEAR, amax, false, 0u, stream);
 }
 
 const char *fp4q_status_str(int status)

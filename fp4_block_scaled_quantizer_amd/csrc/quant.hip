@@ -652,6 +652,164 @@ __global__ __launch_bounds__(kThreads) void nv_quant_tile_kernel(const uint16_t 
     }
 }
 
+// ------------------------------------------------------------------
+// NVFP4 along columns (the logical operand is x^T; optionally the fixed-sign
+// Hadamard-32 along K first).  A workgroup owns one 128 x 128 tile of x,
+// i.e. one 128 x 128 tile of the logical operand: exactly one per-tile scale
+// domain.  The tile is staged in LDS as in the MX column kernel; thread t
+// then holds two adjacent columns (output rows) x 32 rows (K) in registers:
+// two 16-element NV blocks per column.
+//   kMode 0, per-tile domain: tile amax (of the transformed values with
+//            Hadamard) by a workgroup reduction -> S -> quantize.
+//   kMode 1, global domain: S from the partial maxima -> quantize.
+//   kMode 2, global domain with Hadamard, pass 1: the amax of the
+//            transformed values of tiles blockIdx.x, + gridDim.x, ... into
+//            partial[blockIdx.x].
+// Requires cols % 4 == 0 and rows % 16 == 0 (rows % 32 == 0 with Hadamard).
+// ------------------------------------------------------------------
+template <bool kSR, bool kHad, int kMode>
+__global__ __launch_bounds__(kThreads) void nv_quant_cols_kernel(const uint16_t *__restrict__ x, uint32_t rows,
+                                                                 uint32_t cols, uint32_t ld,
+                                                                 uint8_t *__restrict__ codes,
+                                                                 uint8_t *__restrict__ scales,
+                                                                 float *__restrict__ tensor_scale,
+                                                                 uint32_t *__restrict__ partial, uint32_t npartial,
+                                                                 uint32_t seed_lo, uint32_t seed_hi,
+                                                                 uint32_t stream_id, uint32_t sign_mask)
+{
+    __shared__ __attribute__((aligned(16))) uint8_t tile[kColTile * kColPitch];
+    __shared__ uint32_t sh[kThreads / 64];
+    const int t = threadIdx.x;
+    const uint32_t tiles_c = (cols + kColTile - 1) / kColTile, tiles_r = (rows + kColTile - 1) / kColTile;
+    const uint32_t ntile = tiles_c * tiles_r;
+    uint32_t run_max = 0;  // kMode 2: over this workgroup's tiles
+    for (uint32_t tt = blockIdx.x; tt < ntile; tt += (kMode == 2 ? gridDim.x : ntile)) {
+        const uint32_t c0 = (tt % tiles_c) * kColTile, r0 = (tt / tiles_c) * kColTile;
+        if (kMode == 2 && tt != blockIdx.x) __syncthreads();  // the previous tile's LDS reads are done
+        {
+            const uint32_t ch = t & 15, rr = t >> 4, c = c0 + ch * 8;
+            uint4 q[8];
+#pragma unroll
+            for (int p = 0; p < 8; ++p) {
+                const uint32_t r = r0 + p * 16 + rr;
+                q[p] = make_uint4(0u, 0u, 0u, 0u);
+                if (r < rows) {
+                    const uint16_t *src = x + (size_t)r * ld + c;
+                    if (c + 8 <= cols) {
+                        q[p] = load_nt16(src);
+                    } else if (c + 4 <= cols) {
+                        const uint2 h = load_nt8(src);
+                        q[p] = make_uint4(h.x, h.y, 0u, 0u);
+                    }
+                }
+            }
+#pragma unroll
+            for (int p = 0; p < 8; ++p) *reinterpret_cast<uint4 *>(tile + (p * 16 + rr) * kColPitch + ch * 16) = q[p];
+        }
+        __syncthreads();
+        const uint32_t cp = t & 63, jb = t >> 6;
+        const uint32_t col = c0 + 2 * cp;               // output rows col, col + 1
+        const uint32_t k0 = r0 + 32 * jb;               // first K of the thread's 32
+        const uint32_t kvalid = k0 < rows ? min(32u, rows - k0) : 0u;  // 0, 16 or 32
+        float v[2][32];
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+            const uint32_t w = *reinterpret_cast<const uint32_t *>(tile + (jb * 32 + i) * kColPitch + cp * 4);
+            v[0][i] = bf16_lo(w);
+            v[1][i] = bf16_hi(w);
+        }
+        if (kHad) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+#pragma unroll
+                for (int i = 0; i < 32; ++i)
+                    if ((sign_mask >> i) & 1u) v[h][i] = -v[h][i];
+#pragma unroll
+                for (int st = 1; st < 32; st <<= 1) {
+#pragma unroll
+                    for (int i = 0; i < 32; ++i) {
+                        if (i & st) continue;
+                        const float a = v[h][i], b = v[h][i + st];
+                        v[h][i] = a + b;
+                        v[h][i + st] = a - b;
+                    }
+                }
+            }
+        }
+        // block maxima (rows past the end and missing columns are zeros in the
+        // tile, so they never raise a maximum)
+        uint32_t bmax[2][2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int b = 0; b < 2; ++b) {
+                uint32_t m = 0;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) m = max(m, f2u(v[h][16 * b + i]) & 0x7FFFFFFFu);
+                bmax[h][b] = m;
+            }
+        float S;
+        if (kMode == 1) {
+            uint32_t a = 0;
+            for (uint32_t i = t; i < npartial; i += kThreads) a = max(a, partial[i]);
+            S = nv_tensor_scale(u2f(block_max_u32(a, sh)));
+            if (blockIdx.x == 0 && t == 0) *tensor_scale = S;
+        } else {
+            const uint32_t a = block_max_u32(max(max(bmax[0][0], bmax[0][1]), max(bmax[1][0], bmax[1][1])), sh);
+            if (kMode == 2) {
+                run_max = max(run_max, a);
+                continue;
+            }
+            S = nv_tensor_scale(u2f(a));
+            if (t == 0) tensor_scale[(c0 / kColTile) * tiles_r + r0 / kColTile] = S;
+        }
+        if (kvalid == 0 || col >= cols) continue;
+        const uint32_t K2 = rows >> 1, K16 = rows >> 4;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            uint32_t out[4], sbs = 0;
+#pragma unroll
+            for (int b = 0; b < 2; ++b) {
+                const uint32_t sb = nv_block_scale(u2f(bmax[h][b]), S);
+                const float inv = nv_inv_decode(sb, S);
+                sbs |= sb << (8 * b);
+#pragma unroll
+                for (int g2 = 0; g2 < 2; ++g2) {
+                    const int g = 2 * b + g2;  // 8-element group within the 32
+                    float y[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) y[e] = v[h][8 * g + e] * inv;
+                    if (kSR) {
+                        uint32_t w[4];
+                        philox4x32_10((k0 >> 3) + g, col + h, stream_id, 0u, seed_lo, seed_hi, w);
+                        uint32_t packed = 0;
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) packed |= e2m1_sr(y[e], r16_of(w, e)) << (4 * e);
+                        out[g] = packed;
+                    } else {
+                        out[g] = cvt8_f32(y, 1.0f);
+                    }
+                }
+            }
+            uint8_t *crow = codes + (size_t)(col + h) * K2 + (k0 >> 1);
+            uint8_t *srow = scales + (size_t)(col + h) * K16 + (k0 >> 4);
+            if (kvalid == 32 && (rows & 31u) == 0) {  // 16- and 2-byte aligned rows
+                *reinterpret_cast<uint4 *>(crow) = make_uint4(out[0], out[1], out[2], out[3]);
+                *reinterpret_cast<uint16_t *>(srow) = (uint16_t)sbs;
+            } else {  // rows % 32 == 16: 8-byte aligned code rows, byte scales
+                *reinterpret_cast<uint2 *>(crow) = make_uint2(out[0], out[1]);
+                srow[0] = (uint8_t)sbs;
+                if (kvalid == 32) {
+                    *reinterpret_cast<uint2 *>(crow + 8) = make_uint2(out[2], out[3]);
+                    srow[1] = (uint8_t)(sbs >> 8);
+                }
+            }
+        }
+    }
+    if (kMode == 2 && t == 0) partial[blockIdx.x] = run_max;
+    if (kMode == 1 && ntile == 0 && t == 0) *tensor_scale = 1.0f;  // an empty operand: S = 1
+}
+
 }  // namespace
 
 // ------------------------------------------------------------------ launchers
@@ -732,6 +890,32 @@ int launch_quant_nv(const QuantArgs &a, int domain, float *tensor_scale, void *w
     auto *x = reinterpret_cast<const uint16_t *>(a.x);
     auto *codes = reinterpret_cast<uint32_t *>(a.codes);
     auto *scales = reinterpret_cast<uint8_t *>(a.scales);
+    if (a.axis == 1) {
+        // along columns (x^T), optionally with the Hadamard: rows = K
+        const uint32_t rows = (uint32_t)a.rows, cols = (uint32_t)a.cols;
+        const uint32_t ntile = ((cols + kColTile - 1) / kColTile) * ((rows + kColTile - 1) / kColTile);
+        auto *c8 = reinterpret_cast<uint8_t *>(a.codes);
+        if (domain == 1) {
+            if (ntile == 0) return 0;
+#define FP4Q_NVC(SR, HAD, MODE, G, PART, NP)                                                                       \
+    hipLaunchKernelGGL((nv_quant_cols_kernel<SR, HAD, MODE>), dim3(G), dim3(kThreads), 0, st, x, rows, cols,       \
+                       (uint32_t)a.ld, c8, scales, tensor_scale, PART, NP, seed_lo, seed_hi, a.stream_id, a.sign_mask)
+            if (a.sr) { if (a.hadamard) FP4Q_NVC(true, true, 0, ntile, nullptr, 0u); else FP4Q_NVC(true, false, 0, ntile, nullptr, 0u); }
+            else { if (a.hadamard) FP4Q_NVC(false, true, 0, ntile, nullptr, 0u); else FP4Q_NVC(false, false, 0, ntile, nullptr, 0u); }
+        } else {
+            // pass 1: partial maxima of the (transformed) values; an empty
+            // operand still gets S = 1 from pass 2
+            auto *part = reinterpret_cast<uint32_t *>(workspace);
+            const uint32_t np = ntile == 0 ? 1u : min(ntile, (uint32_t)kAmaxBlocks);
+            if (a.hadamard) FP4Q_NVC(false, true, 2, np, part, 0u);
+            else FP4Q_NVC(false, false, 2, np, part, 0u);
+            const uint32_t g = ntile == 0 ? 1u : ntile;
+            if (a.sr) { if (a.hadamard) FP4Q_NVC(true, true, 1, g, part, np); else FP4Q_NVC(true, false, 1, g, part, np); }
+            else { if (a.hadamard) FP4Q_NVC(false, true, 1, g, part, np); else FP4Q_NVC(false, false, 1, g, part, np); }
+#undef FP4Q_NVC
+        }
+        return hipGetLastError() == hipSuccess ? 0 : 1;
+    }
     if (domain == 0) {
         const uint64_t nchunks = (uint64_t)R * (K >> 3);
         const uint32_t *partial;

@@ -186,12 +186,26 @@ FP4Q_API size_t fp4q_nv_workspace_bytes(int64_t rows, int64_t cols, int axis, in
  * 128 x 128 tile, one kernel) ([Fusion] section "The Design Philosophy of
  * Format-Aware Fusion"; the two-level scale of [Stack] section "NVFP4 is more
  * than a 4-bit value").  Writes codes [R x K/2], E4M3 scales [R x K/16] and
- * tensor_scale.  Requires K % 16 == 0.  FP4Q_EUNSUPPORTED: axis
- * FP4Q_ALONG_COLS, layout FP4Q_LAYOUT_TILED. */
+ * tensor_scale.  Both axes: along columns (the transpose a wgrad operand
+ * needs) a 128 x 128 tile of x is one tile domain of x^T.  Requires
+ * K % 16 == 0, and cols % 4 == 0 along columns.  FP4Q_EUNSUPPORTED: layout
+ * FP4Q_LAYOUT_TILED. */
 FP4Q_API fp4q_status fp4_quantize_nv(const void *x, int64_t rows, int64_t cols, int64_t ld_x, int axis, int round,
                             uint64_t seed, uint32_t stream_id, int domain, void *codes, void *scales,
                             float *tensor_scale, void *workspace, size_t workspace_bytes, int layout,
                             void *stream);
+
+/* Fixed-sign 32-point Hadamard along K, then NVFP4 ([Fusion] section "Two Key
+ * Numerical Techniques" names it for the weight-gradient operands; here on
+ * the NVFP4 path): as fp4_quantize_nv on the transformed values, which the
+ * domain amax, the block amax and the codes all see.  Along columns only
+ * (the wgrad operands, quantized along tokens); requires K % 32 == 0 and
+ * cols % 4 == 0.  FP4Q_EUNSUPPORTED: FP4Q_ALONG_ROWS, layout
+ * FP4Q_LAYOUT_TILED. */
+FP4Q_API fp4q_status fp4_hadamard32_quantize_nv(const void *x, int64_t rows, int64_t cols, int64_t ld_x, int axis,
+                                       uint32_t sign_mask, int round, uint64_t seed, uint32_t stream_id, int domain,
+                                       void *codes, void *scales, float *tensor_scale, void *workspace,
+                                       size_t workspace_bytes, int layout, void *stream);
 
 /* MXFP4 GEMM on gfx950's scaled FP4 MFMA (E8M0 scales applied by the matrix
  * core): C = alpha * A * B^T.  a_codes [M x K/2], a_scales [M x K/32],

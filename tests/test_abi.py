@@ -26,8 +26,8 @@ def lib():
 def test_exports_every_declared_function():
     names = B.declared_functions()
     assert set(names) >= {"fp4_quantize_mx", "fp4_quantize_nv", "fp4_hadamard32_quantize", "fp4_quantize_mx_dual",
-                          "fp4_quantize_nv_amax", "fp4_gemm_mx", "fp4_gemm_nv", "fp4_gemm_mx_amax",
-                          "fp4_gemm_nv_amax"}
+                          "fp4_quantize_nv_amax", "fp4_hadamard32_quantize_nv", "fp4_gemm_mx", "fp4_gemm_nv",
+                          "fp4_gemm_mx_amax", "fp4_gemm_nv_amax"}
     for n in names:
         assert hasattr(L, n), n
     assert B.abi_version() == 1
@@ -79,7 +79,9 @@ def test_quantize_nv_status_codes():
     assert L.fp4q_nv_workspace_bytes(64, 64, 0, 0) > 0
     assert L.fp4q_nv_workspace_bytes(64, 64, 0, 1) == 0
     assert q_nv(dom=2) == B.EINVAL
-    assert q_nv(axis=1) == B.EUNSUPPORTED
+    assert q_nv(axis=1) in (B.OK, B.ELAUNCH)         # along columns is valid (no GPU here: the launch fails)
+    assert q_nv(axis=1, rows=40) == B.ESHAPE         # K = rows % 16
+    assert q_nv(axis=1, cols=62, ld=64) == B.ESHAPE  # column axis needs cols % 4
     assert q_nv(cols=40, ld=48) == B.ESHAPE
     assert q_nv(ts=None) == B.EINVAL
     assert q_nv(ws=None) == B.EINVAL
@@ -193,3 +195,17 @@ def test_amax_entry_points_status_codes():
     assert q_nv1(amax=AMAX + 1) == B.EALIGN
     assert q_nv1(amax=CODES + 16) == B.EINVAL    # overlaps an output
     assert q_nv1(cols=24) == B.ESHAPE            # K % 16
+
+
+def test_hadamard_nv_status_codes():
+    def q(axis=1, rows=64, cols=64, ld=64, dom=0, rnd=0):
+        wb = L.fp4q_nv_workspace_bytes(rows, cols, axis, dom)
+        return L.fp4_hadamard32_quantize_nv(X, rows, cols, ld, axis, 0x1234, rnd, 7, 0, dom, CODES, SCALES, TS, WS,
+                                            wb, 0, None)
+
+    assert q() in (B.OK, B.ELAUNCH)       # valid (no GPU here: the launch fails)
+    assert q(dom=1) in (B.OK, B.ELAUNCH)
+    assert q(axis=0) == B.EUNSUPPORTED   # along rows not built
+    assert q(rows=48) == B.ESHAPE        # K = rows % 32
+    assert q(cols=62, ld=64) == B.ESHAPE
+    assert q(rnd=3) == B.EINVAL
