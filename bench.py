@@ -49,7 +49,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="qkv",
                     choices=["qkv", "mlp", "backward", "backward_dual", "dual_x", "nvfp4_global", "nvfp4_tile",
-                             "nvfp4_chain", "nvfp4_chain_2pass", "nvfp4_wgrad", "copy"],
+                             "nvfp4_chain", "nvfp4_chain_2pass", "nvfp4_wgrad", "mlp_chain", "mlp_chain_fused",
+                             "copy"],
                     help="copy = a plain 1 GiB device copy: the HBM reference for counter scaling")
     ap.add_argument("--copies", type=int, default=4, help="input copies rotated across steps (cold producers)")
     ap.add_argument("--layout", default="tiled", choices=["tiled", "linear"],
@@ -225,6 +226,48 @@ def build_workload(name, dev, copies, layout_name="tiled"):
                            (", dY's two operands from one read (dual producer)" if dual else ""),
                "dgrad_mnk": [T, I, O], "wgrad_mnk": [O, I, T], "layout": layout_name, "input_copies": copies}
         return cfg, ops, 2.0 * T * I * O * 2
+    if name in ("mlp_chain", "mlp_chain_fused"):
+        # two MXFP4 GEMMs in a row (MLP up then down shapes, tiled layout):
+        # mlp_chain writes H = X W1^T in bf16 and quantizes it for GEMM2;
+        # mlp_chain_fused has GEMM1's epilogue write H as GEMM2's MXFP4
+        # operand directly (fp4_gemm_mx_quant)
+        fused = name == "mlp_chain_fused"
+        X = gen("qkv", "X", copies)
+        W1 = gen("nvfp4", "W", copies)
+        W2 = gen("mlp_down", "W", copies)
+        M, K = X[0].shape
+        N1, N2 = W1[0].shape[0], W2[0].shape[0]
+        bx, bw1, bh, bw2 = mx_bufs(M, K), mx_bufs(N1, K), mx_bufs(M, N1), mx_bufs(N2, N1)
+        H = None if fused else torch.empty((M, N1), dtype=torch.bfloat16, device=dev)
+        C2 = torch.empty((M, N2), dtype=torch.bfloat16, device=dev)
+        ops = [
+            ("quantize X", qk, lambda s: B.fp4_quantize_mx(X[s % copies], codes=bx[0], scales=bx[1], layout=L),
+             M * K * MX_BYTES_PER_ELEM, "GB/s", HBM_PEAK_GBS, "hbm"),
+            ("quantize W1", qk, lambda s: B.fp4_quantize_mx(W1[s % copies], codes=bw1[0], scales=bw1[1], layout=L),
+             N1 * K * MX_BYTES_PER_ELEM, "GB/s", HBM_PEAK_GBS, "hbm"),
+        ]
+        if fused:
+            ops.append(("GEMM1 X W1^T -> MXFP4 H (fused quantize)", "gemm_mx_kernel",
+                        lambda s: B.fp4_gemm_mx_quant(*bx, *bw1, layout=L, m=M, n=N1, c_layout=L, codes=bh[0],
+                                                      scales=bh[1]),
+                        2.0 * M * N1 * K, "TFLOP/s", FP4_PEAK_TFLOPS, "mfma"))
+        else:
+            ops += [("GEMM1 X W1^T -> bf16 H", "gemm_mx_kernel",
+                     lambda s: B.fp4_gemm_mx(*bx, *bw1, c=H, layout=L, m=M, n=N1), 2.0 * M * N1 * K, "TFLOP/s",
+                     FP4_PEAK_TFLOPS, "mfma"),
+                    ("quantize H", qk, lambda s: B.fp4_quantize_mx(H, codes=bh[0], scales=bh[1], layout=L),
+                     M * N1 * MX_BYTES_PER_ELEM, "GB/s", HBM_PEAK_GBS, "hbm")]
+        ops += [
+            ("quantize W2", qk, lambda s: B.fp4_quantize_mx(W2[s % copies], codes=bw2[0], scales=bw2[1], layout=L),
+             N2 * N1 * MX_BYTES_PER_ELEM, "GB/s", HBM_PEAK_GBS, "hbm"),
+            ("GEMM2 H W2^T -> bf16", "gemm_mx_kernel",
+             lambda s: B.fp4_gemm_mx(*bh, *bw2, c=C2, layout=L, m=M, n=N2), 2.0 * M * N2 * N1, "TFLOP/s",
+             FP4_PEAK_TFLOPS, "mfma"),
+        ]
+        cfg = {"workload": "MXFP4, two chained GEMMs (MLP up then down shapes), H " +
+                           ("quantized in GEMM1's epilogue" if fused else "written in bf16 and quantized by the producer"),
+               "gemm1_mnk": [M, N1, K], "gemm2_mnk": [M, N2, N1], "layout": layout_name, "input_copies": copies}
+        return cfg, ops, 2.0 * M * N1 * K + 2.0 * M * N2 * N1
     if name == "nvfp4_wgrad":
         # the o_proj weight gradient in NVFP4 (per-tile domain): dY^T and X^T
         # quantized along tokens with the fixed-sign Hadamard (SR on dY), then

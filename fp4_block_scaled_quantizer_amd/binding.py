@@ -64,13 +64,14 @@ def lib() -> ctypes.CDLL:
     L.fp4_gemm_mx.argtypes = [vp, vp, vp, vp, i64, i64, i64, f32, i32, vp, i32, i64, vp]
     L.fp4_gemm_nv.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, i64, i64, f32, i32, vp, i32, i64, vp]
     L.fp4_gemm_mx_amax.argtypes = [vp, vp, vp, vp, i64, i64, i64, f32, i32, vp, i32, i64, vp, vp]
+    L.fp4_gemm_mx_quant.argtypes = [vp, vp, vp, vp, i64, i64, i64, f32, i32, vp, vp, i32, vp]
     L.fp4_gemm_nv_amax.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, i64, i64, f32, i32, vp, i32, i64, vp, vp]
     L.fp4_quantize_nv_amax.argtypes = [vp, i64, i64, i64, i32, u64, u32, vp, vp, vp, vp, vp]
     L.fp4_hadamard32_quantize_nv.argtypes = [vp, i64, i64, i64, i32, u32, i32, u64, u32, i32, vp, vp, vp, vp,
                                              ctypes.c_size_t, i32, vp]
     for fn in ("fp4_quantize_mx", "fp4_hadamard32_quantize", "fp4_quantize_mx_dual", "fp4_quantize_nv",
                "fp4_quantize_nv_amax", "fp4_hadamard32_quantize_nv", "fp4_gemm_mx", "fp4_gemm_nv",
-               "fp4_gemm_mx_amax", "fp4_gemm_nv_amax"):
+               "fp4_gemm_mx_amax", "fp4_gemm_nv_amax", "fp4_gemm_mx_quant"):
         getattr(L, fn).restype = i32
     L.fp4q_status_str.argtypes = [i32]
     L.fp4q_status_str.restype = ctypes.c_char_p
@@ -265,6 +266,25 @@ def fp4_gemm_mx(a_codes: torch.Tensor, a_scales: torch.Tensor, b_codes: torch.Te
                                             b_scales.data_ptr(), M, N, K, float(alpha), layout,
                                             c.data_ptr(), ctype, ldc, _stream(stream)))
     return c
+
+
+def fp4_gemm_mx_quant(a_codes: torch.Tensor, a_scales: torch.Tensor, b_codes: torch.Tensor, b_scales: torch.Tensor,
+                      *, alpha: float = 1.0, layout: int = LAYOUT_LINEAR, m: Optional[int] = None,
+                      n: Optional[int] = None, c_layout: int = LAYOUT_LINEAR, codes: Optional[torch.Tensor] = None,
+                      scales: Optional[torch.Tensor] = None, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """C = alpha * A B^T written as an MXFP4 operand along rows (RNE of the
+    bf16 C) in c_layout: returns (codes, scales)."""
+    M = a_codes.shape[0] if m is None else m
+    N = b_codes.shape[0] if n is None else n
+    K = a_codes.shape[1] * 2
+    if b_codes.shape[1] * 2 != K:
+        raise ValueError("A and B must have the same K")
+    codes, scales = _mx_outputs(M, N, c_layout, codes, scales, a_codes.device)
+    _check("fp4_gemm_mx_quant",
+           lib().fp4_gemm_mx_quant(a_codes.data_ptr(), a_scales.data_ptr(), b_codes.data_ptr(), b_scales.data_ptr(),
+                                   M, N, K, float(alpha), layout, codes.data_ptr(), scales.data_ptr(), c_layout,
+                                   _stream(stream)))
+    return codes, scales
 
 
 def fp4_gemm_nv(a_codes: torch.Tensor, a_scales: torch.Tensor, a_tensor_scale: torch.Tensor, b_codes: torch.Tensor,

@@ -150,6 +150,57 @@ fp4q_status run_gemm_mx(const void *a_codes, const void *a_scales, const void *b
     return launched(fp4q::launch_gemm_mx(g, as_stream(stream)));
 }
 
+// MX GEMM whose C leaves as an MXFP4 operand along rows (codes + E8M0
+// scales in c_layout) instead of as bf16 / fp32.
+fp4q_status run_gemm_mx_quant(const void *a_codes, const void *a_scales, const void *b_codes, const void *b_scales,
+                              int64_t M, int64_t N, int64_t K, float alpha, int layout, void *c_codes,
+                              void *c_scales, int c_layout, void *stream)
+{
+    if ((layout != FP4Q_LAYOUT_LINEAR && layout != FP4Q_LAYOUT_TILED) ||
+        (c_layout != FP4Q_LAYOUT_LINEAR && c_layout != FP4Q_LAYOUT_TILED))
+        return FP4Q_EINVAL;
+    const bool tiled = layout == FP4Q_LAYOUT_TILED, ctiled = c_layout == FP4Q_LAYOUT_TILED;
+    if (M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return FP4Q_ESHAPE;
+    if (K % 128 != 0 || N % (ctiled ? 128 : 32) != 0) return FP4Q_ESHAPE;
+    const uint64_t Ms = tiled ? (uint64_t)(M + 31) / 32 * 32 : (uint64_t)M;
+    const uint64_t Ns = tiled ? (uint64_t)(N + 31) / 32 * 32 : (uint64_t)N;
+    const uint64_t Mq = ctiled ? (uint64_t)(M + 31) / 32 * 32 : (uint64_t)M;  // stored output rows
+    if (Ms * (uint64_t)K / 2 >= (1ull << 32) || Ns * (uint64_t)K / 2 >= (1ull << 32) ||
+        Mq * (uint64_t)N / 2 >= (1ull << 32))
+        return FP4Q_ESHAPE;
+    if (M == 0 || N == 0) return FP4Q_OK;
+    if (!c_codes || !c_scales) return FP4Q_EINVAL;
+    if (!aligned(c_codes, 16) || !aligned(c_scales, 4)) return FP4Q_EALIGN;
+    const Range oc = bytes(c_codes, Mq * N / 2), os = bytes(c_scales, Mq * N / 32);
+    if (overlap(oc, os)) return FP4Q_EINVAL;
+    if (K > 0) {
+        if (!a_codes || !a_scales || !b_codes || !b_scales) return FP4Q_EINVAL;
+        if (!aligned(a_codes, 16) || !aligned(b_codes, 16) || !aligned(a_scales, 4) || !aligned(b_scales, 4))
+            return FP4Q_EALIGN;
+        const Range ins[4] = {bytes(a_codes, Ms * K / 2), bytes(a_scales, Ms * K / 32), bytes(b_codes, Ns * K / 2),
+                              bytes(b_scales, Ns * K / 32)};
+        for (const Range &r : ins)
+            if (overlap(oc, r) || overlap(os, r)) return FP4Q_EINVAL;
+    }
+    fp4q::GemmArgs g{};
+    g.a_codes = a_codes;
+    g.a_scales = a_scales;
+    g.b_codes = b_codes;
+    g.b_scales = b_scales;
+    g.M = M;
+    g.N = N;
+    g.K = K;
+    g.alpha = alpha;
+    g.c_bf16 = true;
+    g.ldc = N;
+    g.tiled = tiled;
+    g.q_codes = c_codes;
+    g.q_scales = c_scales;
+    g.q_tiled = ctiled;
+    (void)hipGetLastError();
+    return launched(fp4q::launch_gemm_mx(g, as_stream(stream)));
+}
+
 fp4q_status run_gemm_nv(const void *a_codes, const void *a_scales, const float *a_tensor_scale, const void *b_codes,
                         const void *b_scales, const float *b_tensor_scale, int domain, int64_t M, int64_t N,
                         int64_t K, float alpha, int layout, void *c, int c_type, int64_t ldc, float *c_amax,
@@ -346,6 +397,14 @@ fp4q_status fp4_gemm_mx_amax(const void *a_codes, const void *a_scales, const vo
 {
     if (!c_amax) return FP4Q_EINVAL;
     return run_gemm_mx(a_codes, a_scales, b_codes, b_scales, M, N, K, alpha, layout, c, c_type, ldc, c_amax, stream);
+}
+
+fp4q_status fp4_gemm_mx_quant(const void *a_codes, const void *a_scales, const void *b_codes, const void *b_scales,
+                              int64_t M, int64_t N, int64_t K, float alpha, int layout, void *c_codes, void *c_scales,
+                              int c_layout, void *stream)
+{
+    return run_gemm_mx_quant(a_codes, a_scales, b_codes, b_scales, M, N, K, alpha, layout, c_codes, c_scales,
+                             c_layout, stream);
 }
 
 fp4q_status fp4_gemm_nv(const void *a_codes, const void *a_scales, const float *a_tensor_scale, const void *b_codes,

@@ -147,4 +147,24 @@ FP4Q_HD void philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3, u
 // words are w[4]: word j/2, high half for odd j.
 FP4Q_HD uint32_t r16_of(const uint32_t w[4], int j) { return (j & 1) ? (w[j >> 1] >> 16) : (w[j >> 1] & 0xFFFFu); }
 
+// Device-only helpers shared by the producers and the GEMM epilogue that
+// quantizes its output.
+// 2^E as binary32 for E8M0 byte E + 127 (byte 0 -> the subnormal 2^-127).
+__device__ __forceinline__ float mx_scale_f32(uint32_t byte) { return byte ? u2f(byte << 23) : u2f(0x00400000u); }
+
+// E2M1 round-to-nearest-even of x / scale for 8 values, by gfx950's scaled
+// FP4 convert (2 values per instruction, element 2j in the low nibble of byte
+// j); scale an exact power of two (see cvt8_bf16 in quant.hip for how the
+// instruction was checked against the library's RNE rule).
+__device__ __forceinline__ uint32_t cvt8_f32(const float f[8], float scale)
+{
+    uint32_t r = 0;
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, f[0], f[1], scale, 0);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, f[2], f[3], scale, 1);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, f[4], f[5], scale, 2);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, f[6], f[7], scale, 3);
+    return r;
+}
+
+
 }  // namespace fp4q

@@ -39,6 +39,9 @@ struct GemmArgs {
     bool c_bf16;
     int64_t ldc;
     uint32_t *c_amax;  // optional: max |C| as stored, folded in as binary32 bits
+    // MX only, optional: C written as an MXFP4 operand along rows instead
+    void *q_codes, *q_scales;
+    bool q_tiled;
 };
 
 int launch_quant_mx(const QuantArgs &a, hipStream_t st);

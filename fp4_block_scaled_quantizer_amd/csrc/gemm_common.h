@@ -9,6 +9,8 @@
 
 #include <type_traits>
 
+#include "fp4q_device.h"
+
 namespace fp4q {
 namespace gemm {
 
@@ -261,6 +263,137 @@ __device__ __forceinline__ void store_wave_block_any(const v16f_t (&acc)[4][kNJ]
             store_wave_block<kNJ, false, false>(acc, ep, el, row_base, col_base, M, N, alpha, C, ldc, vec_ok, full,
                                                 amax_out);
     }
+}
+
+// One accumulator register read in program order.  Read through plain C++,
+// the accumulators of a whole wave block are copied out of the accumulator
+// registers at once and spill; the opaque read keeps each copy next to its
+// use.  The caller covers the matrix-core write-to-read distance.
+__device__ __forceinline__ float acc_read(float a)
+{
+    float v;
+    asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v) : "a"(a));
+    return v;
+}
+
+// The value lane l ^ 32 holds (v_permlane32_swap: no LDS traffic); h = l / 32.
+__device__ __forceinline__ uint32_t lane_half_exchange(uint32_t v, int h)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return h ? r[0] : r[1];
+}
+
+// Epilogue that writes a wave's 128 x 128 block of C as an MXFP4 operand
+// along rows (the next GEMM's A operand) instead of as C itself.  Each value
+// (times alpha) is rounded to bf16 first, so the output is exactly what the
+// MX row producer makes of the bf16 C.  A row's 32-column block lies in
+// lanes l and l ^ 32 (16 values each, four groups of four columns 8 g + 4 h):
+// one exchange gives the block amax, a second the other lane's codes, after
+// which lane h writes bytes 8 h .. 8 h + 7 of the row's 16 code bytes; the
+// lane h = 0 also writes the row's four scale bytes of the 128 columns as
+// one word.  Requires N % 32 == 0 (N % 128 == 0 tiled); in the tiled layout
+// rows M .. Mp-1 are written as zero codes and zero scales, as the producers
+// write them.
+template <bool kScale, bool kTiled>
+__device__ __forceinline__ void store_wave_block_mxq(const v16f_t (&acc)[4][4], int el, int row_base, int col_base,
+                                                     int M, int N, int Mp, float alpha, uint8_t *codes,
+                                                     uint8_t *scales)
+{
+    const int fr = el & 31, h = el >> 5;
+    // the opaque reads hide the last matrix-core writes from the compiler's
+    // hazard tracking: wait out the longest write-to-read distance here
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int row = row_base + 32 * i + fr;
+        const bool live = row < M;
+        const bool pad = !live && kTiled && row < Mp;
+        uint32_t sword = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int c = col_base + 32 * j;
+            if (c >= N) continue;  // the same for every lane
+            // bf16 pairs (round to nearest even, as the bf16 epilogue
+            // stores them); the block amax is taken on the fp32 values and
+            // rounded once (rounding is monotonic)
+            bf16x2_t p[8];
+            float fmx = 0.0f;
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+                float a0 = acc_read(acc[i][j][2 * r]), a1 = acc_read(acc[i][j][2 * r + 1]);
+                if (kScale) {
+                    a0 *= alpha;
+                    a1 *= alpha;
+                }
+                fmx = fmaxf(fmx, fmaxf(fabsf(a0), fabsf(a1)));
+                p[r] = __builtin_convertvector((f32x2_t){a0, a1}, bf16x2_t);
+            }
+            uint32_t amax =
+                (__builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){fmx, 0.0f}, bf16x2_t)) & 0xFFFFu) << 16;
+            amax = max(amax, lane_half_exchange(amax, h));
+            const uint32_t sbyte = mx_scale_byte(amax);
+            const float scale = mx_scale_f32(sbyte);
+            uint32_t grp[4];  // 4 codes (16 bits) of columns 8 g + 4 h .. + 3
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const uint32_t r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(0u, p[2 * g], scale, 0);
+                grp[g] = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, p[2 * g + 1], scale, 1);
+            }
+            // lane h = 0 keeps groups 0, 1 of its half and takes the other
+            // half's; lane h = 1 keeps groups 2, 3
+            const uint32_t give = h ? (grp[0] | grp[1] << 16) : (grp[2] | grp[3] << 16);
+            const uint32_t got = lane_half_exchange(give, h);
+            uint2 out = h ? make_uint2((got & 0xFFFFu) | grp[2] << 16, (got >> 16) | grp[3] << 16)
+                          : make_uint2(grp[0] | got << 16, grp[1] | (got & 0xFFFF0000u));
+            if (pad) out = make_uint2(0u, 0u);
+            sword |= (live ? sbyte : 0u) << (8 * j);
+            if (live || pad) {
+                uint8_t *dst = kTiled ? codes + ((int64_t)(row >> 5) * (N >> 6) + (c >> 6)) * 1024 +
+                                            ((row & 31) + 32 * ((c >> 5) & 1)) * 16 + 8 * h
+                                      : codes + (int64_t)row * (N >> 1) + (c >> 1) + 8 * h;
+                *reinterpret_cast<uint2 *>(dst) = out;
+            }
+        }
+        if (h == 0 && (live || pad)) {
+            if (kTiled) {
+                *reinterpret_cast<uint32_t *>(scales + ((int64_t)(col_base >> 7) * Mp + row) * 4) = sword;
+            } else {
+                uint8_t *dst = scales + (int64_t)row * (N >> 5) + (col_base >> 5);
+                if (col_base + 128 <= N) {
+                    *reinterpret_cast<uint32_t *>(dst) = sword;
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        if (col_base + 32 * j < N) dst[j] = (uint8_t)(sword >> (8 * j));
+                }
+            }
+        }
+    }
+}
+
+// The quantizing epilogue for a runtime alpha and output layout.
+__device__ __forceinline__ void store_wave_block_mxq_any(const v16f_t (&acc)[4][4], int el, int row_base,
+                                                         int col_base, int M, int N, int Mp, float alpha,
+                                                         uint8_t *codes, uint8_t *scales, bool tiled)
+{
+    if (tiled) {
+        if (alpha != 1.0f)
+            store_wave_block_mxq<true, true>(acc, el, row_base, col_base, M, N, Mp, alpha, codes, scales);
+        else
+            store_wave_block_mxq<false, true>(acc, el, row_base, col_base, M, N, Mp, alpha, codes, scales);
+    } else {
+        if (alpha != 1.0f)
+            store_wave_block_mxq<true, false>(acc, el, row_base, col_base, M, N, Mp, alpha, codes, scales);
+        else
+            store_wave_block_mxq<false, false>(acc, el, row_base, col_base, M, N, Mp, alpha, codes, scales);
+    }
+}
+
+// n zero bytes (the quantized form of C = 0: zero codes, zero scales).
+static __global__ void fill_bytes_zero_kernel(uint8_t *__restrict__ p, int64_t n)
+{
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = 0;
 }
 
 // C = 0 (the K == 0 product); one thread per element.

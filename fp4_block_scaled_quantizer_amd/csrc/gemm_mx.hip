@@ -70,7 +70,8 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(const uint8_t *__restrict_
                                                       const uint8_t *__restrict__ B, const uint8_t *__restrict__ Bs,
                                                       int M, int N, int K, float alpha, void *__restrict__ C,
                                                       int64_t ldc, int c_bf16, int vec_ok, int tiles_m, int tiles_n,
-                                                      uint32_t *__restrict__ c_amax)
+                                                      uint32_t *__restrict__ c_amax, uint8_t *__restrict__ q_codes,
+                                                      uint8_t *__restrict__ q_scales, int q_tiled)
 {
     __shared__ __attribute__((aligned(1024))) uint8_t lds[kLdsBytes];
     const int tid = threadIdx.x, lane = tid & 63;
@@ -347,7 +348,12 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(const uint8_t *__restrict_
         // whole vector-memory counter (the next tile's DMA included).
         int el;
         asm volatile("v_mov_b32 %0, %1" : "=v"(el) : "v"(lane));
-        store_wave_block_any(acc, ep, el, row_base, col_base, M, N, alpha, C, ldc, c_bf16 != 0, vec_ok != 0, c_amax);
+        if (q_codes)  // C leaves as the next GEMM's MXFP4 operand
+            store_wave_block_mxq_any(acc, el, row_base, col_base, M, N, q_tiled ? (int)Mp : M, alpha, q_codes,
+                                     q_scales, q_tiled != 0);
+        else
+            store_wave_block_any(acc, ep, el, row_base, col_base, M, N, alpha, C, ldc, c_bf16 != 0, vec_ok != 0,
+                                 c_amax);
         if (next >= ntiles) break;
         tile = next;
     }
@@ -359,6 +365,15 @@ int launch_gemm_mx(const GemmArgs &g, hipStream_t st)
 {
     const int M = (int)g.M, N = (int)g.N, K = (int)g.K;
     if (M == 0 || N == 0) return 0;
+    auto *q_codes = reinterpret_cast<uint8_t *>(g.q_codes);
+    auto *q_scales = reinterpret_cast<uint8_t *>(g.q_scales);
+    if (K == 0 && q_codes) {
+        const int64_t ms = g.q_tiled ? (M + 31) / 32 * 32 : M;
+        const int64_t nc = ms * N / 2, ns = ms * N / 32;
+        hipLaunchKernelGGL(fill_bytes_zero_kernel, dim3((unsigned)((nc + 255) / 256)), dim3(256), 0, st, q_codes, nc);
+        hipLaunchKernelGGL(fill_bytes_zero_kernel, dim3((unsigned)((ns + 255) / 256)), dim3(256), 0, st, q_scales, ns);
+        return hipGetLastError() == hipSuccess ? 0 : 1;
+    }
     if (K == 0) {
         const int64_t n = (int64_t)M * N;
         hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, g.c, M, N, g.ldc,
@@ -383,10 +398,12 @@ int launch_gemm_mx(const GemmArgs &g, hipStream_t st)
     const int grid = min(tiles_m * tiles_n, cus);
     if (g.tiled)
         hipLaunchKernelGGL(gemm_mx_kernel<true>, dim3(grid), dim3(256), 0, st, a, as, b, bs, M, N, K, g.alpha, g.c,
-                           g.ldc, (int)g.c_bf16, vec_ok, tiles_m, tiles_n, g.c_amax);
+                           g.ldc, (int)g.c_bf16, vec_ok, tiles_m, tiles_n, g.c_amax, q_codes, q_scales,
+                           (int)g.q_tiled);
     else
         hipLaunchKernelGGL(gemm_mx_kernel<false>, dim3(grid), dim3(256), 0, st, a, as, b, bs, M, N, K, g.alpha, g.c,
-                           g.ldc, (int)g.c_bf16, vec_ok, tiles_m, tiles_n, g.c_amax);
+                           g.ldc, (int)g.c_bf16, vec_ok, tiles_m, tiles_n, g.c_amax, q_codes, q_scales,
+                           (int)g.q_tiled);
     return hipGetLastError() == hipSuccess ? 0 : 1;
 }
 

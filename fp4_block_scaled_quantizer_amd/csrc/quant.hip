@@ -88,18 +88,7 @@ __device__ __forceinline__ uint32_t cvt8_bf16(const uint4 &q, float scale)
     r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, __builtin_bit_cast(bf16x2_t, q.w), scale, 3);
     return r;
 }
-__device__ __forceinline__ uint32_t cvt8_f32(const float f[8], float scale)
-{
-    uint32_t r = 0;
-    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, f[0], f[1], scale, 0);
-    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, f[2], f[3], scale, 1);
-    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, f[4], f[5], scale, 2);
-    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, f[6], f[7], scale, 3);
-    return r;
-}
 
-// 2^E as binary32 for E8M0 byte E + 127 (byte 0 -> the subnormal 2^-127).
-__device__ __forceinline__ float mx_scale_f32(uint32_t byte) { return byte ? u2f(byte << 23) : u2f(0x00400000u); }
 
 // Largest |bf16| bit pattern (15 bits) among the 8 values of a chunk.
 __device__ __forceinline__ uint32_t amax8_bf16(const uint4 &q)

@@ -229,6 +229,21 @@ FP4Q_API fp4q_status fp4_gemm_nv(const void *a_codes, const void *a_scales, cons
                         int64_t M, int64_t N, int64_t K, float alpha, int layout, void *c, int c_type,
                         int64_t ldc, void *stream);
 
+/* MXFP4 GEMM whose output leaves as the next GEMM's MXFP4 operand: C =
+ * alpha * A * B^T is rounded to bf16 and quantized along rows (RNE, E8M0
+ * per 32) in the epilogue, so that no bf16 C is written and read back
+ * ([Fusion] section "Why FP4 Speedups Often Remain Theoretical": unfused
+ * quantization steps around the matrix multiply cost the gain; section "The
+ * Design Philosophy of Format-Aware Fusion": the producer writes the layout
+ * its consumer loads).  c_codes / c_scales are exactly what fp4_quantize_mx
+ * (FP4Q_ALONG_ROWS, FP4Q_RNE, c_layout) writes for the bf16 C that
+ * fp4_gemm_mx would produce.  A, B in `layout`; requires K % 128 == 0 and
+ * N % 32 == 0 (linear output) or N % 128 == 0 (tiled output, rows padded to
+ * 32 with zero codes and scales).  Errors as fp4_gemm_mx. */
+FP4Q_API fp4q_status fp4_gemm_mx_quant(const void *a_codes, const void *a_scales, const void *b_codes,
+                              const void *b_scales, int64_t M, int64_t N, int64_t K, float alpha, int layout,
+                              void *c_codes, void *c_scales, int c_layout, void *stream);
+
 /* The GEMMs above, also reporting max |C| for a following NVFP4 "global
  * nvfp" quantization of C, so that it needs no amax pass over C (the amax is
  * produced by the op before the quantizer: [Fusion] section "The Design

@@ -27,7 +27,7 @@ def test_exports_every_declared_function():
     names = B.declared_functions()
     assert set(names) >= {"fp4_quantize_mx", "fp4_quantize_nv", "fp4_hadamard32_quantize", "fp4_quantize_mx_dual",
                           "fp4_quantize_nv_amax", "fp4_hadamard32_quantize_nv", "fp4_gemm_mx", "fp4_gemm_nv",
-                          "fp4_gemm_mx_amax", "fp4_gemm_nv_amax"}
+                          "fp4_gemm_mx_amax", "fp4_gemm_nv_amax", "fp4_gemm_mx_quant"}
     for n in names:
         assert hasattr(L, n), n
     assert B.abi_version() == 1
@@ -209,3 +209,23 @@ def test_hadamard_nv_status_codes():
     assert q(rows=48) == B.ESHAPE        # K = rows % 32
     assert q(cols=62, ld=64) == B.ESHAPE
     assert q(rnd=3) == B.EINVAL
+
+
+def test_gemm_mx_quant_status_codes():
+    def g(M=64, N=128, K=128, layout=0, cl=0, codes=CODES2, scales=SCALES2, a=CODES):
+        return L.fp4_gemm_mx_quant(a, SCALES, X, C, M, N, K, 1.0, layout, codes, scales, cl, None)
+
+    assert g() in (B.OK, B.ELAUNCH)      # valid (no GPU here: the launch fails)
+    assert g(layout=2) == B.EINVAL
+    assert g(cl=2) == B.EINVAL
+    assert g(K=96) == B.ESHAPE           # K % 128
+    assert g(N=48) == B.ESHAPE           # N % 32 (linear output)
+    assert g(N=96, cl=1) == B.ESHAPE     # N % 128 (tiled output)
+    assert g(M=-1) == B.ESHAPE
+    assert g(codes=None) == B.EINVAL
+    assert g(a=None) == B.EINVAL
+    assert g(codes=CODES2 + 8) == B.EALIGN
+    assert g(scales=SCALES2 + 2) == B.EALIGN
+    assert g(scales=CODES2 + 16) == B.EINVAL   # output codes and scales overlap
+    assert g(codes=CODES + 64) == B.EINVAL     # output overlaps an input
+    assert g(M=0) == B.OK
