@@ -65,7 +65,7 @@ constexpr int kDmaB = kDmaPerStage - kDmaA;
 // Between two tiles the next tile's first two K steps are put in flight
 // before the finished tile's epilogue runs, so the epilogue hides the start
 // latency of the next tile.
-template <bool kTiled>
+template <bool kTiled, bool kQuantOut>
 __global__ __launch_bounds__(256) void gemm_mx_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
                                                       const uint8_t *__restrict__ B, const uint8_t *__restrict__ Bs,
                                                       int M, int N, int K, float alpha, void *__restrict__ C,
@@ -348,7 +348,7 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(const uint8_t *__restrict_
         // whole vector-memory counter (the next tile's DMA included).
         int el;
         asm volatile("v_mov_b32 %0, %1" : "=v"(el) : "v"(lane));
-        if (q_codes)  // C leaves as the next GEMM's MXFP4 operand
+        if constexpr (kQuantOut)  // C leaves as the next GEMM's MXFP4 operand
             store_wave_block_mxq_any(acc, el, row_base, col_base, M, N, q_tiled ? (int)Mp : M, alpha, q_codes,
                                      q_scales, q_tiled != 0);
         else
@@ -396,14 +396,15 @@ int launch_gemm_mx(const GemmArgs &g, hipStream_t st)
                                                  hipSuccess || cus <= 0)
         return 1;
     const int grid = min(tiles_m * tiles_n, cus);
-    if (g.tiled)
-        hipLaunchKernelGGL(gemm_mx_kernel<true>, dim3(grid), dim3(256), 0, st, a, as, b, bs, M, N, K, g.alpha, g.c,
-                           g.ldc, (int)g.c_bf16, vec_ok, tiles_m, tiles_n, g.c_amax, q_codes, q_scales,
-                           (int)g.q_tiled);
-    else
-        hipLaunchKernelGGL(gemm_mx_kernel<false>, dim3(grid), dim3(256), 0, st, a, as, b, bs, M, N, K, g.alpha, g.c,
-                           g.ldc, (int)g.c_bf16, vec_ok, tiles_m, tiles_n, g.c_amax, q_codes, q_scales,
-                           (int)g.q_tiled);
+#define FP4Q_GEMM_MX(T, Q)                                                                                     \
+    hipLaunchKernelGGL((gemm_mx_kernel<T, Q>), dim3(grid), dim3(256), 0, st, a, as, b, bs, M, N, K, g.alpha, g.c, \
+                       g.ldc, (int)g.c_bf16, vec_ok, tiles_m, tiles_n, g.c_amax, q_codes, q_scales, (int)g.q_tiled)
+    if (g.tiled) {
+        if (q_codes) FP4Q_GEMM_MX(true, true); else FP4Q_GEMM_MX(true, false);
+    } else {
+        if (q_codes) FP4Q_GEMM_MX(false, true); else FP4Q_GEMM_MX(false, false);
+    }
+#undef FP4Q_GEMM_MX
     return hipGetLastError() == hipSuccess ? 0 : 1;
 }
 
