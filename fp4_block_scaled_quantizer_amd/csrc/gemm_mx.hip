@@ -266,6 +266,10 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(const uint8_t *__restrict_
                 constexpr int i = t >> 2, j = t & 3;
                 acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb0[j], fa0[i], acc[i][j], 4, 4, 0,
                                                                              (int)sb[j], 0, (int)sa[i]);
+                // an opaque use keeps each MFMA in its slot: left alone, the
+                // compiler sinks the first MFMAs of a phase below the DMA and
+                // LDS reads of the following slots
+                asm volatile("" ::"a"(acc[i][j]));
                 if constexpr (t < kDmaA) dma_piece(dma_addr, t_tag);
                 if constexpr (t < 4) fa1[t] = frag(st, 0, t, 1);
                 else if constexpr (t < 8) fb1[t - 4] = frag(st, 1, t - 4, 1);
@@ -281,6 +285,7 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(const uint8_t *__restrict_
                 constexpr int i = t >> 2, j = t & 3;
                 acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb1[j], fa1[i], acc[i][j], 4, 4, 2,
                                                                              (int)sb[j], 2, (int)sa[i]);
+                asm volatile("" ::"a"(acc[i][j]));
                 if constexpr (t < kDmaB)
                     dma_piece(dma_addr, std::integral_constant<int, kDmaA + t>{});
                 // next step's operands, in the order phase A consumes them,

@@ -282,6 +282,10 @@ __global__ __launch_bounds__(256) void gemm_nv_fp16_kernel(
                         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[j], fa[i], (v16f_t){}, 0, 0, 0);
                     else
                         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[j], fa[i], acc[i][j], 0, 0, 0);
+                    // an opaque use keeps each MFMA in its slot (the compiler
+                    // would sink some below the DMA and dequantization of the
+                    // following slots)
+                    asm volatile("" ::"a"(acc[i][j]));
                     // DMA of step ks+3: two instructions per slice from slice 0 on
                     if constexpr (t < 2 && 2 * s + t < kDma)
                         dma_piece(dma_addr, std::integral_constant<int, 2 * s + t>{});
