@@ -73,6 +73,10 @@ def _load():
     sig("oc_dequant_mx", None, u8p, u8p, i64, i64, f64p)
     sig("oc_dequant_nv", None, u8p, u8p, f32p, i32, i64, i64, f64p)
     sig("oc_gemm_bruteforce", None, f64p, f64p, i64, i64, i64, ctypes.c_double, f64p, f64p)
+    sig("oc_float_to_bf16", ctypes.c_uint16, ctypes.c_float)
+    sig("oc_exp_f32_seq", ctypes.c_float, ctypes.c_float)
+    sig("oc_silu_f32", ctypes.c_float, ctypes.c_float)
+    sig("oc_swiglu_bf16", i32, u16p, i64, i64, i64, i64, u16p)
     _lib = lib
     return lib
 
@@ -297,3 +301,35 @@ def gemm_ref(a_dq, b_dq, alpha=1.0):
     C = alpha * (A @ B.T)
     W = abs(alpha) * (np.abs(A) @ np.abs(B).T)
     return C, W
+
+
+def float_to_bf16(f: float) -> int:
+    """binary32 -> bf16 bits, round to nearest even."""
+    return int(_load().oc_float_to_bf16(float(f)))
+
+
+def exp_f32_seq(t: float) -> float:
+    """e^t for t in [-20, 88] by the fixed binary32 sequence of fp4_oracle.c."""
+    return float(_load().oc_exp_f32_seq(float(t)))
+
+
+def silu_f32(x: float) -> float:
+    """SiLU(x) = x / (1 + e^-x) in binary32 (see fp4_oracle.c)."""
+    return float(_load().oc_silu_f32(float(x)))
+
+
+def swiglu_bf16(c, F, pair=32):
+    """H = bf16(SiLU(gate) * up) from a bf16 GEMM output C [M x >= 2F] whose
+    columns interleave gate and up in groups of `pair` (pair = 32: the
+    layout of the fused GEMM's weight; pair = F: [gate | up]).  c: a 2-D
+    uint16 array of bf16 bit patterns.  Returns uint16 bits [M x F]."""
+    cb = _as_bf16_bits(c)
+    M, ldc = cb.shape
+    if ldc < 2 * F:
+        raise ValueError("C needs at least 2F columns")
+    h = np.zeros((M, F), dtype=np.uint16)
+    if M and F:
+        rc = _load().oc_swiglu_bf16(_ptr(cb, ctypes.c_uint16), M, F, ldc, pair, _ptr(h, ctypes.c_uint16))
+        if rc != 0:
+            raise ValueError("pair must divide F")
+    return h

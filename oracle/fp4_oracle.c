@@ -488,3 +488,92 @@ void oc_gemm_bruteforce(const double *A, const double *B, int64_t M, int64_t N, 
             W[m * N + n] = fabs(alpha) * w;
         }
 }
+
+/* ------------------------------------------------------------------ */
+/* SwiGLU: the MLP activation whose output H the fused producer        */
+/* quantizes ([Fusion], section "The Design Philosophy of Format-Aware */
+/* Fusion": the producer is fused with the operation that creates its  */
+/* input).  Outside definitions: SwiGLU(g, u) = SiLU(g) * u with       */
+/* SiLU(x) = x / (1 + e^-x) (Shazeer, "GLU Variants Improve            */
+/* Transformer", 2020); the exponential follows Cody and Waite,        */
+/* "Software Manual for the Elementary Functions" (1980): reduction by */
+/* a two-part ln 2, then a polynomial.                                 */
+/* ------------------------------------------------------------------ */
+
+/* float -> bf16 bits, round to nearest even (NaN -> a quiet NaN). */
+static uint16_t float_to_bf16_rne(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x0040u);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+uint16_t oc_float_to_bf16(float f) { return float_to_bf16_rne(f); }
+
+/* e^t for t in [-20, 88], as one fixed sequence of binary32 operations (no
+ * library call, so that any implementation of the same sequence returns the
+ * same bits):
+ *   k = rint(t * log2(e))                      (round half to even)
+ *   r = (t - k * ln2_hi) - k * ln2_lo          ln2_hi has 15 significant bits,
+ *                                              so k * ln2_hi is exact, and so
+ *                                              is t - k * ln2_hi (Sterbenz)
+ *   p = 1 + r(1 + r(1/2 + r(1/6 + r(1/24 + r(1/120 + r(1/720 + r/5040))))))
+ *       (Horner, each product and sum rounded; the degree-7 Taylor
+ *       polynomial: truncation below 2^-27 relative for |r| <= 0.35)
+ *   e^t = p * 2^k                              (exact: the result is normal)
+ * Constants as binary32 (hex): log2(e) 0x1.715476p+0, ln2_hi 0x1.62e4p-1,
+ * ln2_lo 0x1.7f7d1cp-20, 1/5040 0x1.a01a02p-13, 1/720 0x1.6c16c2p-10,
+ * 1/120 0x1.111112p-7, 1/24 0x1.555556p-5, 1/6 0x1.555556p-3. */
+float oc_exp_f32_seq(float t)
+{
+    const float log2e = 0x1.715476p+0f, ln2_hi = 0x1.62e4p-1f, ln2_lo = 0x1.7f7d1cp-20f;
+    const float k = rintf(t * log2e);
+    float r = t - k * ln2_hi;
+    r = r - k * ln2_lo;
+    float p = 0x1.a01a02p-13f;
+    p = p * r + 0x1.6c16c2p-10f;
+    p = p * r + 0x1.111112p-7f;
+    p = p * r + 0x1.555556p-5f;
+    p = p * r + 0x1.555556p-3f;
+    p = p * r + 0.5f;
+    p = p * r + 1.0f;
+    p = p * r + 1.0f;
+    return ldexpf(p, (int)k);
+}
+
+/* SiLU(x) = x / (1 + e^-x) in binary32 (correctly rounded division).  For
+ * -x < -20, e^-x < 2^-28 and 1 + e^-x rounds to 1, so SiLU(x) = x exactly
+ * (this also covers x = +inf); for -x > 88 (x < -88, where the true value
+ * is above -1e-36 in magnitude) the result is -0; NaN stays NaN. */
+float oc_silu_f32(float x)
+{
+    if (x != x) return x;
+    const float t = -x;
+    if (t < -20.0f) return x;
+    if (t > 88.0f) return -0.0f;
+    return x / (1.0f + oc_exp_f32_seq(t));
+}
+
+/* H[m][j] = bf16(SiLU(g) * u), g and u the bf16 gate and up values of
+ * hidden column j read from the GEMM output C (row pitch ldc elements):
+ * C's columns interleave gate and up in groups of `pair` columns -- gate
+ * columns j of group b = j / pair sit at 2 pair b + (j mod pair), the up
+ * columns `pair` further -- so pair = 32 is the layout whose 32-column gate
+ * and up blocks share an accumulator lane, and pair = F is [gate | up].
+ * The product is one binary32 multiply, rounded to bf16 to nearest even
+ * (the activation's bf16 output, before the MX producer).  Returns 0, or -1
+ * if pair does not divide F. */
+int oc_swiglu_bf16(const uint16_t *c, int64_t M, int64_t F, int64_t ldc, int64_t pair, uint16_t *h)
+{
+    if (pair <= 0 || F % pair != 0) return -1;
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t j = 0; j < F; ++j) {
+            const int64_t gcol = (j / pair) * 2 * pair + (j % pair);
+            const float g = bf16_bits_to_float(c[m * ldc + gcol]);
+            const float u = bf16_bits_to_float(c[m * ldc + gcol + pair]);
+            h[m * F + j] = float_to_bf16_rne(oc_silu_f32(g) * u);
+        }
+    return 0;
+}
