@@ -309,12 +309,13 @@ def float_to_bf16(f: float) -> int:
 
 
 def exp_f32_seq(t: float) -> float:
-    """e^t for t in [-20, 88] by the fixed binary32 sequence of fp4_oracle.c."""
+    """e^t for t in [-20, 80] by the fixed binary32 sequence of fp4_oracle.c."""
     return float(_load().oc_exp_f32_seq(float(t)))
 
 
 def silu_f32(x: float) -> float:
-    """SiLU(x) = x / (1 + e^-x) in binary32 (see fp4_oracle.c)."""
+    """SiLU(x) = x / (1 + e^-x) in binary32: clamped argument, the exp
+    sequence, a Newton reciprocal (see fp4_oracle.c)."""
     return float(_load().oc_silu_f32(float(x)))
 
 

@@ -512,16 +512,17 @@ static uint16_t float_to_bf16_rne(float f)
 
 uint16_t oc_float_to_bf16(float f) { return float_to_bf16_rne(f); }
 
-/* e^t for t in [-20, 88], as one fixed sequence of binary32 operations (no
+/* e^t for t in [-20, 80], as one fixed sequence of binary32 operations (no
  * library call, so that any implementation of the same sequence returns the
- * same bits):
+ * same bits; fmaf is the IEEE fused multiply-add, one rounding):
  *   k = rint(t * log2(e))                      (round half to even)
- *   r = (t - k * ln2_hi) - k * ln2_lo          ln2_hi has 15 significant bits,
- *                                              so k * ln2_hi is exact, and so
- *                                              is t - k * ln2_hi (Sterbenz)
- *   p = 1 + r(1 + r(1/2 + r(1/6 + r(1/24 + r(1/120 + r(1/720 + r/5040))))))
- *       (Horner, each product and sum rounded; the degree-7 Taylor
- *       polynomial: truncation below 2^-27 relative for |r| <= 0.35)
+ *   r = fma(-k, ln2_hi, t)                     exact: ln2_hi has 15 significant
+ *                                              bits, so k * ln2_hi is exact and
+ *                                              t - k * ln2_hi too (Sterbenz)
+ *   r = fma(-k, ln2_lo, r)
+ *   p = Horner with fma: 1/5040 -> 1/720 -> 1/120 -> 1/24 -> 1/6 -> 1/2 -> 1 -> 1
+ *       (the degree-7 Taylor polynomial of e^r: truncation below 2^-27
+ *       relative for |r| <= 0.35)
  *   e^t = p * 2^k                              (exact: the result is normal)
  * Constants as binary32 (hex): log2(e) 0x1.715476p+0, ln2_hi 0x1.62e4p-1,
  * ln2_lo 0x1.7f7d1cp-20, 1/5040 0x1.a01a02p-13, 1/720 0x1.6c16c2p-10,
@@ -530,30 +531,57 @@ float oc_exp_f32_seq(float t)
 {
     const float log2e = 0x1.715476p+0f, ln2_hi = 0x1.62e4p-1f, ln2_lo = 0x1.7f7d1cp-20f;
     const float k = rintf(t * log2e);
-    float r = t - k * ln2_hi;
-    r = r - k * ln2_lo;
+    float r = fmaf(-k, ln2_hi, t);
+    r = fmaf(-k, ln2_lo, r);
     float p = 0x1.a01a02p-13f;
-    p = p * r + 0x1.6c16c2p-10f;
-    p = p * r + 0x1.111112p-7f;
-    p = p * r + 0x1.555556p-5f;
-    p = p * r + 0x1.555556p-3f;
-    p = p * r + 0.5f;
-    p = p * r + 1.0f;
-    p = p * r + 1.0f;
+    p = fmaf(p, r, 0x1.6c16c2p-10f);
+    p = fmaf(p, r, 0x1.111112p-7f);
+    p = fmaf(p, r, 0x1.555556p-5f);
+    p = fmaf(p, r, 0x1.555556p-3f);
+    p = fmaf(p, r, 0.5f);
+    p = fmaf(p, r, 1.0f);
+    p = fmaf(p, r, 1.0f);
     return ldexpf(p, (int)k);
 }
 
-/* SiLU(x) = x / (1 + e^-x) in binary32 (correctly rounded division).  For
- * -x < -20, e^-x < 2^-28 and 1 + e^-x rounds to 1, so SiLU(x) = x exactly
- * (this also covers x = +inf); for -x > 88 (x < -88, where the true value
- * is above -1e-36 in magnitude) the result is -0; NaN stays NaN. */
+/* SiLU(x) = x * (1 / (1 + e^-x)) in binary32, division-free:
+ *   t = min(max(-x, -20), 80)                  (NaN -> -20; clamping changes
+ *                                              nothing below -20, where
+ *                                              1 + e^t rounds to 1, and above
+ *                                              80 gives x / (1 + e^80), within
+ *                                              1e-33 of the true value)
+ *   d = 1 + e^t                                (oc_exp_f32_seq)
+ *   y = bits 0x7EF311C3 - bits(d)              (a linear reciprocal seed from
+ *                                              the exponent and mantissa bits,
+ *                                              within 5.1 % of 1/d)
+ *   three Newton steps: q = fma(-d, y, 1), y = fma(y, q, y)
+ *   SiLU = x * y
+ * So SiLU(x) = x exactly for x > 20 (then d = 1 and y converges to 1) and a
+ * NaN stays NaN. */
+static float bits_f32(uint32_t u)
+{
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+static uint32_t f32_bits(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    return u;
+}
+
 float oc_silu_f32(float x)
 {
-    if (x != x) return x;
-    const float t = -x;
-    if (t < -20.0f) return x;
-    if (t > 88.0f) return -0.0f;
-    return x / (1.0f + oc_exp_f32_seq(t));
+    const float t = fminf(fmaxf(-x, -20.0f), 80.0f);
+    const float d = 1.0f + oc_exp_f32_seq(t);
+    float y = bits_f32(0x7EF311C3u - f32_bits(d));
+    for (int i = 0; i < 3; ++i) {
+        const float q = fmaf(-d, y, 1.0f);
+        y = fmaf(y, q, y);
+    }
+    return x * y;
 }
 
 /* H[m][j] = bf16(SiLU(g) * u), g and u the bf16 gate and up values of
