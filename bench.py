@@ -50,7 +50,7 @@ def parse():
     ap.add_argument("--workload", default="qkv",
                     choices=["qkv", "mlp", "backward", "backward_dual", "dual_x", "nvfp4_global", "nvfp4_tile",
                              "nvfp4_chain", "nvfp4_chain_2pass", "nvfp4_wgrad", "mlp_chain", "mlp_chain_fused",
-                             "copy"],
+                             "mlp_swiglu", "mlp_swiglu_fused", "copy"],
                     help="copy = a plain 1 GiB device copy: the HBM reference for counter scaling")
     ap.add_argument("--copies", type=int, default=4, help="input copies rotated across steps (cold producers)")
     ap.add_argument("--layout", default="tiled", choices=["tiled", "linear"],
@@ -268,6 +268,56 @@ def build_workload(name, dev, copies, layout_name="tiled"):
                            ("quantized in GEMM1's epilogue" if fused else "written in bf16 and quantized by the producer"),
                "gemm1_mnk": [M, N1, K], "gemm2_mnk": [M, N2, N1], "layout": layout_name, "input_copies": copies}
         return cfg, ops, 2.0 * M * N1 * K + 2.0 * M * N2 * N1
+    if name in ("mlp_swiglu", "mlp_swiglu_fused"):
+        # the whole MLP forward: gate/up GEMM, SwiGLU, down GEMM (tiled
+        # layout; the gate/up weight's rows are taken as gate and up
+        # interleaved in groups of 32, the layout the fused epilogue reads).
+        # mlp_swiglu writes C in bf16, applies fp4_swiglu_bf16 and quantizes
+        # H; mlp_swiglu_fused has GEMM1's epilogue apply SwiGLU and write H
+        # as GEMM2's MXFP4 operand (fp4_gemm_mx_swiglu_quant)
+        fused = name == "mlp_swiglu_fused"
+        X = gen("mlp_gate_up", "X", copies)
+        W1 = gen("mlp_gate_up", "W", copies)
+        W2 = gen("mlp_down", "W", copies)
+        M, K = X[0].shape
+        N1, N2 = W1[0].shape[0], W2[0].shape[0]
+        F = N1 // 2
+        bx, bw1, bh, bw2 = mx_bufs(M, K), mx_bufs(N1, K), mx_bufs(M, F), mx_bufs(N2, F)
+        C1 = None if fused else torch.empty((M, N1), dtype=torch.bfloat16, device=dev)
+        H = None if fused else torch.empty((M, F), dtype=torch.bfloat16, device=dev)
+        C2 = torch.empty((M, N2), dtype=torch.bfloat16, device=dev)
+        ops = [
+            ("quantize X", qk, lambda s: B.fp4_quantize_mx(X[s % copies], codes=bx[0], scales=bx[1], layout=L),
+             M * K * MX_BYTES_PER_ELEM, "GB/s", HBM_PEAK_GBS, "hbm"),
+            ("quantize W_gate_up", qk,
+             lambda s: B.fp4_quantize_mx(W1[s % copies], codes=bw1[0], scales=bw1[1], layout=L),
+             N1 * K * MX_BYTES_PER_ELEM, "GB/s", HBM_PEAK_GBS, "hbm"),
+        ]
+        if fused:
+            ops.append(("GEMM gate/up -> SwiGLU -> MXFP4 H (fused)", "gemm_mx_kernel",
+                        lambda s: B.fp4_gemm_mx_swiglu_quant(*bx, *bw1, layout=L, m=M, n=N1, h_layout=L,
+                                                             codes=bh[0], scales=bh[1]),
+                        2.0 * M * N1 * K, "TFLOP/s", FP4_PEAK_TFLOPS, "mfma"))
+        else:
+            ops += [("GEMM gate/up -> bf16 C", "gemm_mx_kernel",
+                     lambda s: B.fp4_gemm_mx(*bx, *bw1, c=C1, layout=L, m=M, n=N1), 2.0 * M * N1 * K, "TFLOP/s",
+                     FP4_PEAK_TFLOPS, "mfma"),
+                    ("SwiGLU C -> bf16 H", "swiglu_kernel", lambda s: B.fp4_swiglu_bf16(C1, F, pair=32, h=H),
+                     M * F * 6, "GB/s", HBM_PEAK_GBS, "hbm"),
+                    ("quantize H", qk, lambda s: B.fp4_quantize_mx(H, codes=bh[0], scales=bh[1], layout=L),
+                     M * F * MX_BYTES_PER_ELEM, "GB/s", HBM_PEAK_GBS, "hbm")]
+        ops += [
+            ("quantize W_down", qk, lambda s: B.fp4_quantize_mx(W2[s % copies], codes=bw2[0], scales=bw2[1], layout=L),
+             N2 * F * MX_BYTES_PER_ELEM, "GB/s", HBM_PEAK_GBS, "hbm"),
+            ("GEMM down H W_down^T -> bf16", "gemm_mx_kernel",
+             lambda s: B.fp4_gemm_mx(*bh, *bw2, c=C2, layout=L, m=M, n=N2), 2.0 * M * N2 * F, "TFLOP/s",
+             FP4_PEAK_TFLOPS, "mfma"),
+        ]
+        cfg = {"workload": "Llama-3-8B MLP forward, MXFP4: gate/up GEMM, SwiGLU, down GEMM; H " +
+                           ("made and quantized in the gate/up GEMM's epilogue" if fused
+                            else "via bf16 C, the SwiGLU kernel and the producer"),
+               "gemm1_mnk": [M, N1, K], "gemm2_mnk": [M, N2, F], "layout": layout_name, "input_copies": copies}
+        return cfg, ops, 2.0 * M * N1 * K + 2.0 * M * N2 * F
     if name == "nvfp4_wgrad":
         # the o_proj weight gradient in NVFP4 (per-tile domain): dY^T and X^T
         # quantized along tokens with the fixed-sign Hadamard (SR on dY), then

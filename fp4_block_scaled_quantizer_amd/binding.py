@@ -65,6 +65,8 @@ def lib() -> ctypes.CDLL:
     L.fp4_gemm_nv.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, i64, i64, f32, i32, vp, i32, i64, vp]
     L.fp4_gemm_mx_amax.argtypes = [vp, vp, vp, vp, i64, i64, i64, f32, i32, vp, i32, i64, vp, vp]
     L.fp4_gemm_mx_quant.argtypes = [vp, vp, vp, vp, i64, i64, i64, f32, i32, vp, vp, i32, vp]
+    L.fp4_gemm_mx_swiglu_quant.argtypes = [vp, vp, vp, vp, i64, i64, i64, f32, i32, vp, vp, i32, vp]
+    L.fp4_swiglu_bf16.argtypes = [vp, i64, i64, i64, i64, vp, i64, vp]
     L.fp4_gemm_nv_amax.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, i64, i64, f32, i32, vp, i32, i64, vp, vp]
     L.fp4_quantize_nv_amax.argtypes = [vp, i64, i64, i64, i32, u64, u32, vp, vp, vp, vp, vp]
     L.fp4_hadamard32_quantize_nv.argtypes = [vp, i64, i64, i64, i32, u32, i32, u64, u32, i32, vp, vp, vp, vp,
@@ -285,6 +287,52 @@ def fp4_gemm_mx_quant(a_codes: torch.Tensor, a_scales: torch.Tensor, b_codes: to
                                    M, N, K, float(alpha), layout, codes.data_ptr(), scales.data_ptr(), c_layout,
                                    _stream(stream)))
     return codes, scales
+
+
+def fp4_gemm_mx_swiglu_quant(a_codes: torch.Tensor, a_scales: torch.Tensor, b_codes: torch.Tensor,
+                             b_scales: torch.Tensor, *, alpha: float = 1.0, layout: int = LAYOUT_LINEAR,
+                             m: Optional[int] = None, n: Optional[int] = None, h_layout: int = LAYOUT_LINEAR,
+                             codes: Optional[torch.Tensor] = None, scales: Optional[torch.Tensor] = None,
+                             stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """H = SwiGLU(alpha * A B^T) written as an MXFP4 operand along rows in
+    h_layout; B's n = 2F rows interleave gate and up rows in groups of 32
+    (pair_gate_up).  Returns (codes, scales) of H [m x F]."""
+    M = a_codes.shape[0] if m is None else m
+    N = b_codes.shape[0] if n is None else n
+    K = a_codes.shape[1] * 2
+    if b_codes.shape[1] * 2 != K:
+        raise ValueError("A and B must have the same K")
+    codes, scales = _mx_outputs(M, N // 2, h_layout, codes, scales, a_codes.device)
+    _check("fp4_gemm_mx_swiglu_quant",
+           lib().fp4_gemm_mx_swiglu_quant(a_codes.data_ptr(), a_scales.data_ptr(), b_codes.data_ptr(),
+                                          b_scales.data_ptr(), M, N, K, float(alpha), layout, codes.data_ptr(),
+                                          scales.data_ptr(), h_layout, _stream(stream)))
+    return codes, scales
+
+
+def fp4_swiglu_bf16(c: torch.Tensor, f: int, *, pair: int = 32, h: Optional[torch.Tensor] = None,
+                    stream=None) -> torch.Tensor:
+    """h = bf16(SiLU(gate) * up) from a bf16 C [M x >= 2f] whose columns
+    interleave gate and up in groups of `pair` columns."""
+    if c.dtype != torch.bfloat16 or c.dim() != 2 or c.stride(1) != 1:
+        raise ValueError("c must be a 2-D bf16 tensor with contiguous rows")
+    M = c.shape[0]
+    if h is None:
+        h = torch.empty((M, f), dtype=torch.bfloat16, device=c.device)
+    _check("fp4_swiglu_bf16", lib().fp4_swiglu_bf16(c.data_ptr(), M, f, c.stride(0), pair, h.data_ptr(),
+                                                    h.stride(0), _stream(stream)))
+    return h
+
+
+def pair_gate_up(w_gate: torch.Tensor, w_up: torch.Tensor, pair: int = 32) -> torch.Tensor:
+    """The gate/up weight in the row order fp4_gemm_mx_swiglu_quant takes:
+    rows 2 pair b .. + pair-1 = gate rows pair b .., the next pair rows the
+    up rows of the same units (a one-time layout of the weight, like the
+    tiled operand layout)."""
+    F, K = w_gate.shape
+    if w_up.shape != (F, K) or F % pair != 0:
+        raise ValueError("gate and up must have the same [F x K] shape, F a multiple of pair")
+    return torch.stack([w_gate.reshape(F // pair, pair, K), w_up.reshape(F // pair, pair, K)], dim=1).reshape(2 * F, K)
 
 
 def fp4_gemm_nv(a_codes: torch.Tensor, a_scales: torch.Tensor, a_tensor_scale: torch.Tensor, b_codes: torch.Tensor,

@@ -18,7 +18,7 @@ ROOT = os.path.dirname(HERE)
 OUT = os.path.join(HERE, "libfp4q.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["quant.hip", "gemm_mx.hip", "gemm_nv.hip", "fp4q_api.hip"]
+SOURCES = ["quant.hip", "gemm_mx.hip", "gemm_nv.hip", "swiglu.hip", "fp4q_api.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

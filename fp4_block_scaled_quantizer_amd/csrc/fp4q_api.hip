@@ -152,26 +152,28 @@ fp4q_status run_gemm_mx(const void *a_codes, const void *a_scales, const void *b
 
 // MX GEMM whose C leaves as an MXFP4 operand along rows (codes + E8M0
 // scales in c_layout) instead of as bf16 / fp32.
+// swiglu: the output is SwiGLU(C) (N / 2 columns) instead of C
 fp4q_status run_gemm_mx_quant(const void *a_codes, const void *a_scales, const void *b_codes, const void *b_scales,
                               int64_t M, int64_t N, int64_t K, float alpha, int layout, void *c_codes,
-                              void *c_scales, int c_layout, void *stream)
+                              void *c_scales, int c_layout, bool swiglu, void *stream)
 {
     if ((layout != FP4Q_LAYOUT_LINEAR && layout != FP4Q_LAYOUT_TILED) ||
         (c_layout != FP4Q_LAYOUT_LINEAR && c_layout != FP4Q_LAYOUT_TILED))
         return FP4Q_EINVAL;
     const bool tiled = layout == FP4Q_LAYOUT_TILED, ctiled = c_layout == FP4Q_LAYOUT_TILED;
     if (M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return FP4Q_ESHAPE;
-    if (K % 128 != 0 || N % (ctiled ? 128 : 32) != 0) return FP4Q_ESHAPE;
+    if (K % 128 != 0 || N % ((ctiled ? 128 : 32) * (swiglu ? 2 : 1)) != 0) return FP4Q_ESHAPE;
+    const int64_t Nq = swiglu ? N / 2 : N;  // the quantized output's columns
     const uint64_t Ms = tiled ? (uint64_t)(M + 31) / 32 * 32 : (uint64_t)M;
     const uint64_t Ns = tiled ? (uint64_t)(N + 31) / 32 * 32 : (uint64_t)N;
     const uint64_t Mq = ctiled ? (uint64_t)(M + 31) / 32 * 32 : (uint64_t)M;  // stored output rows
     if (Ms * (uint64_t)K / 2 >= (1ull << 32) || Ns * (uint64_t)K / 2 >= (1ull << 32) ||
-        Mq * (uint64_t)N / 2 >= (1ull << 32))
+        Mq * (uint64_t)Nq / 2 >= (1ull << 32))
         return FP4Q_ESHAPE;
     if (M == 0 || N == 0) return FP4Q_OK;
     if (!c_codes || !c_scales) return FP4Q_EINVAL;
     if (!aligned(c_codes, 16) || !aligned(c_scales, 4)) return FP4Q_EALIGN;
-    const Range oc = bytes(c_codes, Mq * N / 2), os = bytes(c_scales, Mq * N / 32);
+    const Range oc = bytes(c_codes, Mq * Nq / 2), os = bytes(c_scales, Mq * Nq / 32);
     if (overlap(oc, os)) return FP4Q_EINVAL;
     if (K > 0) {
         if (!a_codes || !a_scales || !b_codes || !b_scales) return FP4Q_EINVAL;
@@ -197,6 +199,7 @@ fp4q_status run_gemm_mx_quant(const void *a_codes, const void *a_scales, const v
     g.q_codes = c_codes;
     g.q_scales = c_scales;
     g.q_tiled = ctiled;
+    g.q_swiglu = swiglu;
     (void)hipGetLastError();
     return launched(fp4q::launch_gemm_mx(g, as_stream(stream)));
 }
@@ -404,7 +407,32 @@ fp4q_status fp4_gemm_mx_quant(const void *a_codes, const void *a_scales, const v
                               int c_layout, void *stream)
 {
     return run_gemm_mx_quant(a_codes, a_scales, b_codes, b_scales, M, N, K, alpha, layout, c_codes, c_scales,
-                             c_layout, stream);
+                             c_layout, false, stream);
+}
+
+fp4q_status fp4_gemm_mx_swiglu_quant(const void *a_codes, const void *a_scales, const void *b_codes,
+                                     const void *b_scales, int64_t M, int64_t N, int64_t K, float alpha, int layout,
+                                     void *h_codes, void *h_scales, int h_layout, void *stream)
+{
+    return run_gemm_mx_quant(a_codes, a_scales, b_codes, b_scales, M, N, K, alpha, layout, h_codes, h_scales,
+                             h_layout, true, stream);
+}
+
+fp4q_status fp4_swiglu_bf16(const void *c, int64_t M, int64_t F, int64_t ldc, int64_t pair, void *h, int64_t ldh,
+                            void *stream)
+{
+    if (M < 0 || F < 0 || M > kMaxDim || F > kMaxDim) return FP4Q_ESHAPE;
+    if (F % 8 != 0 || pair <= 0 || pair % 8 != 0 || (F > 0 && F % pair != 0) || ldc < 2 * F || ldh < F ||
+        ldc % 8 != 0 || ldh % 8 != 0 || ldc > kMaxDim * 2 || ldh > kMaxDim)
+        return FP4Q_ESHAPE;
+    if (M == 0 || F == 0) return FP4Q_OK;
+    if (!c || !h) return FP4Q_EINVAL;
+    if (!aligned(c, 16) || !aligned(h, 16)) return FP4Q_EALIGN;
+    const Range rc = bytes(c, ((uint64_t)(M - 1) * (uint64_t)ldc + 2 * (uint64_t)F) * 2);
+    const Range rh = bytes(h, ((uint64_t)(M - 1) * (uint64_t)ldh + (uint64_t)F) * 2);
+    if (overlap(rc, rh)) return FP4Q_EINVAL;
+    (void)hipGetLastError();
+    return launched(fp4q::launch_swiglu(c, M, F, ldc, pair, h, ldh, as_stream(stream)));
 }
 
 fp4q_status fp4_gemm_nv(const void *a_codes, const void *a_scales, const float *a_tensor_scale, const void *b_codes,

@@ -32,6 +32,49 @@ FP4Q_HD uint32_t f32_to_bf16_rne(float f)
     return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
+// SiLU(x) = x / (1 + e^-x) (SwiGLU's gate activation; Shazeer, "GLU Variants
+// Improve Transformer") in binary32 as one fixed sequence of IEEE operations,
+// so that every implementation of the sequence returns the same bits (the
+// activation feeds the MX producer of H, whose codes must be reproducible);
+// fused multiply-adds are explicit (one rounding each), nothing else is
+// contracted (the library is built with contraction off).
+//   e^t, t in [-20, 80]: Cody-Waite reduction k = rint(t log2 e) (half to
+//   even), r = fma(-k, ln2_hi, t) (exact: ln2_hi has 15 significant bits),
+//   r = fma(-k, ln2_lo, r); the degree-7 Taylor polynomial of e^r by Horner
+//   with fma; times 2^k (exact).
+//   SiLU: t = min(max(-x, -20), 80) (NaN -> -20); d = 1 + e^t; y = the bit
+//   pattern 0x7EF311C3 - bits(d) (within 5.1 % of 1/d), three Newton steps
+//   q = fma(-d, y, 1), y = fma(y, q, y); SiLU = x * y.  So SiLU(x) = x
+//   exactly above 20, x / (1 + e^80) below -80, NaN stays NaN.
+FP4Q_HD float exp_seq_f32(float t)
+{
+    const float k = __builtin_rintf(t * 0x1.715476p+0f);
+    float r = __builtin_fmaf(-k, 0x1.62e4p-1f, t);
+    r = __builtin_fmaf(-k, 0x1.7f7d1cp-20f, r);
+    float p = 0x1.a01a02p-13f;                   // 1/5040
+    p = __builtin_fmaf(p, r, 0x1.6c16c2p-10f);   // 1/720
+    p = __builtin_fmaf(p, r, 0x1.111112p-7f);    // 1/120
+    p = __builtin_fmaf(p, r, 0x1.555556p-5f);    // 1/24
+    p = __builtin_fmaf(p, r, 0x1.555556p-3f);    // 1/6
+    p = __builtin_fmaf(p, r, 0.5f);
+    p = __builtin_fmaf(p, r, 1.0f);
+    p = __builtin_fmaf(p, r, 1.0f);
+    return __builtin_ldexpf(p, (int)k);
+}
+
+FP4Q_HD float silu_f32(float x)
+{
+    const float t = __builtin_fminf(__builtin_fmaxf(-x, -20.0f), 80.0f);
+    const float d = 1.0f + exp_seq_f32(t);
+    float y = u2f(0x7EF311C3u - f2u(d));
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+        const float q = __builtin_fmaf(-d, y, 1.0f);
+        y = __builtin_fmaf(y, q, y);
+    }
+    return x * y;
+}
+
 // E2M1 stochastic rounding ([Fusion] section "Two Key Numerical Techniques":
 // up or down with probability proportional to the distance).  The grid step
 // is g = 0.5 below 2, 1 in [2, 4), 2 in [4, 6); with t = |y| / g, f its

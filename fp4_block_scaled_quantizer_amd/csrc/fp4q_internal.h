@@ -39,9 +39,12 @@ struct GemmArgs {
     bool c_bf16;
     int64_t ldc;
     uint32_t *c_amax;  // optional: max |C| as stored, folded in as binary32 bits
-    // MX only, optional: C written as an MXFP4 operand along rows instead
+    // MX only, optional: C written as an MXFP4 operand along rows instead;
+    // with q_swiglu, SwiGLU(C) (N / 2 columns: gate and up columns of C
+    // interleaved in groups of 32)
     void *q_codes, *q_scales;
     bool q_tiled;
+    bool q_swiglu;
 };
 
 int launch_quant_mx(const QuantArgs &a, hipStream_t st);
@@ -52,5 +55,9 @@ int launch_quant_nv(const QuantArgs &a, int domain, float *tensor_scale, void *w
 size_t nv_workspace_bytes(int domain);
 int launch_gemm_mx(const GemmArgs &g, hipStream_t st);
 int launch_gemm_nv(const GemmArgs &g, hipStream_t st);
+// h[m][j] = bf16(SiLU(gate) * up) from a bf16 C whose columns interleave gate
+// and up in groups of `pair` (a multiple of 8 dividing F)
+int launch_swiglu(const void *c, int64_t M, int64_t F, int64_t ldc, int64_t pair, void *h, int64_t ldh,
+                  hipStream_t st);
 
 }  // namespace fp4q

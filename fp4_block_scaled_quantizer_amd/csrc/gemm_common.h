@@ -283,17 +283,55 @@ __device__ __forceinline__ uint32_t lane_half_exchange(uint32_t v, int h)
     return h ? r[0] : r[1];
 }
 
+// One row's 32-column MX block of an epilogue output, held as bf16 pairs
+// p[r] = columns 8 (r / 2) + 4 h + 2 (r mod 2) + {0, 1} in lane h = l / 32
+// (the other 16 values in lane l ^ 32), with fmx = the largest |value|
+// before the bf16 rounding: the block amax is fmx rounded once (rounding is
+// monotonic) and exchanged with v_permlane32_swap, the codes come from the
+// producers' scaled convert, and half of them are exchanged so that lane h
+// writes bytes 8 h .. 8 h + 7 of the row's 16 code bytes, at column c of a
+// ncols-wide output (tiled: 1 KiB lane-order blocks; a padding row writes
+// zeros).  Returns the block's E8M0 byte.
+template <bool kTiled>
+__device__ __forceinline__ uint32_t emit_mx_block(const bf16x2_t (&p)[8], float fmx, int h, bool live, bool pad, int row,
+                                                  int c, int ncols, uint8_t *codes)
+{
+    uint32_t amax = (__builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){fmx, 0.0f}, bf16x2_t)) & 0xFFFFu)
+                    << 16;
+    amax = max(amax, lane_half_exchange(amax, h));
+    const uint32_t sbyte = mx_scale_byte(amax);
+    const float scale = mx_scale_f32(sbyte);
+    uint32_t grp[4];  // 4 codes (16 bits) of columns 8 g + 4 h .. + 3
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        const uint32_t r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(0u, p[2 * g], scale, 0);
+        grp[g] = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, p[2 * g + 1], scale, 1);
+    }
+    // lane h = 0 keeps groups 0, 1 of its half and takes the other half's;
+    // lane h = 1 keeps groups 2, 3
+    const uint32_t give = h ? (grp[0] | grp[1] << 16) : (grp[2] | grp[3] << 16);
+    const uint32_t got = lane_half_exchange(give, h);
+    uint2 out = h ? make_uint2((got & 0xFFFFu) | grp[2] << 16, (got >> 16) | grp[3] << 16)
+                  : make_uint2(grp[0] | got << 16, grp[1] | (got & 0xFFFF0000u));
+    if (pad) out = make_uint2(0u, 0u);
+    if (live || pad) {
+        uint8_t *dst = kTiled ? codes + ((int64_t)(row >> 5) * (ncols >> 6) + (c >> 6)) * 1024 +
+                                    ((row & 31) + 32 * ((c >> 5) & 1)) * 16 + 8 * h
+                              : codes + (int64_t)row * (ncols >> 1) + (c >> 1) + 8 * h;
+        *reinterpret_cast<uint2 *>(dst) = out;
+    }
+    return live ? sbyte : 0u;
+}
+
 // Epilogue that writes a wave's 128 x 128 block of C as an MXFP4 operand
 // along rows (the next GEMM's A operand) instead of as C itself.  Each value
 // (times alpha) is rounded to bf16 first, so the output is exactly what the
 // MX row producer makes of the bf16 C.  A row's 32-column block lies in
-// lanes l and l ^ 32 (16 values each, four groups of four columns 8 g + 4 h):
-// one exchange gives the block amax, a second the other lane's codes, after
-// which lane h writes bytes 8 h .. 8 h + 7 of the row's 16 code bytes; the
-// lane h = 0 also writes the row's four scale bytes of the 128 columns as
-// one word.  Requires N % 32 == 0 (N % 128 == 0 tiled); in the tiled layout
-// rows M .. Mp-1 are written as zero codes and zero scales, as the producers
-// write them.
+// lanes l and l ^ 32 (16 values each, four groups of four columns 8 g + 4 h),
+// written by emit_mx_block; the lane h = 0 also writes the row's four scale
+// bytes of the 128 columns as one word.  Requires N % 32 == 0 (N % 128 == 0
+// tiled); in the tiled layout rows M .. Mp-1 are written as zero codes and
+// zero scales, as the producers write them.
 template <bool kScale, bool kTiled>
 __device__ __forceinline__ void store_wave_block_mxq(const v16f_t (&acc)[4][4], int el, int row_base, int col_base,
                                                      int M, int N, int Mp, float alpha, uint8_t *codes,
@@ -314,8 +352,7 @@ __device__ __forceinline__ void store_wave_block_mxq(const v16f_t (&acc)[4][4], 
             const int c = col_base + 32 * j;
             if (c >= N) continue;  // the same for every lane
             // bf16 pairs (round to nearest even, as the bf16 epilogue
-            // stores them); the block amax is taken on the fp32 values and
-            // rounded once (rounding is monotonic)
+            // stores them); the block amax is taken on the fp32 values
             bf16x2_t p[8];
             float fmx = 0.0f;
 #pragma unroll
@@ -328,31 +365,7 @@ __device__ __forceinline__ void store_wave_block_mxq(const v16f_t (&acc)[4][4], 
                 fmx = fmaxf(fmx, fmaxf(fabsf(a0), fabsf(a1)));
                 p[r] = __builtin_convertvector((f32x2_t){a0, a1}, bf16x2_t);
             }
-            uint32_t amax =
-                (__builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){fmx, 0.0f}, bf16x2_t)) & 0xFFFFu) << 16;
-            amax = max(amax, lane_half_exchange(amax, h));
-            const uint32_t sbyte = mx_scale_byte(amax);
-            const float scale = mx_scale_f32(sbyte);
-            uint32_t grp[4];  // 4 codes (16 bits) of columns 8 g + 4 h .. + 3
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const uint32_t r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(0u, p[2 * g], scale, 0);
-                grp[g] = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, p[2 * g + 1], scale, 1);
-            }
-            // lane h = 0 keeps groups 0, 1 of its half and takes the other
-            // half's; lane h = 1 keeps groups 2, 3
-            const uint32_t give = h ? (grp[0] | grp[1] << 16) : (grp[2] | grp[3] << 16);
-            const uint32_t got = lane_half_exchange(give, h);
-            uint2 out = h ? make_uint2((got & 0xFFFFu) | grp[2] << 16, (got >> 16) | grp[3] << 16)
-                          : make_uint2(grp[0] | got << 16, grp[1] | (got & 0xFFFF0000u));
-            if (pad) out = make_uint2(0u, 0u);
-            sword |= (live ? sbyte : 0u) << (8 * j);
-            if (live || pad) {
-                uint8_t *dst = kTiled ? codes + ((int64_t)(row >> 5) * (N >> 6) + (c >> 6)) * 1024 +
-                                            ((row & 31) + 32 * ((c >> 5) & 1)) * 16 + 8 * h
-                                      : codes + (int64_t)row * (N >> 1) + (c >> 1) + 8 * h;
-                *reinterpret_cast<uint2 *>(dst) = out;
-            }
+            sword |= emit_mx_block<kTiled>(p, fmx, h, live, pad, row, c, N, codes) << (8 * j);
         }
         if (h == 0 && (live || pad)) {
             if (kTiled) {
@@ -366,6 +379,70 @@ __device__ __forceinline__ void store_wave_block_mxq(const v16f_t (&acc)[4][4], 
                     for (int j = 0; j < 4; ++j)
                         if (col_base + 32 * j < N) dst[j] = (uint8_t)(sword >> (8 * j));
                 }
+            }
+        }
+    }
+}
+
+// Epilogue that applies SwiGLU to a wave's 128 x 128 block of C and writes
+// the result H as an MXFP4 operand along rows.  The weight's rows (C's
+// columns) interleave gate and up in groups of 32, so accumulator blocks
+// j = 0, 2 hold gate columns and j = 1, 3 the up columns of the same 32
+// hidden columns, lane for lane, and the wave's 128 columns of C are the
+// 64 hidden columns hcol_base .. + 63 of H (F = N / 2 wide).  Per value:
+// g and u = alpha C rounded to bf16 (as the bf16 GEMM stores C), then
+// bf16(SiLU(g) * u) (silu_f32: the fixed binary32 sequence), then the MX
+// block of emit_mx_block -- exactly what the bf16 GEMM, the SwiGLU kernel
+// and the MX row producer compute one after another.  The lane h = 0 writes
+// the row's two scale bytes as one 16-bit word.  Requires F % 32 == 0
+// (F % 128 == 0 tiled).
+template <bool kScale, bool kTiled>
+__device__ __forceinline__ void store_wave_block_swiglu_mxq(const v16f_t (&acc)[4][4], int el, int row_base,
+                                                            int hcol_base, int M, int F, int Mp, float alpha,
+                                                            uint8_t *codes, uint8_t *scales)
+{
+    const int fr = el & 31, h = el >> 5;
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int row = row_base + 32 * i + fr;
+        const bool live = row < M;
+        const bool pad = !live && kTiled && row < Mp;
+        uint32_t sword = 0;
+#pragma unroll
+        for (int jp = 0; jp < 2; ++jp) {
+            const int c = hcol_base + 32 * jp;
+            if (c >= F) continue;  // the same for every lane
+            bf16x2_t p[8];
+            float fmx = 0.0f;
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+                float g0 = acc_read(acc[i][2 * jp][2 * r]), g1 = acc_read(acc[i][2 * jp][2 * r + 1]);
+                float u0 = acc_read(acc[i][2 * jp + 1][2 * r]), u1 = acc_read(acc[i][2 * jp + 1][2 * r + 1]);
+                if (kScale) {
+                    g0 *= alpha; g1 *= alpha; u0 *= alpha; u1 *= alpha;
+                }
+                const uint32_t gb = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){g0, g1}, bf16x2_t));
+                const uint32_t ub = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){u0, u1}, bf16x2_t));
+                const float h0 = silu_f32(bf16_lo(gb)) * bf16_lo(ub);
+                const float h1 = silu_f32(bf16_hi(gb)) * bf16_hi(ub);
+                fmx = fmaxf(fmx, fmaxf(fabsf(h0), fabsf(h1)));
+                p[r] = __builtin_convertvector((f32x2_t){h0, h1}, bf16x2_t);
+            }
+            sword |= emit_mx_block<kTiled>(p, fmx, h, live, pad, row, c, F, codes) << (8 * jp);
+        }
+        if (h == 0 && (live || pad)) {
+            if (kTiled) {
+                // bytes 2 (hcol_base / 64 mod 2) .. +1 of the row's word of
+                // the 128-column step
+                *reinterpret_cast<uint16_t *>(scales + ((int64_t)(hcol_base >> 7) * Mp + row) * 4 +
+                                              ((hcol_base >> 5) & 2)) = (uint16_t)sword;
+            } else {
+                uint8_t *dst = scales + (int64_t)row * (F >> 5) + (hcol_base >> 5);
+                if (hcol_base + 64 <= F)
+                    *reinterpret_cast<uint16_t *>(dst) = (uint16_t)sword;
+                else
+                    dst[0] = (uint8_t)sword;
             }
         }
     }
@@ -386,6 +463,24 @@ __device__ __forceinline__ void store_wave_block_mxq_any(const v16f_t (&acc)[4][
             store_wave_block_mxq<true, false>(acc, el, row_base, col_base, M, N, Mp, alpha, codes, scales);
         else
             store_wave_block_mxq<false, false>(acc, el, row_base, col_base, M, N, Mp, alpha, codes, scales);
+    }
+}
+
+// The SwiGLU epilogue for a runtime alpha and output layout.
+__device__ __forceinline__ void store_wave_block_swiglu_mxq_any(const v16f_t (&acc)[4][4], int el, int row_base,
+                                                                int hcol_base, int M, int F, int Mp, float alpha,
+                                                                uint8_t *codes, uint8_t *scales, bool tiled)
+{
+    if (tiled) {
+        if (alpha != 1.0f)
+            store_wave_block_swiglu_mxq<true, true>(acc, el, row_base, hcol_base, M, F, Mp, alpha, codes, scales);
+        else
+            store_wave_block_swiglu_mxq<false, true>(acc, el, row_base, hcol_base, M, F, Mp, alpha, codes, scales);
+    } else {
+        if (alpha != 1.0f)
+            store_wave_block_swiglu_mxq<true, false>(acc, el, row_base, hcol_base, M, F, Mp, alpha, codes, scales);
+        else
+            store_wave_block_swiglu_mxq<false, false>(acc, el, row_base, hcol_base, M, F, Mp, alpha, codes, scales);
     }
 }
 

@@ -65,7 +65,10 @@ constexpr int kDmaB = kDmaPerStage - kDmaA;
 // Between two tiles the next tile's first two K steps are put in flight
 // before the finished tile's epilogue runs, so the epilogue hides the start
 // latency of the next tile.
-template <bool kTiled, bool kQuantOut>
+// kOut: 0 writes C (bf16 or fp32); 1 writes C as an MXFP4 operand along
+// rows; 2 writes SwiGLU(C) (gate and up columns interleaved in groups of 32)
+// as an MXFP4 operand along rows.
+template <bool kTiled, int kOut>
 __global__ __launch_bounds__(256) void gemm_mx_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
                                                       const uint8_t *__restrict__ B, const uint8_t *__restrict__ Bs,
                                                       int M, int N, int K, float alpha, void *__restrict__ C,
@@ -353,9 +356,12 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(const uint8_t *__restrict_
         // whole vector-memory counter (the next tile's DMA included).
         int el;
         asm volatile("v_mov_b32 %0, %1" : "=v"(el) : "v"(lane));
-        if constexpr (kQuantOut)  // C leaves as the next GEMM's MXFP4 operand
+        if constexpr (kOut == 1)  // C leaves as the next GEMM's MXFP4 operand
             store_wave_block_mxq_any(acc, el, row_base, col_base, M, N, q_tiled ? (int)Mp : M, alpha, q_codes,
                                      q_scales, q_tiled != 0);
+        else if constexpr (kOut == 2)  // so does SwiGLU(C), N / 2 columns wide
+            store_wave_block_swiglu_mxq_any(acc, el, row_base, col_base >> 1, M, N >> 1, q_tiled ? (int)Mp : M, alpha,
+                                            q_codes, q_scales, q_tiled != 0);
         else
             store_wave_block_any(acc, ep, el, row_base, col_base, M, N, alpha, C, ldc, c_bf16 != 0, vec_ok != 0,
                                  c_amax);
@@ -372,9 +378,10 @@ int launch_gemm_mx(const GemmArgs &g, hipStream_t st)
     if (M == 0 || N == 0) return 0;
     auto *q_codes = reinterpret_cast<uint8_t *>(g.q_codes);
     auto *q_scales = reinterpret_cast<uint8_t *>(g.q_scales);
-    if (K == 0 && q_codes) {
+    if (K == 0 && q_codes) {  // C = 0 and SwiGLU(0) = 0: zero codes and scales
         const int64_t ms = g.q_tiled ? (M + 31) / 32 * 32 : M;
-        const int64_t nc = ms * N / 2, ns = ms * N / 32;
+        const int64_t cols = g.q_swiglu ? N / 2 : N;  // the quantized output's width
+        const int64_t nc = ms * cols / 2, ns = ms * cols / 32;
         hipLaunchKernelGGL(fill_bytes_zero_kernel, dim3((unsigned)((nc + 255) / 256)), dim3(256), 0, st, q_codes, nc);
         hipLaunchKernelGGL(fill_bytes_zero_kernel, dim3((unsigned)((ns + 255) / 256)), dim3(256), 0, st, q_scales, ns);
         return hipGetLastError() == hipSuccess ? 0 : 1;
@@ -404,10 +411,11 @@ int launch_gemm_mx(const GemmArgs &g, hipStream_t st)
 #define FP4Q_GEMM_MX(T, Q)                                                                                     \
     hipLaunchKernelGGL((gemm_mx_kernel<T, Q>), dim3(grid), dim3(256), 0, st, a, as, b, bs, M, N, K, g.alpha, g.c, \
                        g.ldc, (int)g.c_bf16, vec_ok, tiles_m, tiles_n, g.c_amax, q_codes, q_scales, (int)g.q_tiled)
+    const int out = !q_codes ? 0 : g.q_swiglu ? 2 : 1;
     if (g.tiled) {
-        if (q_codes) FP4Q_GEMM_MX(true, true); else FP4Q_GEMM_MX(true, false);
+        if (out == 2) FP4Q_GEMM_MX(true, 2); else if (out == 1) FP4Q_GEMM_MX(true, 1); else FP4Q_GEMM_MX(true, 0);
     } else {
-        if (q_codes) FP4Q_GEMM_MX(false, true); else FP4Q_GEMM_MX(false, false);
+        if (out == 2) FP4Q_GEMM_MX(false, 2); else if (out == 1) FP4Q_GEMM_MX(false, 1); else FP4Q_GEMM_MX(false, 0);
     }
 #undef FP4Q_GEMM_MX
     return hipGetLastError() == hipSuccess ? 0 : 1;

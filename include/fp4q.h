@@ -244,6 +244,41 @@ FP4Q_API fp4q_status fp4_gemm_mx_quant(const void *a_codes, const void *a_scales
                               const void *b_scales, int64_t M, int64_t N, int64_t K, float alpha, int layout,
                               void *c_codes, void *c_scales, int c_layout, void *stream);
 
+/* SwiGLU of a bf16 gate/up GEMM output (the activation before the MX
+ * producer of the MLP's hidden operand H; [Fusion] section "The Design
+ * Philosophy of Format-Aware Fusion": the producer is fused with the op that
+ * makes its input -- this is that op on its own).  c: bf16 [M x >= 2F],
+ * row pitch ldc elements, whose columns interleave gate and up in groups of
+ * `pair` columns (gate column j at 2 pair (j / pair) + j mod pair, its up
+ * column `pair` further; pair = 32 is the layout fp4_gemm_mx_swiglu_quant
+ * takes, pair = F the plain [gate | up]).  h: bf16 [M x F], pitch ldh:
+ * h[m][j] = bf16(SiLU(g) * u), SiLU(x) = x / (1 + e^-x) with e^t evaluated by
+ * one fixed binary32 sequence (Cody-Waite reduction with a two-part ln 2,
+ * degree-7 Horner polynomial, scaling by 2^k; x itself for x > 20, -0 for
+ * x < -88), a correctly rounded division and one binary32 product rounded to
+ * nearest even.  Requires F % 8 == 0, pair % 8 == 0, F % pair == 0,
+ * ldc >= 2F and ldh >= F both multiples of 8 (FP4Q_ESHAPE), c and h 16-byte
+ * aligned (FP4Q_EALIGN), h not overlapping c (FP4Q_EINVAL). */
+FP4Q_API fp4q_status fp4_swiglu_bf16(const void *c, int64_t M, int64_t F, int64_t ldc, int64_t pair, void *h,
+                            int64_t ldh, void *stream);
+
+/* MXFP4 gate/up GEMM whose output leaves as SwiGLU(C) quantized along rows:
+ * the MLP's hidden operand H for the down projection, with neither the
+ * bf16 C nor the bf16 H written ([Fusion] sections "Why FP4 Speedups Often
+ * Remain Theoretical" and "The Design Philosophy of Format-Aware Fusion").
+ * B's N rows (N = 2F) interleave the gate and up weight rows in groups of 32
+ * (B rows 64 b .. 64 b + 31 = gate rows 32 b .. 32 b + 31, the next 32 = the
+ * up rows of the same hidden units), so that each 32-column gate block of C
+ * shares the accumulator lanes of its up block.  h_codes / h_scales: H
+ * [M x F] exactly as fp4_quantize_mx (FP4Q_ALONG_ROWS, FP4Q_RNE, h_layout)
+ * writes it for the bf16 H that fp4_gemm_mx (bf16 C) followed by
+ * fp4_swiglu_bf16 (pair 32) produces.  A, B in `layout`; requires K % 128
+ * == 0 and N % 64 == 0 (linear output) or N % 256 == 0 (tiled output, rows
+ * padded to 32 with zero codes and scales).  Errors as fp4_gemm_mx_quant. */
+FP4Q_API fp4q_status fp4_gemm_mx_swiglu_quant(const void *a_codes, const void *a_scales, const void *b_codes,
+                                     const void *b_scales, int64_t M, int64_t N, int64_t K, float alpha,
+                                     int layout, void *h_codes, void *h_scales, int h_layout, void *stream);
+
 /* The GEMMs above, also reporting max |C| for a following NVFP4 "global
  * nvfp" quantization of C, so that it needs no amax pass over C (the amax is
  * produced by the op before the quantizer: [Fusion] section "The Design

@@ -21,6 +21,10 @@ void h_e4m3_batch(const float *z, uint8_t *out, size_t n)
 {
     for (size_t i = 0; i < n; ++i) out[i] = (uint8_t)fp4q::e4m3_rne_satfinite(z[i]);
 }
+void h_silu_batch(const float *x, float *out, size_t n)
+{
+    for (size_t i = 0; i < n; ++i) out[i] = fp4q::silu_f32(x[i]);
+}
 void h_e2m1_sr_batch(const float *y, const uint32_t *r, uint8_t *out, size_t n)
 {
     for (size_t i = 0; i < n; ++i) out[i] = (uint8_t)fp4q::e2m1_sr(y[i], r[i]);

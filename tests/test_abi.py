@@ -27,7 +27,8 @@ def test_exports_every_declared_function():
     names = B.declared_functions()
     assert set(names) >= {"fp4_quantize_mx", "fp4_quantize_nv", "fp4_hadamard32_quantize", "fp4_quantize_mx_dual",
                           "fp4_quantize_nv_amax", "fp4_hadamard32_quantize_nv", "fp4_gemm_mx", "fp4_gemm_nv",
-                          "fp4_gemm_mx_amax", "fp4_gemm_nv_amax", "fp4_gemm_mx_quant"}
+                          "fp4_gemm_mx_amax", "fp4_gemm_nv_amax", "fp4_gemm_mx_quant", "fp4_gemm_mx_swiglu_quant",
+                          "fp4_swiglu_bf16"}
     for n in names:
         assert hasattr(L, n), n
     assert B.abi_version() == 1
@@ -229,3 +230,45 @@ def test_gemm_mx_quant_status_codes():
     assert g(scales=CODES2 + 16) == B.EINVAL   # output codes and scales overlap
     assert g(codes=CODES + 64) == B.EINVAL     # output overlaps an input
     assert g(M=0) == B.OK
+
+
+def test_gemm_mx_swiglu_quant_status_codes():
+    def g(M=64, N=128, K=128, layout=0, hl=0, codes=CODES2, scales=SCALES2, a=CODES):
+        return L.fp4_gemm_mx_swiglu_quant(a, SCALES, X, C, M, N, K, 1.0, layout, codes, scales, hl, None)
+
+    assert g() in (B.OK, B.ELAUNCH)      # valid (no GPU here: the launch fails)
+    assert g(N=256, hl=1) in (B.OK, B.ELAUNCH)
+    assert g(layout=2) == B.EINVAL
+    assert g(hl=2) == B.EINVAL
+    assert g(K=96) == B.ESHAPE           # K % 128
+    assert g(N=96) == B.ESHAPE           # N % 64: F = N / 2 a multiple of 32 (linear output)
+    assert g(N=128, hl=1) == B.ESHAPE    # N % 256: F a multiple of 128 (tiled output)
+    assert g(M=-1) == B.ESHAPE
+    assert g(codes=None) == B.EINVAL
+    assert g(a=None) == B.EINVAL
+    assert g(codes=CODES2 + 8) == B.EALIGN
+    assert g(scales=SCALES2 + 2) == B.EALIGN
+    assert g(scales=CODES2 + 16) == B.EINVAL   # output codes and scales overlap
+    assert g(codes=CODES + 64) == B.EINVAL     # output overlaps an input
+    assert g(M=0) == B.OK
+
+
+def test_swiglu_status_codes():
+    def s(M=16, F=64, ldc=128, pair=32, h=C, ldh=64, c=X):
+        return L.fp4_swiglu_bf16(c, M, F, ldc, pair, h, ldh, None)
+
+    assert s() in (B.OK, B.ELAUNCH)
+    assert s(pair=64) in (B.OK, B.ELAUNCH)
+    assert s(F=60, ldc=120, ldh=64) == B.ESHAPE   # F % 8
+    assert s(pair=12) == B.ESHAPE                 # pair % 8
+    assert s(pair=48) == B.ESHAPE                 # pair does not divide F
+    assert s(ldc=120) == B.ESHAPE                 # ldc < 2F
+    assert s(ldh=56) == B.ESHAPE                  # ldh < F
+    assert s(ldc=132) == B.ESHAPE                 # ldc % 8
+    assert s(M=-1) == B.ESHAPE
+    assert s(c=None) == B.EINVAL
+    assert s(h=None) == B.EINVAL
+    assert s(c=X + 8) == B.EALIGN
+    assert s(h=C + 2) == B.EALIGN
+    assert s(h=X + 64) == B.EINVAL                # h overlaps c
+    assert s(M=0) == B.OK

@@ -13,6 +13,7 @@ import oracle
 from tests import second_formulation as sf
 
 HERE = os.path.dirname(os.path.abspath(__file__))
+ALL_BF16_BITS = np.arange(65536, dtype=np.uint32).astype(np.uint16)
 CSRC = os.path.join(os.path.dirname(HERE), "fp4_block_scaled_quantizer_amd", "csrc")
 
 
@@ -38,6 +39,7 @@ def H(tmp_path_factory):
     L.h_philox.argtypes = [u32] * 6 + [ctypes.POINTER(u32)]
     L.h_e4m3_batch.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t]
     L.h_e2m1_sr_batch.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t]
+    L.h_silu_batch.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t]
     return L
 
 
@@ -122,3 +124,16 @@ def test_bf16_rne_output_conversion(H):
     want = sf.f32_to_bf16_bits_rne(v)
     got = np.array([H.h_f32_to_bf16_rne(float(x)) for x in v], dtype=np.uint16)
     assert np.array_equal(got, want)
+
+
+def test_silu_matches_oracle_bitwise(H):
+    # every finite bf16 value (the activation reads bf16 GEMM outputs) and
+    # random binary32 values across the exponential's domain edges
+    f = sf.bf16_to_f32(ALL_BF16_BITS)
+    rng = np.random.default_rng(5)
+    x = np.concatenate([f[np.isfinite(f)], rng.uniform(-90, 90, 50000),
+                        np.float32([-88.0, -88.00001, -20.0, -19.99999, 20.0, 20.00001, 1e-40, -1e-40])]).astype(np.float32)
+    got = np.zeros_like(x)
+    H.h_silu_batch(x.ctypes.data, got.ctypes.data, x.size)
+    want = np.array([oracle.silu_f32(float(v)) for v in x], dtype=np.float32)
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
