@@ -40,7 +40,7 @@ def test_swiglu_matches_oracle(M, F, pair, pad):
 
 def test_swiglu_special_values():
     # every bf16 bit pattern that is finite as the gate, against up values
-    # of both signs, small and large: covers -0, subnormals, the -88 / 20
+    # of both signs, small and large: covers -0, subnormals, the -80 / 20
     # cut-offs and overflow of the product
     dev = device()
     announce("swiglu all finite bf16 gates")
@@ -155,3 +155,11 @@ def test_gemm_swiglu_quant_full_size_mlp_gate_up():
     torch.cuda.synchronize()
     assert_bytes_equal(np_u8(scales), np_u8(rs), "scales")
     assert_bytes_equal(np_u8(codes), np_u8(rc), "codes")
+    # the SwiGLU stage of that chain against the oracle on sampled rows of
+    # the full-size bf16 C
+    c16 = B.fp4_gemm_mx(*a, *b, out_dtype=torch.bfloat16, layout=L, m=M, n=N)
+    h = B.fp4_swiglu_bf16(c16, N // 2, pair=32)
+    rows = torch.tensor([0, 1, 255, 256, 4097, 8190, 8191], device=dev)
+    want = oracle.swiglu_bf16(bf16_bits_of(c16[rows]), N // 2, 32)
+    torch.cuda.synchronize()
+    assert_bytes_equal(bf16_bits_of(h[rows]), want, "h rows")
