@@ -501,19 +501,29 @@ __device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t *sh)
     return r;
 }
 
+// kFlat: the rows are contiguous (ld == K), so chunk c starts at element 8 c
+// (no division); four 16-byte loads per thread are in flight per iteration
+template <bool kFlat>
 __global__ __launch_bounds__(kThreads) void nv_amax_partial_kernel(const uint16_t *__restrict__ x, uint32_t K,
                                                                    uint32_t ld, uint32_t nchunks,
                                                                    uint32_t *__restrict__ partial)
 {
     __shared__ uint32_t sh[kThreads / 64];
     const uint32_t cpr = K >> 3;
-    uint32_t m = 0;
-    for (uint32_t c = blockIdx.x * kThreads + threadIdx.x; c < nchunks; c += gridDim.x * kThreads) {
+    const uint32_t stride = gridDim.x * kThreads;
+    auto src = [&](uint32_t c) -> const uint16_t * {
+        if (kFlat) return x + (size_t)c * 8;
         const uint32_t r = c / cpr;
-        const uint4 q = load_nt16(x + (size_t)r * ld + (size_t)(c - r * cpr) * 8);
-        m = max(m, max(max(q.x & 0x7FFFu, (q.x >> 16) & 0x7FFFu), max(q.y & 0x7FFFu, (q.y >> 16) & 0x7FFFu)));
-        m = max(m, max(max(q.z & 0x7FFFu, (q.z >> 16) & 0x7FFFu), max(q.w & 0x7FFFu, (q.w >> 16) & 0x7FFFu)));
+        return x + (size_t)r * ld + (size_t)(c - r * cpr) * 8;
+    };
+    uint32_t m = 0;
+    uint32_t c = blockIdx.x * kThreads + threadIdx.x;
+    for (; (uint64_t)c + 3ull * stride < nchunks; c += 4 * stride) {
+        const uint4 q0 = load_nt16(src(c)), q1 = load_nt16(src(c + stride));
+        const uint4 q2 = load_nt16(src(c + 2 * stride)), q3 = load_nt16(src(c + 3 * stride));
+        m = max(m, max(max(amax8_bf16(q0), amax8_bf16(q1)), max(amax8_bf16(q2), amax8_bf16(q3))));
     }
+    for (; c < nchunks; c += stride) m = max(m, amax8_bf16(load_nt16(src(c))));
     m = block_max_u32(m, sh);
     if (threadIdx.x == 0) partial[blockIdx.x] = m << 16;  // binary32 bits of the partial amax
 }
@@ -920,8 +930,12 @@ int launch_quant_nv(const QuantArgs &a, int domain, float *tensor_scale, void *w
             if (np > (uint32_t)kAmaxBlocks) np = kAmaxBlocks;
             if (np == 0) np = 1;
             // pass 1 (also runs for an empty operand so that S = 1 is written)
-            hipLaunchKernelGGL(nv_amax_partial_kernel, dim3(np), dim3(kThreads), 0, st, x, K, (uint32_t)a.ld,
-                               (uint32_t)nchunks, part);
+            if (a.ld == (int64_t)K)
+                hipLaunchKernelGGL(nv_amax_partial_kernel<true>, dim3(np), dim3(kThreads), 0, st, x, K,
+                                   (uint32_t)a.ld, (uint32_t)nchunks, part);
+            else
+                hipLaunchKernelGGL(nv_amax_partial_kernel<false>, dim3(np), dim3(kThreads), 0, st, x, K,
+                                   (uint32_t)a.ld, (uint32_t)nchunks, part);
             partial = part;
         }
         const uint32_t grid = (uint32_t)((nchunks + kThreads * kChunksPerThread - 1) / (kThreads * kChunksPerThread));
