@@ -272,3 +272,22 @@ def test_swiglu_status_codes():
     assert s(h=C + 2) == B.EALIGN
     assert s(h=X + 64) == B.EINVAL                # h overlaps c
     assert s(M=0) == B.OK
+
+
+def test_size_limits():
+    # fake device addresses 16 TiB apart, so that only the size rule decides
+    x, codes, scales, c = 0x100000000000, 0x200000000000, 0x300000000000, 0x400000000000
+    # MX producer: the 8-element chunk count must stay below 2^32
+    assert q_mx(x=x, rows=2 ** 22, cols=2 ** 13, ld=2 ** 13, codes=codes, scales=scales) == B.ESHAPE
+    assert q_mx(x=x, rows=2 ** 22 - 32, cols=2 ** 13, ld=2 ** 13, codes=codes, scales=scales) in (B.OK, B.ELAUNCH)
+    # tiled: the padded row count counts (2^22 - 31 rows pad to 2^22)
+    assert q_mx(x=x, rows=2 ** 22 - 31, cols=2 ** 13, ld=2 ** 13, codes=codes, scales=scales, layout=1) == B.ESHAPE
+    # MX GEMM: each operand's code bytes must stay below 2^32
+    def g(M, N=256, K=8192, a=codes, sa=scales, b=x, sb=x + (1 << 40)):
+        return L.fp4_gemm_mx(a, sa, b, sb, M, N, K, 1.0, 0, c, 0, N, None)
+
+    assert g(M=2 ** 20) == B.ESHAPE                  # 2^20 rows x 4096 bytes = 2^32
+    assert g(M=2 ** 20 - 1) in (B.OK, B.ELAUNCH)
+    assert g(M=256, N=2 ** 20) == B.ESHAPE
+    # dimensions above INT32_MAX are rejected outright
+    assert g(M=2 ** 31) == B.ESHAPE
