@@ -600,13 +600,21 @@ __global__ __launch_bounds__(kThreads) void nv_quant_global_kernel(const uint16_
 }
 
 // ------------------------------------------------------------------
-// NVFP4, per-128x128-tile domain ("CTA-local"): one workgroup owns one tile,
-// takes its amax, writes its S, then quantizes it from registers.  No
-// grid-wide dependency.  Lane t handles chunks t + 256 i (i < 8) of the
-// tile's 128 rows x 16 chunks.
+// NVFP4, per-128x128-tile domain ("CTA-local"): a 512-thread workgroup owns
+// two horizontally adjacent tiles (128 rows x 256 K), takes each tile's
+// amax, writes its S, then quantizes from registers.  No grid-wide
+// dependency.  Thread t handles chunk t mod 32 (tile (t mod 32) / 16) of
+// rows t / 32 + 16 i (i < 8), so a row's 32 codes words are one full
+// 128-byte line and the two tiles' maxima reduce over lane bits 0-3 and 5
+// (then over the 8 waves through LDS).  Four scale bytes
+// (lanes +0, +2, +4, +6 of the row's 32) are gathered with DPP row shifts
+// and written as one 32-bit word when K % 64 == 0 and the scales are
+// 4-byte aligned (word-aligned rows); else one byte per even lane.
 // ------------------------------------------------------------------
+constexpr int kTileThreads = 512, kTileRowsPerIter = kTileThreads / 32, kTileIters = 128 / kTileRowsPerIter;
+
 template <bool kSR>
-__global__ __launch_bounds__(kThreads) void nv_quant_tile_kernel(const uint16_t *__restrict__ x, uint32_t R,
+__global__ __launch_bounds__(kTileThreads) void nv_quant_tile_kernel(const uint16_t *__restrict__ x, uint32_t R,
                                                                  uint32_t K, uint32_t ld,
                                                                  uint32_t *__restrict__ codes,
                                                                  uint8_t *__restrict__ scales,
@@ -614,39 +622,59 @@ __global__ __launch_bounds__(kThreads) void nv_quant_tile_kernel(const uint16_t 
                                                                  uint32_t seed_lo, uint32_t seed_hi,
                                                                  uint32_t stream_id)
 {
-    __shared__ uint32_t sh[kThreads / 64];
+    __shared__ uint32_t sh[2 * (kTileThreads / 64)];
     const uint32_t TK = (K + 127) >> 7;
-    const uint32_t tr = blockIdx.y, tk = blockIdx.x;
+    const uint32_t tr = blockIdx.y, tp = blockIdx.x;  // tile row, tile pair
     const uint32_t cpr = K >> 3;
-    uint4 q[8];
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const uint32_t cc = t & 31, half = cc >> 4;        // chunk within the pair, its tile
+    const uint32_t c8 = tp * 32 + cc;
+    const bool cvalid = c8 < cpr;
+    uint4 q[kTileIters];
     uint32_t m = 0;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const uint32_t t = threadIdx.x + kThreads * i;
-        const uint32_t r = tr * 128 + (t >> 4);
-        const uint32_t c8 = tk * 16 + (t & 15);
+    for (int i = 0; i < kTileIters; ++i) {
+        const uint32_t r = tr * 128 + (t >> 5) + kTileRowsPerIter * i;
         q[i] = make_uint4(0u, 0u, 0u, 0u);
-        if (r < R && c8 < cpr)
-            q[i] = load_nt16(x + (size_t)r * ld + (size_t)c8 * 8);
-        m = max(m, max(max(q[i].x & 0x7FFFu, (q[i].x >> 16) & 0x7FFFu), max(q[i].y & 0x7FFFu, (q[i].y >> 16) & 0x7FFFu)));
-        m = max(m, max(max(q[i].z & 0x7FFFu, (q[i].z >> 16) & 0x7FFFu), max(q[i].w & 0x7FFFu, (q[i].w >> 16) & 0x7FFFu)));
+        if (r < R && cvalid) q[i] = load_nt16(x + (size_t)r * ld + (size_t)c8 * 8);
+        m = max(m, amax8_bf16(q[i]));
     }
-    m = block_max_u32(m, sh);
-    const float S = nv_tensor_scale(u2f(m << 16));
-    if (threadIdx.x == 0) tensor_scale[tr * TK + tk] = S;
+    // per tile: lanes with the same bit 4 (and any bits 0-3, 5) share it
+    m = max(m, (uint32_t)__shfl_xor((int)m, 1, 64));
+    m = max(m, (uint32_t)__shfl_xor((int)m, 2, 64));
+    m = max(m, (uint32_t)__shfl_xor((int)m, 4, 64));
+    m = max(m, (uint32_t)__shfl_xor((int)m, 8, 64));
+    m = max(m, (uint32_t)__shfl_xor((int)m, 32, 64));
+    if (lane == 0) sh[2 * wave] = m;
+    if (lane == 16) sh[2 * wave + 1] = m;
+    __syncthreads();
+    uint32_t tm = sh[half];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const uint32_t t = threadIdx.x + kThreads * i;
-        const uint32_t r = tr * 128 + (t >> 4);
-        const uint32_t c8 = tk * 16 + (t & 15);
+    for (int w = 1; w < kTileThreads / 64; ++w) tm = max(tm, sh[2 * w + half]);
+    const float S = nv_tensor_scale(u2f(tm << 16));
+    const uint32_t tk = tp * 2 + half;
+    if ((t == 0 || t == 16) && tk < TK) tensor_scale[tr * TK + tk] = S;
+    const bool word_scales = (K & 63u) == 0 && ((uintptr_t)scales & 3u) == 0;
+#pragma unroll
+    for (int i = 0; i < kTileIters; ++i) {
+        const uint32_t r = tr * 128 + (t >> 5) + kTileRowsPerIter * i;
         float f[8];
         unpack8(q[i], f);
         uint32_t sb;
         const uint32_t packed = nv_encode8<kSR>(f, S, &sb, r, c8, stream_id, seed_lo, seed_hi);
-        if (r < R && c8 < cpr) {
+        // scale bytes of chunks cc, cc + 2, cc + 4, cc + 6 (one per 16-element block)
+        const uint32_t s2 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)sb, 0x102, 0xF, 0xF, true);
+        const uint32_t s4 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)sb, 0x104, 0xF, 0xF, true);
+        const uint32_t s6 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)sb, 0x106, 0xF, 0xF, true);
+        if (r < R && cvalid) {
             const size_t c = (size_t)r * cpr + c8;
             __builtin_nontemporal_store(packed, codes + c);
-            if ((threadIdx.x & 1) == 0) scales[c >> 1] = (uint8_t)sb;
+            if (word_scales) {
+                if ((cc & 7) == 0)  // chunks c8 .. c8 + 7 lie inside the row (cpr % 8 == 0)
+                    *reinterpret_cast<uint32_t *>(scales + (c >> 1)) = sb | s2 << 8 | s4 << 16 | s6 << 24;
+            } else if ((cc & 1) == 0) {
+                scales[c >> 1] = (uint8_t)sb;
+            }
         }
     }
 }
@@ -950,12 +978,12 @@ int launch_quant_nv(const QuantArgs &a, int domain, float *tensor_scale, void *w
                                seed_hi, a.stream_id);
     } else {
         if (R == 0 || K == 0) return 0;
-        dim3 grid((K + 127) / 128, (R + 127) / 128);
+        dim3 grid(((K + 127) / 128 + 1) / 2, (R + 127) / 128);  // pairs of tiles
         if (a.sr)
-            hipLaunchKernelGGL(nv_quant_tile_kernel<true>, grid, dim3(kThreads), 0, st, x, R, K, (uint32_t)a.ld,
+            hipLaunchKernelGGL(nv_quant_tile_kernel<true>, grid, dim3(kTileThreads), 0, st, x, R, K, (uint32_t)a.ld,
                                codes, scales, tensor_scale, seed_lo, seed_hi, a.stream_id);
         else
-            hipLaunchKernelGGL(nv_quant_tile_kernel<false>, grid, dim3(kThreads), 0, st, x, R, K, (uint32_t)a.ld,
+            hipLaunchKernelGGL(nv_quant_tile_kernel<false>, grid, dim3(kTileThreads), 0, st, x, R, K, (uint32_t)a.ld,
                                codes, scales, tensor_scale, seed_lo, seed_hi, a.stream_id);
     }
     return hipGetLastError() == hipSuccess ? 0 : 1;

@@ -84,7 +84,10 @@ def test_hadamard_rows_small(rows, cols, sr):
         assert_bytes_equal(np_u8(codes), oc, f"codes mask={mask:#x}")
 
 
-NV_SHAPES = [(1, 16, None), (3, 48, None), (130, 144, None), (300, 400, 416), (256, 256, None)]
+# cols: one tile; two, the second partial; three (an odd tile count); K % 64
+# == 0 with a partial last tile (word-sized scale stores)
+NV_SHAPES = [(1, 16, None), (3, 48, None), (130, 144, None), (300, 400, 416), (256, 256, None), (70, 384, None),
+             (129, 192, None)]
 
 
 @pytest.mark.parametrize("rows,cols,ld", NV_SHAPES)
@@ -101,6 +104,23 @@ def test_nv_small(rows, cols, ld, domain, sr):
     assert_bytes_equal(ts.cpu().numpy().view(np.uint32), ots.view(np.uint32), "tensor scales")
     assert_bytes_equal(np_u8(scales), os_, "block scales")
     assert_bytes_equal(np_u8(codes), oc, "codes")
+
+
+@pytest.mark.parametrize("domain", [0, 1])
+def test_nv_scales_not_word_aligned(domain):
+    # scale bytes at an odd address: written byte by byte, same bytes
+    dev = device()
+    announce(f"nv scales at an odd address, domain={domain}")
+    rows, cols = 200, 512
+    xb = synth.bf16_bits(synth.activation(rows, cols, 13))
+    big = torch.full((rows * cols // 16 + 2,), 0xA5, dtype=torch.uint8, device=dev)
+    sc = big[1:1 + rows * cols // 16].view(rows, cols // 16)
+    codes, scales, ts = B.fp4_quantize_nv(synth.from_bf16_bits(xb).to(dev), domain, scales=sc)
+    torch.cuda.synchronize()
+    oc, os_, ots = oracle.quantize_nv(xb, domain=domain)
+    assert_bytes_equal(np_u8(sc), os_, "block scales")
+    assert_bytes_equal(np_u8(codes), oc, "codes")
+    assert int(big[0].item()) == 0xA5 and int(big[-1].item()) == 0xA5
 
 
 def test_nv_zero_tile_and_empty():
