@@ -555,7 +555,12 @@ __device__ __forceinline__ uint32_t nv_encode8(const float f[8], float S, uint32
     return packed;
 }
 
-template <bool kSR>
+// kFlat: contiguous rows (ld == K), chunk c starts at element 8 c.  The
+// data loads go out first and the domain amax is reduced from the partial
+// maxima while they are in flight; four scale bytes (lanes +0, +2, +4, +6:
+// consecutive chunks) are gathered by DPP row shifts into one 32-bit store
+// when the chunk count is a multiple of 8 and the scales are word-aligned.
+template <bool kSR, bool kFlat>
 __global__ __launch_bounds__(kThreads) void nv_quant_global_kernel(const uint16_t *__restrict__ x, uint32_t K,
                                                                    uint32_t ld, uint32_t nchunks,
                                                                    const uint32_t *__restrict__ partial,
@@ -566,12 +571,6 @@ __global__ __launch_bounds__(kThreads) void nv_quant_global_kernel(const uint16_
                                                                    uint32_t stream_id)
 {
     __shared__ uint32_t sh[kThreads / 64];
-    uint32_t a = 0;
-    for (uint32_t i = threadIdx.x; i < npartial; i += kThreads) a = max(a, partial[i]);
-    a = block_max_u32(a, sh);
-    const float S = nv_tensor_scale(u2f(a));
-    if (blockIdx.x == 0 && threadIdx.x == 0) *tensor_scale = S;
-
     const uint32_t cpr = K >> 3;
     const uint32_t base = blockIdx.x * (kThreads * kChunksPerThread) + threadIdx.x;
     uint4 q[kChunksPerThread];
@@ -580,21 +579,43 @@ __global__ __launch_bounds__(kThreads) void nv_quant_global_kernel(const uint16_
         const uint32_t c = base + i * kThreads;
         q[i] = make_uint4(0u, 0u, 0u, 0u);
         if (c < nchunks) {
-            const uint32_t r = c / cpr;
-            q[i] = load_nt16(x + (size_t)r * ld + (size_t)(c - r * cpr) * 8);
+            if (kFlat) {
+                q[i] = load_nt16(x + (size_t)c * 8);
+            } else {
+                const uint32_t r = c / cpr;
+                q[i] = load_nt16(x + (size_t)r * ld + (size_t)(c - r * cpr) * 8);
+            }
         }
     }
+    uint32_t a = 0;
+    for (uint32_t i = threadIdx.x; i < npartial; i += kThreads) a = max(a, partial[i]);
+    a = block_max_u32(a, sh);
+    const float S = nv_tensor_scale(u2f(a));
+    if (blockIdx.x == 0 && threadIdx.x == 0) *tensor_scale = S;
+    const bool word_scales = (nchunks & 7u) == 0 && ((uintptr_t)scales & 3u) == 0;
 #pragma unroll
     for (int i = 0; i < kChunksPerThread; ++i) {
         const uint32_t c = base + i * kThreads;
-        const uint32_t r = c / cpr;
+        uint32_t r = 0, col = 0;  // only stochastic rounding keys on them
+        if (kSR) {
+            r = c / cpr;
+            col = c - r * cpr;
+        }
         float f[8];
         unpack8(q[i], f);
         uint32_t sb;
-        const uint32_t packed = nv_encode8<kSR>(f, S, &sb, r, c - r * cpr, stream_id, seed_lo, seed_hi);
+        const uint32_t packed = nv_encode8<kSR>(f, S, &sb, r, col, stream_id, seed_lo, seed_hi);
+        const uint32_t s2 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)sb, 0x102, 0xF, 0xF, true);
+        const uint32_t s4 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)sb, 0x104, 0xF, 0xF, true);
+        const uint32_t s6 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)sb, 0x106, 0xF, 0xF, true);
         if (c < nchunks) {
             __builtin_nontemporal_store(packed, codes + c);
-            if ((threadIdx.x & 1) == 0) scales[c >> 1] = (uint8_t)sb;
+            if (word_scales) {
+                if ((threadIdx.x & 7) == 0)  // c % 8 == 0 and c + 7 < nchunks
+                    *reinterpret_cast<uint32_t *>(scales + (c >> 1)) = sb | s2 << 8 | s4 << 16 | s6 << 24;
+            } else if ((threadIdx.x & 1) == 0) {
+                scales[c >> 1] = (uint8_t)sb;
+            }
         }
     }
 }
@@ -968,14 +989,16 @@ int launch_quant_nv(const QuantArgs &a, int domain, float *tensor_scale, void *w
         }
         const uint32_t grid = (uint32_t)((nchunks + kThreads * kChunksPerThread - 1) / (kThreads * kChunksPerThread));
         const uint32_t g = grid == 0 ? 1 : grid;
-        if (a.sr)
-            hipLaunchKernelGGL(nv_quant_global_kernel<true>, dim3(g), dim3(kThreads), 0, st, x, K, (uint32_t)a.ld,
-                               (uint32_t)nchunks, partial, np, codes, scales, tensor_scale, seed_lo, seed_hi,
-                               a.stream_id);
-        else
-            hipLaunchKernelGGL(nv_quant_global_kernel<false>, dim3(g), dim3(kThreads), 0, st, x, K,
-                               (uint32_t)a.ld, (uint32_t)nchunks, partial, np, codes, scales, tensor_scale, seed_lo,
-                               seed_hi, a.stream_id);
+#define FP4Q_NVG(SR, FLAT)                                                                                    \
+    hipLaunchKernelGGL((nv_quant_global_kernel<SR, FLAT>), dim3(g), dim3(kThreads), 0, st, x, K, (uint32_t)a.ld,      \
+                       (uint32_t)nchunks, partial, np, codes, scales, tensor_scale, seed_lo, seed_hi, a.stream_id)
+        const bool flat = a.ld == (int64_t)K;
+        if (a.sr) {
+            if (flat) FP4Q_NVG(true, true); else FP4Q_NVG(true, false);
+        } else {
+            if (flat) FP4Q_NVG(false, true); else FP4Q_NVG(false, false);
+        }
+#undef FP4Q_NVG
     } else {
         if (R == 0 || K == 0) return 0;
         dim3 grid(((K + 127) / 128 + 1) / 2, (R + 127) / 128);  // pairs of tiles
