@@ -86,6 +86,10 @@ FP4Q_HD float silu_f32(float x)
 //    adding 2^22 - 1 - 64 r16 carries into the code iff 2^22 f > 64 r16;
 //  - |y| < 1: P = 2^17 |y| (exact) is t in units of 2^-16 steps, and the code
 //    is the number of the thresholds r16 and r16 + 2^16 that P exceeds.
+// Saturation is min(code, 7): the fixed-point code of the first case is at
+// least 7 for every |y| >= 6 (Inf and NaN included, no 32-bit wrap) and at
+// most 7 below, so one min replaces a select that the compiler would
+// otherwise turn into a divergent branch per element.
 FP4Q_HD uint32_t e2m1_sr(float y, uint32_t r16)
 {
     const uint32_t b = f2u(y);
@@ -95,7 +99,8 @@ FP4Q_HD uint32_t e2m1_sr(float y, uint32_t r16)
     const float P = u2f(u) * 131072.0f;
     const float rf = (float)r16;
     const uint32_t lo = (P > rf ? 1u : 0u) + (P > rf + 65536.0f ? 1u : 0u);
-    return s | (u >= 0x40C00000u ? 7u : (u >= 0x3F800000u ? hi : lo));
+    const uint32_t hs = hi < 7u ? hi : 7u;
+    return s | (u >= 0x3F800000u ? hs : lo);
 }
 
 // OCP MX shared exponent byte (E8M0) of a block whose amax has binary32 bits

@@ -427,12 +427,21 @@ __global__ __launch_bounds__(kThreads) void quant_mx_rows_tiled_kernel(
     const uint32_t c8 = lane % (kWin / 8);  // 8-element chunk within the window
     const uint32_t sub = lane / (kWin / 8); // which row of the load instruction
     const bool kvalid = (c8 >> 4) < nsteps;
+    // Unconditional loads from a clamped address (row R - 1, or a chunk of the
+    // first K step, which the launch guarantees in bounds: R >= 1, K % 128 ==
+    // 0, k0 < K), zeroed afterwards: a load under a branch lets the compiler
+    // wait for it inside the branch, which serializes the four loads.
     uint4 q[kLoads];
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
         const uint32_t row = g * 32 + (i * 4 + wave) * kRowsPerLoad + sub;
-        q[i] = make_uint4(0u, 0u, 0u, 0u);
-        if (row < R && kvalid) q[i] = load_nt16(x + (size_t)row * ld + k0 + 8 * c8);
+        const uint32_t rc = min(row, R - 1), cc = kvalid ? c8 : (c8 & 15u);
+        q[i] = load_nt16(x + (size_t)rc * ld + k0 + 8 * cc);
+    }
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+        const uint32_t row = g * 32 + (i * 4 + wave) * kRowsPerLoad + sub;
+        if (!(row < R && kvalid)) q[i] = make_uint4(0u, 0u, 0u, 0u);
     }
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {

@@ -81,6 +81,18 @@ def test_e2m1_sr_matches_oracle(H):
     lib = oracle._load()
     want = np.fromiter((lib.oc_e2m1_sr(float(a), int(b)) for a, b in zip(y, r)), dtype=np.uint8, count=y.size)
     assert np.array_equal(got, want)
+    # the saturation boundary: just below 6, 6, and the largest finite
+    # binary32, both signs, with the extreme random draws
+    edge = np.array([0x40BFFFFF, 0x40C00000, 0x40C00001, 0x7F7FFFFF, 0x3F7FFFFF, 0x3F800000], np.uint32).view(np.float32)
+    ye = np.repeat(np.concatenate([edge, -edge]), 2)
+    re = np.tile(np.uint32([0, 65535]), edge.size * 2)
+    ge = np.zeros(ye.size, dtype=np.uint8)
+    H.h_e2m1_sr_batch(ye.ctypes.data, re.ctypes.data, ge.ctypes.data, ye.size)
+    we = np.fromiter((lib.oc_e2m1_sr(float(a), int(b)) for a, b in zip(ye, re)), dtype=np.uint8, count=ye.size)
+    assert np.array_equal(ge, we)
+    # 6 - ulp is 2^-23 steps below 6: f 2^16 exceeds every draw, so it rounds
+    # up to 6 (code 7) always; likewise 1 - ulp always rounds up to 1 (code 2)
+    assert list(we[:6]) == [7, 7, 7, 7, 7, 7] and list(we[8:12]) == [2, 2, 2, 2]
 
 
 def test_mx_scale_byte_matches_oracle(H):
