@@ -80,27 +80,26 @@ FP4Q_HD float silu_f32(float x)
 // is g = 0.5 below 2, 1 in [2, 4), 2 in [4, 6); with t = |y| / g, f its
 // fractional part (the distance to the lower neighbour in steps), the value
 // rounds up iff f * 2^16 > r16.  |y| >= 6 saturates.  r16 is uniform on
-// [0, 65535].  Evaluated branch-free and exactly:
-//  - |y| in [1, 6): the binary32 bits of |y| minus those of 0.5 give t on the
-//    code axis in fixed point (code = bits 22 and up, f = the low 22 bits);
-//    adding 2^22 - 1 - 64 r16 carries into the code iff 2^22 f > 64 r16;
-//  - |y| < 1: P = 2^17 |y| (exact) is t in units of 2^-16 steps, and the code
-//    is the number of the thresholds r16 and r16 + 2^16 that P exceeds.
-// Saturation is min(code, 7): the fixed-point code of the first case is at
-// least 7 for every |y| >= 6 (Inf and NaN included, no 32-bit wrap) and at
-// most 7 below, so one min replaces a select that the compiler would
-// otherwise turn into a divergent branch per element.
+// [0, 65535].  Evaluated branch-free and exactly, on the code axis in fixed
+// point (X = code * 2^22 + 2^22 f, codes 0..7 for 0, 0.5, 1, 1.5, 2, 3, 4, 6):
+//  - |y| >= 1: X = bits(|y|) - bits(0.5) (one binade holds two codes);
+//  - |y| < 1: the grid is linear, X = 2^23 |y| (exact); for integer m,
+//    f 2^22 > m iff ceil(f 2^22) > m, so X = ceil(2^23 |y|) serves;
+// then adding 2^22 - 1 - 64 r16 carries into the code iff 2^22 f > 64 r16
+// (64 r16 < 2^22 - 1, so a ceiling that reaches the next code still rounds
+// up).  Saturation is min(code, 7): the code is at least 7 for every
+// |y| >= 6 (Inf and NaN included, no 32-bit wrap) and at most 7 below.  The
+// selects stay selects: no divergent branch per element.
 FP4Q_HD uint32_t e2m1_sr(float y, uint32_t r16)
 {
     const uint32_t b = f2u(y);
     const uint32_t u = b & 0x7FFFFFFFu;
     const uint32_t s = (b >> 28) & 8u;
-    const uint32_t hi = (u - 0x3F000000u + 0x3FFFFFu - (r16 << 6)) >> 22;
-    const float P = u2f(u) * 131072.0f;
-    const float rf = (float)r16;
-    const uint32_t lo = (P > rf ? 1u : 0u) + (P > rf + 65536.0f ? 1u : 0u);
-    const uint32_t hs = hi < 7u ? hi : 7u;
-    return s | (u >= 0x3F800000u ? hs : lo);
+    const uint32_t ul = u < 0x3F800000u ? u : 0x3F800000u;  // |y| clamped to 1: in range of the conversion
+    const uint32_t xl = (uint32_t)__builtin_ceilf(u2f(ul) * 8388608.0f);
+    const uint32_t X = u >= 0x3F800000u ? u - 0x3F000000u : xl;
+    const uint32_t c = (X + 0x3FFFFFu - (r16 << 6)) >> 22;
+    return s | (c < 7u ? c : 7u);
 }
 
 // OCP MX shared exponent byte (E8M0) of a block whose amax has binary32 bits

@@ -93,6 +93,22 @@ def test_e2m1_sr_matches_oracle(H):
     # 6 - ulp is 2^-23 steps below 6: f 2^16 exceeds every draw, so it rounds
     # up to 6 (code 7) always; likewise 1 - ulp always rounds up to 1 (code 2)
     assert list(we[:6]) == [7, 7, 7, 7, 7, 7] and list(we[8:12]) == [2, 2, 2, 2]
+    # full-mantissa binary32 below 1 (the Hadamard path's outputs), where 2^23 |y|
+    # is not an integer, and values one binary32 step either side of each
+    # threshold (k + r16 / 2^16) / 2 of the draw they meet
+    rng2 = np.random.default_rng(7)
+    yf = np.concatenate([rng2.uniform(0, 1, 100000), 10.0 ** rng2.uniform(-30, 0, 50000)]).astype(np.float32)
+    rf = rng2.integers(0, 65536, yf.size).astype(np.uint32)
+    rt = rng2.integers(0, 65536, 30000).astype(np.uint32)
+    kt = rng2.integers(0, 2, rt.size)
+    yt = ((kt + rt / 65536.0) / 2.0).astype(np.float32)
+    yt = np.concatenate([np.nextafter(yt, np.float32(0)), yt, np.nextafter(yt, np.float32(1))])
+    yf = np.concatenate([yf, yt * np.where(rng2.integers(0, 2, yt.size) == 1, 1, -1).astype(np.float32)])
+    rf = np.concatenate([rf, np.tile(rt, 3)])
+    gf = np.zeros(yf.size, dtype=np.uint8)
+    H.h_e2m1_sr_batch(yf.ctypes.data, rf.ctypes.data, gf.ctypes.data, yf.size)
+    wf = np.fromiter((lib.oc_e2m1_sr(float(a), int(b)) for a, b in zip(yf, rf)), dtype=np.uint8, count=yf.size)
+    assert np.array_equal(gf, wf)
 
 
 def test_mx_scale_byte_matches_oracle(H):
