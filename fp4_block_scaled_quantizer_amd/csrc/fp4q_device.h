@@ -85,6 +85,9 @@ FP4Q_HD float silu_f32(float x)
 //  - |y| >= 1: X = bits(|y|) - bits(0.5) (one binade holds two codes);
 //  - |y| < 1: the grid is linear, X = 2^23 |y| (exact); for integer m,
 //    f 2^22 > m iff ceil(f 2^22) > m, so X = ceil(2^23 |y|) serves;
+//  - both at once: X = max(bits(|y|) - bits(0.5) saturated at 0,
+//    ceil(2^23 min(|y|, 1))); below 1 the second term is the larger (equal
+//    or above within [0.5, 1), the first is 0 below 0.5), from 1 on the first;
 // then adding 2^22 - 1 - 64 r16 carries into the code iff 2^22 f > 64 r16
 // (64 r16 < 2^22 - 1, so a ceiling that reaches the next code still rounds
 // up).  Saturation is min(code, 7): the code is at least 7 for every
@@ -97,7 +100,8 @@ FP4Q_HD uint32_t e2m1_sr(float y, uint32_t r16)
     const uint32_t s = (b >> 28) & 8u;
     const uint32_t ul = u < 0x3F800000u ? u : 0x3F800000u;  // |y| clamped to 1: in range of the conversion
     const uint32_t xl = (uint32_t)__builtin_ceilf(u2f(ul) * 8388608.0f);
-    const uint32_t X = u >= 0x3F800000u ? u - 0x3F000000u : xl;
+    const uint32_t xh = u > 0x3F000000u ? u - 0x3F000000u : 0u;
+    const uint32_t X = xh > xl ? xh : xl;
     const uint32_t c = (X + 0x3FFFFFu - (r16 << 6)) >> 22;
     return s | (c < 7u ? c : 7u);
 }
