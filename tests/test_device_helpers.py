@@ -50,7 +50,8 @@ def e4m3_inputs():
     near = np.concatenate([np.nextafter(pts, np.float32(0)), np.nextafter(pts, np.float32(1e9)), pts])
     rng = np.random.default_rng(0)
     rnd = np.exp(rng.uniform(np.log(1e-6), np.log(600), 200000)).astype(np.float32)
-    tiny = np.array([0, 2.0 ** -10, 2.0 ** -10 * 1.0001, 2.0 ** -149, 1e-30, 448, 463.9, 464, 1e30], np.float32)
+    tiny = np.array([0, 2.0 ** -10, 2.0 ** -10 * 1.0001, 2.0 ** -149, 1e-30, 448, 463.9, 464, 1e30, 3.4e38,
+                     2.0 ** -6, np.nextafter(np.float32(2.0 ** -6), np.float32(0))], np.float32)
     return np.concatenate([near, rnd, tiny]).astype(np.float32)
 
 
