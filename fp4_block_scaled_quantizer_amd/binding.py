@@ -100,9 +100,26 @@ def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
 
-def _amax_ptr(t: torch.Tensor) -> int:
-    if t.dtype != torch.float32 or t.numel() < 1:
-        raise ValueError("c_amax must be a float32 tensor with at least one element")
+def _check_out(t: torch.Tensor, name: str, dtype, shape, device) -> torch.Tensor:
+    """A caller-supplied output: the library cannot see buffer sizes, so a
+    wrong one would be written past its end.  It must be a contiguous tensor
+    of `dtype` on the input's device with exactly `shape`."""
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a tensor")
+    if t.device != torch.device(device):
+        raise ValueError(f"{name} is on {t.device}, the input on {device}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, not {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, not {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _amax_ptr(t: torch.Tensor, device) -> int:
+    if t.dtype != torch.float32 or t.numel() < 1 or t.device != torch.device(device):
+        raise ValueError("c_amax must be a float32 tensor with at least one element on the operands' device")
     return t.data_ptr()
 
 
@@ -138,7 +155,8 @@ def _mx_outputs(R, K, layout, codes, scales, device):
         codes = torch.empty(cshape, dtype=torch.uint8, device=device)
     if scales is None:
         scales = torch.empty(sshape, dtype=torch.uint8, device=device)
-    return codes, scales
+    return (_check_out(codes, "codes", torch.uint8, cshape, device),
+            _check_out(scales, "scales", torch.uint8, sshape, device))
 
 
 def fp4_quantize_mx(x: torch.Tensor, *, cols: Optional[int] = None, axis: int = ALONG_ROWS, round: int = RNE,
@@ -210,9 +228,12 @@ def fp4_quantize_nv(x: torch.Tensor, domain: int = NV_GLOBAL, *, cols: Optional[
         scales = torch.empty((R, K // 16), dtype=torch.uint8, device=x.device)
     if tensor_scale is None:
         tensor_scale = torch.empty(nv_tensor_scale_shape(R, K, domain), dtype=torch.float32, device=x.device)
+    _check_out(codes, "codes", torch.uint8, (R, K // 2), x.device)
+    _check_out(scales, "scales", torch.uint8, (R, K // 16), x.device)
+    _check_out(tensor_scale, "tensor_scale", torch.float32, nv_tensor_scale_shape(R, K, domain), x.device)
     if amax is not None:
-        if domain != NV_GLOBAL or axis != ALONG_ROWS or amax.dtype != torch.float32:
-            raise ValueError("a given amax is a float32 tensor for the global domain along rows")
+        if domain != NV_GLOBAL or axis != ALONG_ROWS or amax.dtype != torch.float32 or amax.device != x.device:
+            raise ValueError("a given amax is a float32 tensor on x's device, for the global domain along rows")
         _check("fp4_quantize_nv_amax",
                lib().fp4_quantize_nv_amax(x.data_ptr(), rows, cols, ld, round, seed, stream_id, amax.data_ptr(),
                                           codes.data_ptr(), scales.data_ptr(), tensor_scale.data_ptr(),
@@ -221,6 +242,8 @@ def fp4_quantize_nv(x: torch.Tensor, domain: int = NV_GLOBAL, *, cols: Optional[
     need = fp4q_nv_workspace_bytes(rows, cols, axis, domain)
     if workspace is None and need > 0:
         workspace = torch.empty((need,), dtype=torch.uint8, device=x.device)
+    if workspace is not None and (workspace.device != x.device or not workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous tensor on x's device")
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     if hadamard_mask is not None:
         _check("fp4_hadamard32_quantize_nv",
@@ -241,6 +264,10 @@ def _gemm_out(M: int, N: int, out_dtype, device, c: Optional[torch.Tensor]):
         c = torch.empty((M, N), dtype=out_dtype, device=device)
     if c.dtype not in (torch.float32, torch.bfloat16) or c.dim() != 2 or c.stride(1) != 1:
         raise ValueError("c must be a 2-D fp32 or bf16 tensor with unit column stride")
+    if tuple(c.shape) != (M, N) or c.device != torch.device(device):
+        raise ValueError(f"c must be a [{M} x {N}] tensor on {device}, not {tuple(c.shape)} on {c.device}")
+    if M > 1 and c.stride(0) < N:
+        raise ValueError("c's rows overlap (row stride below N)")
     ldc = c.stride(0) if M > 1 else N
     return c, (OUT_F32 if c.dtype == torch.float32 else OUT_BF16), ldc
 
@@ -261,7 +288,7 @@ def fp4_gemm_mx(a_codes: torch.Tensor, a_scales: torch.Tensor, b_codes: torch.Te
     if c_amax is not None:
         _check("fp4_gemm_mx_amax",
                lib().fp4_gemm_mx_amax(a_codes.data_ptr(), a_scales.data_ptr(), b_codes.data_ptr(), b_scales.data_ptr(),
-                                      M, N, K, float(alpha), layout, c.data_ptr(), ctype, ldc, _amax_ptr(c_amax),
+                                      M, N, K, float(alpha), layout, c.data_ptr(), ctype, ldc, _amax_ptr(c_amax, a_codes.device),
                                       _stream(stream)))
         return c
     _check("fp4_gemm_mx", lib().fp4_gemm_mx(a_codes.data_ptr(), a_scales.data_ptr(), b_codes.data_ptr(),
@@ -319,6 +346,9 @@ def fp4_swiglu_bf16(c: torch.Tensor, f: int, *, pair: int = 32, h: Optional[torc
     M = c.shape[0]
     if h is None:
         h = torch.empty((M, f), dtype=torch.bfloat16, device=c.device)
+    if (h.dtype != torch.bfloat16 or h.dim() != 2 or h.stride(1) != 1 or tuple(h.shape) != (M, f)
+            or h.device != c.device or (M > 1 and h.stride(0) < f)):
+        raise ValueError(f"h must be a [{M} x {f}] bf16 tensor on {c.device} with unit column stride")
     _check("fp4_swiglu_bf16", lib().fp4_swiglu_bf16(c.data_ptr(), M, f, c.stride(0), pair, h.data_ptr(),
                                                     h.stride(0), _stream(stream)))
     return h
@@ -349,7 +379,7 @@ def fp4_gemm_nv(a_codes: torch.Tensor, a_scales: torch.Tensor, a_tensor_scale: t
         _check("fp4_gemm_nv_amax",
                lib().fp4_gemm_nv_amax(a_codes.data_ptr(), a_scales.data_ptr(), a_tensor_scale.data_ptr(),
                                       b_codes.data_ptr(), b_scales.data_ptr(), b_tensor_scale.data_ptr(), domain, M, N,
-                                      K, float(alpha), LAYOUT_LINEAR, c.data_ptr(), ctype, ldc, _amax_ptr(c_amax),
+                                      K, float(alpha), LAYOUT_LINEAR, c.data_ptr(), ctype, ldc, _amax_ptr(c_amax, a_codes.device),
                                       _stream(stream)))
         return c
     _check("fp4_gemm_nv", lib().fp4_gemm_nv(a_codes.data_ptr(), a_scales.data_ptr(), a_tensor_scale.data_ptr(),

@@ -33,21 +33,26 @@ FP4Q_HD uint32_t f32_to_bf16_rne(float f)
 }
 
 // SiLU(x) = x / (1 + e^-x) (SwiGLU's gate activation; Shazeer, "GLU Variants
-// Improve Transformer") in binary32 as one fixed sequence of IEEE operations,
-// so that every implementation of the sequence returns the same bits (the
-// activation feeds the MX producer of H, whose codes must be reproducible);
-// fused multiply-adds are explicit (one rounding each), nothing else is
-// contracted (the library is built with contraction off).
-//   e^t, t in [-20, 80]: Cody-Waite reduction k = rint(t log2 e) (half to
-//   even), r = fma(-k, ln2_hi, t) (exact: ln2_hi has 15 significant bits),
-//   r = fma(-k, ln2_lo, r); the degree-7 Taylor polynomial of e^r by Horner
-//   with fma; times 2^k (exact).
-//   SiLU: t = min(max(-x, -20), 80) (NaN -> -20); d = 1 + e^t; y = the bit
-//   pattern 0x7EF311C3 - bits(d) (within 5.1 % of 1/d), three Newton steps
-//   q = fma(-d, y, 1), y = fma(y, q, y); SiLU = x * y.  So SiLU(x) = x
-//   exactly above 20, x / (1 + e^80) below -80, NaN stays NaN.
-FP4Q_HD float exp_seq_f32(float t)
+// Improve Transformer") in binary32, division-free, as a fixed sequence of
+// IEEE operations (fused multiply-adds explicit, nothing else contracted:
+// the library is built with contraction off), so that its error over every
+// input the kernels feed it -- all finite bf16 values -- is measured once
+// on the host and holds on the GPU.
+//   e = e^t with t = -min(|x|, 112) (below e^-112 nothing changes): Cody-
+//   Waite reduction k = rint(t log2 e) (half to even), r = fma(-k, ln2_hi,
+//   t) (exact: ln2_hi has 15 significant bits), r = fma(-k, ln2_lo, r); the
+//   degree-7 Taylor polynomial p of e^r by Horner with fma; e = p 2^k.
+//   d = 1 + e lies in (1, 2]; its reciprocal y takes three Newton steps
+//   q = fma(-d, y, 1), y = fma(y, q, y) from the bit-pattern seed
+//   0x7EF311C3 - bits(d) (within 5.1 % of 1/d).
+//   x >= 0: SiLU = x y.  x < 0: SiLU = x e^x / (1 + e^x) = (x p y) 2^k, the
+//   power of two applied last so that a result in the subnormal range is
+//   rounded once (x is clamped at -112 there: below, the result rounds to
+//   -0).  NaN stays NaN.
+FP4Q_HD float silu_f32(float x)
 {
+    const float a = __builtin_fminf(__builtin_fabsf(x), 112.0f);
+    const float t = -a;
     const float k = __builtin_rintf(t * 0x1.715476p+0f);
     float r = __builtin_fmaf(-k, 0x1.62e4p-1f, t);
     r = __builtin_fmaf(-k, 0x1.7f7d1cp-20f, r);
@@ -59,20 +64,16 @@ FP4Q_HD float exp_seq_f32(float t)
     p = __builtin_fmaf(p, r, 0.5f);
     p = __builtin_fmaf(p, r, 1.0f);
     p = __builtin_fmaf(p, r, 1.0f);
-    return __builtin_ldexpf(p, (int)k);
-}
-
-FP4Q_HD float silu_f32(float x)
-{
-    const float t = __builtin_fminf(__builtin_fmaxf(-x, -20.0f), 80.0f);
-    const float d = 1.0f + exp_seq_f32(t);
+    const int ki = (int)k;
+    const float d = 1.0f + __builtin_ldexpf(p, ki);
     float y = u2f(0x7EF311C3u - f2u(d));
 #pragma unroll
     for (int i = 0; i < 3; ++i) {
         const float q = __builtin_fmaf(-d, y, 1.0f);
         y = __builtin_fmaf(y, q, y);
     }
-    return x * y;
+    const float neg = __builtin_ldexpf((-a * p) * y, ki);
+    return x < 0.0f ? neg : x * y;
 }
 
 // E2M1 stochastic rounding ([Fusion] section "Two Key Numerical Techniques":
@@ -197,6 +198,20 @@ FP4Q_HD void philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3, u
 // 16 random bits of element j (0..7) of the 8-element group whose Philox
 // words are w[4]: word j/2, high half for odd j.
 FP4Q_HD uint32_t r16_of(const uint32_t w[4], int j) { return (j & 1) ? (w[j >> 1] >> 16) : (w[j >> 1] & 0xFFFFu); }
+
+// The grid-stride walk of a partial-maximum pass: the thread starting at
+// chunk `start` visits start, start + stride, ... below n, four per step
+// (visit4(c) covers c, c + stride, c + 2 stride, c + 3 stride) while four
+// fit, then one per step (visit1).  The counter is 64-bit: n may lie within
+// a stride of 2^32, where a 32-bit counter would wrap back below n and never
+// exit; every index handed to a visitor is below n, so it fits in 32 bits.
+template <class F4, class F1>
+FP4Q_HD void grid_stride_chunks(uint32_t start, uint32_t stride, uint32_t n, F4 &&visit4, F1 &&visit1)
+{
+    uint64_t c = start;
+    for (; c + 3ull * stride < n; c += 4ull * stride) visit4((uint32_t)c);
+    for (; c < n; c += stride) visit1((uint32_t)c);
+}
 
 // Device-only helpers shared by the producers and the GEMM epilogue that
 // quantizes its output.

@@ -526,13 +526,14 @@ __global__ __launch_bounds__(kThreads) void nv_amax_partial_kernel(const uint16_
         return x + (size_t)r * ld + (size_t)(c - r * cpr) * 8;
     };
     uint32_t m = 0;
-    uint32_t c = blockIdx.x * kThreads + threadIdx.x;
-    for (; (uint64_t)c + 3ull * stride < nchunks; c += 4 * stride) {
-        const uint4 q0 = load_nt16(src(c)), q1 = load_nt16(src(c + stride));
-        const uint4 q2 = load_nt16(src(c + 2 * stride)), q3 = load_nt16(src(c + 3 * stride));
-        m = max(m, max(max(amax8_bf16(q0), amax8_bf16(q1)), max(amax8_bf16(q2), amax8_bf16(q3))));
-    }
-    for (; c < nchunks; c += stride) m = max(m, amax8_bf16(load_nt16(src(c))));
+    grid_stride_chunks(
+        blockIdx.x * kThreads + threadIdx.x, stride, nchunks,
+        [&](uint32_t c) {
+            const uint4 q0 = load_nt16(src(c)), q1 = load_nt16(src(c + stride));
+            const uint4 q2 = load_nt16(src(c + 2 * stride)), q3 = load_nt16(src(c + 3 * stride));
+            m = max(m, max(max(amax8_bf16(q0), amax8_bf16(q1)), max(amax8_bf16(q2), amax8_bf16(q3))));
+        },
+        [&](uint32_t c) { m = max(m, amax8_bf16(load_nt16(src(c)))); });
     m = block_max_u32(m, sh);
     if (threadIdx.x == 0) partial[blockIdx.x] = m << 16;  // binary32 bits of the partial amax
 }

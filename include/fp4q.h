@@ -252,11 +252,16 @@ FP4Q_API fp4q_status fp4_gemm_mx_quant(const void *a_codes, const void *a_scales
  * `pair` columns (gate column j at 2 pair (j / pair) + j mod pair, its up
  * column `pair` further; pair = 32 is the layout fp4_gemm_mx_swiglu_quant
  * takes, pair = F the plain [gate | up]).  h: bf16 [M x F], pitch ldh:
- * h[m][j] = bf16(SiLU(g) * u), SiLU(x) = x / (1 + e^-x) with e^t evaluated by
- * one fixed binary32 sequence (Cody-Waite reduction with a two-part ln 2,
- * degree-7 Horner polynomial, scaling by 2^k; x itself for x > 20, -0 for
- * x < -88), a correctly rounded division and one binary32 product rounded to
- * nearest even.  Requires F % 8 == 0, pair % 8 == 0, F % pair == 0,
+ * h[m][j] = bf16(SiLU(g) * u), SiLU(x) = x / (1 + e^-x), evaluated in
+ * binary32 by one fixed division-free sequence: e = e^-min(|x|, 112) by
+ * Cody-Waite reduction with a two-part ln 2, a degree-7 Horner polynomial p
+ * and scaling by 2^k; the reciprocal y of 1 + e by three Newton steps from a
+ * bit-pattern seed; SiLU = x y for x >= 0 and (x p y) 2^k for x < 0.  Its
+ * error over every finite bf16 x is below 4 binary32 half-ulps (relative)
+ * for normal results and 2^-149 in the subnormal range; then one binary32
+ * product with u, rounded to bf16 to nearest even.  So h is the real
+ * SiLU(g) u rounded to bf16, except where that value lies within this
+ * error of a bf16 rounding midpoint (then either neighbour).  Requires F % 8 == 0, pair % 8 == 0, F % pair == 0,
  * ldc >= 2F and ldh >= F both multiples of 8 (FP4Q_ESHAPE), c and h 16-byte
  * aligned (FP4Q_EALIGN), h not overlapping c (FP4Q_EINVAL). */
 FP4Q_API fp4q_status fp4_swiglu_bf16(const void *c, int64_t M, int64_t F, int64_t ldc, int64_t pair, void *h,

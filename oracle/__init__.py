@@ -74,9 +74,10 @@ def _load():
     sig("oc_dequant_nv", None, u8p, u8p, f32p, i32, i64, i64, f64p)
     sig("oc_gemm_bruteforce", None, f64p, f64p, i64, i64, i64, ctypes.c_double, f64p, f64p)
     sig("oc_float_to_bf16", ctypes.c_uint16, ctypes.c_float)
-    sig("oc_exp_f32_seq", ctypes.c_float, ctypes.c_float)
-    sig("oc_silu_f32", ctypes.c_float, ctypes.c_float)
-    sig("oc_swiglu_bf16", i32, u16p, i64, i64, i64, i64, u16p)
+    sig("oc_double_to_bf16", ctypes.c_uint16, ctypes.c_double)
+    sig("oc_double_to_bf16_array", None, f64p, i64, u16p)
+    sig("oc_swiglu_f64", ctypes.c_double, ctypes.c_float, ctypes.c_float)
+    sig("oc_swiglu_bf16", i32, u16p, i64, i64, i64, i64, u16p, f64p)
     _lib = lib
     return lib
 
@@ -293,13 +294,14 @@ def gemm_bruteforce(a_dq, b_dq, alpha=1.0):
     return C, W
 
 
-def gemm_ref(a_dq, b_dq, alpha=1.0):
-    """C = alpha * A @ B^T and the tolerance weight W = |alpha| * |A| @ |B|^T,
-    with a float64 library matmul (numpy) as the contraction step."""
+def gemm_ref(a_dq, b_dq, alpha=1.0, weights=True):
+    """C = alpha * A @ B^T and the tolerance weight W = |alpha| * |A| @ |B|^T
+    (None with weights=False), with a float64 library matmul (numpy) as the
+    contraction step."""
     A = np.asarray(a_dq, dtype=np.float64)
     B = np.asarray(b_dq, dtype=np.float64)
     C = alpha * (A @ B.T)
-    W = abs(alpha) * (np.abs(A) @ np.abs(B).T)
+    W = abs(alpha) * (np.abs(A) @ np.abs(B).T) if weights else None
     return C, W
 
 
@@ -308,29 +310,44 @@ def float_to_bf16(f: float) -> int:
     return int(_load().oc_float_to_bf16(float(f)))
 
 
-def exp_f32_seq(t: float) -> float:
-    """e^t for t in [-20, 80] by the fixed binary32 sequence of fp4_oracle.c."""
-    return float(_load().oc_exp_f32_seq(float(t)))
+def double_to_bf16(v: float) -> int:
+    """binary64 -> bf16 bits, rounded once to nearest even (no binary32 step)."""
+    return int(_load().oc_double_to_bf16(float(v)))
 
 
-def silu_f32(x: float) -> float:
-    """SiLU(x) = x / (1 + e^-x) in binary32: clamped argument, the exp
-    sequence, a Newton reciprocal (see fp4_oracle.c)."""
-    return float(_load().oc_silu_f32(float(x)))
+def double_to_bf16_array(v):
+    """bf16 bits (uint16, same shape) of a float64 array, each element
+    rounded once to nearest even."""
+    a = np.ascontiguousarray(v, dtype=np.float64)
+    out = np.zeros(a.shape, dtype=np.uint16)
+    if a.size:
+        _load().oc_double_to_bf16_array(_ptr(a, ctypes.c_double), a.size, _ptr(out, ctypes.c_uint16))
+    return out
 
 
-def swiglu_bf16(c, F, pair=32):
-    """H = bf16(SiLU(gate) * up) from a bf16 GEMM output C [M x >= 2F] whose
-    columns interleave gate and up in groups of `pair` (pair = 32: the
-    layout of the fused GEMM's weight; pair = F: [gate | up]).  c: a 2-D
-    uint16 array of bf16 bit patterns.  Returns uint16 bits [M x F]."""
+def swiglu_f64(g: float, u: float) -> float:
+    """SiLU(g) * u = g u / (1 + e^-g) in binary64 (for g, u binary32 values):
+    the value the oracle's bf16 H is rounded from."""
+    return float(_load().oc_swiglu_f64(float(g), float(u)))
+
+
+def swiglu_bf16(c, F, pair=32, with_f64=False):
+    """H = bf16(SiLU(gate) * up), the real value rounded once, from a bf16
+    GEMM output C [M x >= 2F] whose columns interleave gate and up in groups
+    of `pair` (pair = 32: the layout of the fused GEMM's weight; pair = F:
+    [gate | up]).  c: a 2-D uint16 array of bf16 bit patterns.  Returns
+    uint16 bits [M x F]; with ``with_f64`` also the float64 values H was
+    rounded from (to bound a kernel's deviation).  H is the binary64 value of
+    SiLU(g) u rounded once to nearest even."""
     cb = _as_bf16_bits(c)
     M, ldc = cb.shape
     if ldc < 2 * F:
         raise ValueError("C needs at least 2F columns")
     h = np.zeros((M, F), dtype=np.uint16)
+    hv = np.zeros((M, F), dtype=np.float64) if with_f64 else None
     if M and F:
-        rc = _load().oc_swiglu_bf16(_ptr(cb, ctypes.c_uint16), M, F, ldc, pair, _ptr(h, ctypes.c_uint16))
+        rc = _load().oc_swiglu_bf16(_ptr(cb, ctypes.c_uint16), M, F, ldc, pair, _ptr(h, ctypes.c_uint16),
+                                    _ptr(hv, ctypes.c_double) if with_f64 else None)
         if rc != 0:
             raise ValueError("pair must divide F")
-    return h
+    return (h, hv) if with_f64 else h

@@ -493,11 +493,9 @@ void oc_gemm_bruteforce(const double *A, const double *B, int64_t M, int64_t N, 
 /* SwiGLU: the MLP activation whose output H the fused producer        */
 /* quantizes ([Fusion], section "The Design Philosophy of Format-Aware */
 /* Fusion": the producer is fused with the operation that creates its  */
-/* input).  Outside definitions: SwiGLU(g, u) = SiLU(g) * u with       */
+/* input).  Outside definition: SwiGLU(g, u) = SiLU(g) * u with        */
 /* SiLU(x) = x / (1 + e^-x) (Shazeer, "GLU Variants Improve            */
-/* Transformer", 2020); the exponential follows Cody and Waite,        */
-/* "Software Manual for the Elementary Functions" (1980): reduction by */
-/* a two-part ln 2, then a polynomial.                                 */
+/* Transformer", 2020).  H is that real number rounded once to bf16.   */
 /* ------------------------------------------------------------------ */
 
 /* float -> bf16 bits, round to nearest even (NaN -> a quiet NaN). */
@@ -512,76 +510,42 @@ static uint16_t float_to_bf16_rne(float f)
 
 uint16_t oc_float_to_bf16(float f) { return float_to_bf16_rne(f); }
 
-/* e^t for t in [-20, 80], as one fixed sequence of binary32 operations (no
- * library call, so that any implementation of the same sequence returns the
- * same bits; fmaf is the IEEE fused multiply-add, one rounding):
- *   k = rint(t * log2(e))                      (round half to even)
- *   r = fma(-k, ln2_hi, t)                     exact: ln2_hi has 15 significant
- *                                              bits, so k * ln2_hi is exact and
- *                                              t - k * ln2_hi too (Sterbenz)
- *   r = fma(-k, ln2_lo, r)
- *   p = Horner with fma: 1/5040 -> 1/720 -> 1/120 -> 1/24 -> 1/6 -> 1/2 -> 1 -> 1
- *       (the degree-7 Taylor polynomial of e^r: truncation below 2^-27
- *       relative for |r| <= 0.35)
- *   e^t = p * 2^k                              (exact: the result is normal)
- * Constants as binary32 (hex): log2(e) 0x1.715476p+0, ln2_hi 0x1.62e4p-1,
- * ln2_lo 0x1.7f7d1cp-20, 1/5040 0x1.a01a02p-13, 1/720 0x1.6c16c2p-10,
- * 1/120 0x1.111112p-7, 1/24 0x1.555556p-5, 1/6 0x1.555556p-3. */
-float oc_exp_f32_seq(float t)
+/* The bf16 spacing (as a power-of-two exponent) at a finite a > 0: bf16 has
+ * 8 significant bits, so in [2^(e-1), 2^e) the step is 2^(e-8); below 2^-126
+ * (subnormals) it is 2^-133. */
+static int bf16_step_exp(double a)
 {
-    const float log2e = 0x1.715476p+0f, ln2_hi = 0x1.62e4p-1f, ln2_lo = 0x1.7f7d1cp-20f;
-    const float k = rintf(t * log2e);
-    float r = fmaf(-k, ln2_hi, t);
-    r = fmaf(-k, ln2_lo, r);
-    float p = 0x1.a01a02p-13f;
-    p = fmaf(p, r, 0x1.6c16c2p-10f);
-    p = fmaf(p, r, 0x1.111112p-7f);
-    p = fmaf(p, r, 0x1.555556p-5f);
-    p = fmaf(p, r, 0x1.555556p-3f);
-    p = fmaf(p, r, 0.5f);
-    p = fmaf(p, r, 1.0f);
-    p = fmaf(p, r, 1.0f);
-    return ldexpf(p, (int)k);
+    int e;
+    frexp(a, &e); /* a = f * 2^e, 0.5 <= f < 1 */
+    return e - 8 < -133 ? -133 : e - 8;
 }
 
-/* SiLU(x) = x * (1 / (1 + e^-x)) in binary32, division-free:
- *   t = min(max(-x, -20), 80)                  (NaN -> -20; clamping changes
- *                                              nothing below -20, where
- *                                              1 + e^t rounds to 1, and above
- *                                              80 gives x / (1 + e^80), within
- *                                              1e-33 of the true value)
- *   d = 1 + e^t                                (oc_exp_f32_seq)
- *   y = bits 0x7EF311C3 - bits(d)              (a linear reciprocal seed from
- *                                              the exponent and mantissa bits,
- *                                              within 5.1 % of 1/d)
- *   three Newton steps: q = fma(-d, y, 1), y = fma(y, q, y)
- *   SiLU = x * y
- * So SiLU(x) = x exactly for x > 20 (then d = 1 and y converges to 1) and a
- * NaN stays NaN. */
-static float bits_f32(uint32_t u)
+/* binary64 -> bf16 bits, rounded ONCE to nearest, ties to even (no binary32
+ * step in between); magnitudes at or above 2^128 (1 - 2^-9), the midpoint
+ * between the largest finite bf16 and 2^128, become infinities. */
+uint16_t oc_double_to_bf16(double v)
 {
-    float f;
-    memcpy(&f, &u, sizeof f);
-    return f;
-}
-
-static uint32_t f32_bits(float f)
-{
+    if (isnan(v)) return 0x7FC0;
+    const uint16_t s = signbit(v) ? 0x8000 : 0;
+    const double a = fabs(v);
+    if (a == 0.0) return s;
+    if (isinf(a)) return s | 0x7F80;
+    const int q = bf16_step_exp(a);
+    const double r = ldexp(rint(ldexp(a, -q)), q); /* exact scalings; rint: half to even */
+    if (r >= 0x1p128) return s | 0x7F80;
+    const float f = (float)r; /* exact: r is a bf16 value */
     uint32_t u;
     memcpy(&u, &f, sizeof u);
-    return u;
+    return (uint16_t)(s | (u >> 16));
 }
 
-float oc_silu_f32(float x)
+/* SiLU(g) * u evaluated in binary64: the product g u of two bf16 values is
+ * exact, then one division by 1 + e^-g (libm exp).  Relative error a few
+ * binary64 ulps (below 2^-50), far finer than the bf16 step (2^-8). */
+double oc_swiglu_f64(float g, float u)
 {
-    const float t = fminf(fmaxf(-x, -20.0f), 80.0f);
-    const float d = 1.0f + oc_exp_f32_seq(t);
-    float y = bits_f32(0x7EF311C3u - f32_bits(d));
-    for (int i = 0; i < 3; ++i) {
-        const float q = fmaf(-d, y, 1.0f);
-        y = fmaf(y, q, y);
-    }
-    return x * y;
+    const double p = (double)g * (double)u;
+    return p / (1.0 + exp(-(double)g));
 }
 
 /* H[m][j] = bf16(SiLU(g) * u), g and u the bf16 gate and up values of
@@ -590,10 +554,15 @@ float oc_silu_f32(float x)
  * columns j of group b = j / pair sit at 2 pair b + (j mod pair), the up
  * columns `pair` further -- so pair = 32 is the layout whose 32-column gate
  * and up blocks share an accumulator lane, and pair = F is [gate | up].
- * The product is one binary32 multiply, rounded to bf16 to nearest even
- * (the activation's bf16 output, before the MX producer).  Returns 0, or -1
- * if pair does not divide F. */
-int oc_swiglu_bf16(const uint16_t *c, int64_t M, int64_t F, int64_t ldc, int64_t pair, uint16_t *h)
+ * Each element is oc_swiglu_f64 rounded once to bf16 (nearest, ties to
+ * even).  This is the rounding of the real value SiLU(g) u except where
+ * that value lies within the binary64 error (2^-50 relative) of a bf16
+ * midpoint -- for example an exact tie g u when e^-g falls below the
+ * binary64 resolution, whose real value lies just inside the midpoint.
+ * If hv is not null it also receives the binary64 value of each element,
+ * for tests that bound a kernel's deviation.  Returns 0, or -1 if pair does
+ * not divide F. */
+int oc_swiglu_bf16(const uint16_t *c, int64_t M, int64_t F, int64_t ldc, int64_t pair, uint16_t *h, double *hv)
 {
     if (pair <= 0 || F % pair != 0) return -1;
     for (int64_t m = 0; m < M; ++m)
@@ -601,7 +570,16 @@ int oc_swiglu_bf16(const uint16_t *c, int64_t M, int64_t F, int64_t ldc, int64_t
             const int64_t gcol = (j / pair) * 2 * pair + (j % pair);
             const float g = bf16_bits_to_float(c[m * ldc + gcol]);
             const float u = bf16_bits_to_float(c[m * ldc + gcol + pair]);
-            h[m * F + j] = float_to_bf16_rne(oc_silu_f32(g) * u);
+            const double v = oc_swiglu_f64(g, u);
+            h[m * F + j] = oc_double_to_bf16(v);
+            if (hv) hv[m * F + j] = v;
         }
     return 0;
+}
+
+/* bf16 bits of an array of binary64 values, each rounded once (the bf16
+ * output of an exact GEMM result). */
+void oc_double_to_bf16_array(const double *v, int64_t n, uint16_t *out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = oc_double_to_bf16(v[i]);
 }

@@ -62,9 +62,21 @@ def gemm_check(c_gpu, c_ref, w, what, tol=1e-5):
     return float((err / np.maximum(w, 1e-300)).max())
 
 
+def untile_mx(codes_t, scales_t, R, K):
+    """Inverse of the tiled consumer layout (oracle.tile_mx): returns the
+    linear codes [R, K/2] and scales [R, K/32] plus the padding rows'
+    codes and scales (which a producer must write as zeros)."""
+    codes_t = np.asarray(codes_t, dtype=np.uint8)
+    scales_t = np.asarray(scales_t, dtype=np.uint8)
+    Rp = (R + 31) // 32 * 32
+    c = codes_t.reshape(Rp // 32, K // 64, 2, 32, 16).transpose(0, 3, 1, 2, 4).reshape(Rp, K // 2)
+    s = scales_t.reshape(K // 128, Rp, 4).transpose(1, 0, 2).reshape(Rp, K // 32)
+    return c[:R], s[:R], c[R:], s[R:]
+
+
 def bf16_bits_of(t):
     return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
 
 
 __all__ = ["device", "announce", "to_dev", "np_u8", "assert_bytes_equal", "gemm_check", "B", "synth", "oracle",
-           "bf16_bits_of"]
+           "bf16_bits_of", "untile_mx"]

@@ -25,6 +25,33 @@ void h_silu_batch(const float *x, float *out, size_t n)
 {
     for (size_t i = 0; i < n; ++i) out[i] = fp4q::silu_f32(x[i]);
 }
+// H = bf16(SiLU(g) u) as the SwiGLU kernels compute it: binary32 SiLU of the
+// bf16 gate, one binary32 product, round to nearest even
+void h_swiglu_batch(const uint16_t *g, const uint16_t *u, uint16_t *out, size_t n)
+{
+    for (size_t i = 0; i < n; ++i)
+        out[i] = (uint16_t)fp4q::f32_to_bf16_rne(fp4q::silu_f32(fp4q::bf16_lo(g[i])) * fp4q::bf16_lo(u[i]));
+}
+// chunks visited by one thread of the partial-maximum pass: count, index sum
+// and the largest index (visit4 counts its four chunks)
+void h_grid_stride(uint32_t start, uint32_t stride, uint32_t n, uint64_t *out)
+{
+    uint64_t cnt = 0, sum = 0, hi = 0;
+    auto one = [&](uint32_t c) {
+        ++cnt;
+        sum += c;
+        hi = c > hi ? c : hi;
+    };
+    fp4q::grid_stride_chunks(
+        start, stride, n,
+        [&](uint32_t c) {
+            for (int i = 0; i < 4; ++i) one(c + (uint32_t)i * stride);
+        },
+        one);
+    out[0] = cnt;
+    out[1] = sum;
+    out[2] = hi;
+}
 void h_e2m1_sr_batch(const float *y, const uint32_t *r, uint8_t *out, size_t n)
 {
     for (size_t i = 0; i < n; ++i) out[i] = (uint8_t)fp4q::e2m1_sr(y[i], r[i]);

@@ -4,6 +4,7 @@ and rejects bad arguments with the documented status before any HIP call
 import ctypes
 
 import pytest
+import torch
 
 from fp4_block_scaled_quantizer_amd import binding as B
 
@@ -291,3 +292,35 @@ def test_size_limits():
     assert g(M=256, N=2 ** 20) == B.ESHAPE
     # dimensions above INT32_MAX are rejected outright
     assert g(M=2 ** 31) == B.ESHAPE
+
+
+def test_binding_rejects_wrong_output_buffers():
+    # the C ABI cannot see buffer sizes: the binding checks every
+    # caller-supplied output before calling it (CPU tensors: it raises
+    # before any library call)
+    x = torch.zeros((64, 128), dtype=torch.bfloat16)
+    u8 = torch.uint8
+    bad_mx = [
+        dict(codes=torch.zeros((63, 64), dtype=u8)),                    # too few rows
+        dict(codes=torch.zeros((64, 128), dtype=u8)[:, :64]),           # strided view
+        dict(codes=torch.zeros((64, 64), dtype=torch.int16)),           # dtype
+        dict(scales=torch.zeros((64, 3), dtype=u8)),                    # shape
+    ]
+    for kw in bad_mx:
+        with pytest.raises(ValueError):
+            B.fp4_quantize_mx(x, **kw)
+    with pytest.raises(ValueError):
+        B.fp4_quantize_mx(x, layout=B.LAYOUT_TILED, codes=torch.zeros((64, 64), dtype=u8),
+                          scales=torch.zeros((64, 4), dtype=u8))      # tiled scales are [K/128, Rp, 4]
+    for kw in [dict(codes=torch.zeros((64, 32), dtype=u8)), dict(scales=torch.zeros((64, 4), dtype=u8)),
+               dict(tensor_scale=torch.zeros((2,), dtype=torch.float32)),
+               dict(tensor_scale=torch.zeros((1,), dtype=torch.float64))]:
+        with pytest.raises(ValueError):
+            B.fp4_quantize_nv(x, B.NV_GLOBAL, **kw)
+    a = torch.zeros((64, 64), dtype=u8)
+    s = torch.zeros((64, 4), dtype=u8)
+    for c in [torch.zeros((63, 64)), torch.zeros((64, 128))[:, ::2], torch.zeros((64, 64), dtype=torch.float16)]:
+        with pytest.raises(ValueError):
+            B.fp4_gemm_mx(a, s, a, s, c=c)
+    with pytest.raises(ValueError):
+        B.fp4_swiglu_bf16(torch.zeros((4, 64), dtype=torch.bfloat16), 32, h=torch.zeros((4, 16), dtype=torch.bfloat16))

@@ -45,3 +45,18 @@ def test_tile_mx_block_is_one_mfma_operand():
     flat = t.reshape(-1)
     for l in range(64):
         assert np.all(flat[l * 16:(l + 1) * 16] == l % 32)
+
+
+@pytest.mark.parametrize("R,K", [(1, 128), (33, 256), (64, 512), (95, 384)])
+def test_untile_inverts_tile(R, K):
+    # the tests' inverse of the tiled layout (used to read fused kernels'
+    # tiled outputs) undoes oracle.tile_mx and exposes zero padding rows
+    from tests.gpu_common import untile_mx
+
+    rng = np.random.default_rng(R * K)
+    codes = rng.integers(0, 256, (R, K // 2), dtype=np.uint8)
+    scales = rng.integers(0, 256, (R, K // 32), dtype=np.uint8)
+    tc, ts = oracle.tile_mx(codes, scales)
+    c, s, cpad, spad = untile_mx(tc, ts, R, K)
+    assert np.array_equal(c, codes) and np.array_equal(s, scales)
+    assert not cpad.any() and not spad.any()

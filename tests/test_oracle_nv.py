@@ -19,6 +19,32 @@ def test_nv_worked_example_global_and_tile():
         assert codes.ravel().tolist() == g["nv_codes"]
 
 
+@pytest.mark.parametrize("case", ["order1", "order2"])
+def test_nv_operation_order_golden(case):
+    # hand-derived cases whose bytes depend on the order of the binary32
+    # operations: (b / 6) / S for the block scale (case 1) and x * (1 / d)
+    # for the elements (case 2)
+    g = golden_io.load("nv_op_order.txt")
+    x = golden_io.bf16_row(g[f"{case}_x"])
+    for dom in (oracle.NV_GLOBAL, oracle.NV_TILE128):
+        codes, scales, ts = oracle.quantize_nv(x, domain=dom)
+        assert ts.ravel().view(np.uint32).tolist() == g[f"{case}_tensor_scale_f32"]
+        assert scales.ravel().tolist() == g[f"{case}_scales"]
+        assert codes.ravel().tolist() == g[f"{case}_codes"]
+
+
+def test_nv_operation_order_cases_discriminate():
+    # the other orders, in binary32, change a byte of the golden cases: so
+    # an oracle (or kernel) using them fails the test above
+    f32 = np.float32
+    S = f32(976) / f32(2688)
+    assert oracle.e4m3_rne_satfinite(float((f32(22.875) / f32(6)) / S)) == 0x52
+    assert oracle.e4m3_rne_satfinite(float(f32(22.875) / (f32(6) * S))) == 0x53
+    d = f32(1.875)
+    assert oracle.e2m1_rne(float(f32(2.34375) * (f32(1) / d))) == 3
+    assert oracle.e2m1_rne(float(f32(2.34375) / d)) == 2
+
+
 def test_nv_tensor_scale_and_block_scale_closed_forms():
     assert oracle.nv_tensor_scale(0.0) == 1.0
     assert oracle.nv_tensor_scale(2688.0) == 1.0
