@@ -2,21 +2,24 @@
 """Benchmark of the FP4 hot path on one MI355X.
 
 A step is one pass of the path over one batch of synthetic Llama-3-8B-shaped
-operands: quantize the activation, quantize the weight (both re-quantized every
-step, as in training where weights change), then the block-scaled FP4 GEMM.
-The default workload is the QKV projection forward (MXFP4, RNE):
-X bf16 8192x4096, W bf16 6144x4096, C = X W^T bf16 8192x6144.
+operands.  The default workload is the MLP forward (MXFP4, RNE), the largest
+one-GPU configuration: quantize X (8192x4096) and W_gate/up (28672x4096),
+the gate/up GEMM (8192x28672x4096, bf16 out), quantize H (8192x14336, a
+SiLU-product-like bf16 input) and W_down (4096x14336), the down GEMM
+(8192x4096x14336, bf16 out).  Weights are re-quantized every step, as in
+training where they change.
 
-Prints one JSON line.  `value` is quantize+GEMM TFLOP/s = 2MNK / (time per
-step), with inputs resident in HBM (several input copies are rotated so the
-producers read from HBM, not from the 256 MB Infinity Cache).  The timed region is
-K steps launched back to back, after the warmup steps and the per-kernel
-passes.  `roofline` describes the dominant kernel: its average launch
-duration from HIP events on the launch stream, in a pass of K steps with an
-event pair around that kernel's launches only (an event marker between two
-kernels costs a few microseconds of GPU time, so the step timing has none);
-`kernels` lists every kernel of the step; `cpu_baseline` times the CPU oracle
-on one full step on the host cores.
+Prints one JSON line.  `value` is quantize+GEMM TFLOP/s = GEMM flops per step
+/ time per step, with inputs resident in HBM (several input copies are
+rotated so the producers read from HBM, not from the 256 MB Infinity Cache).
+The timed region is K steps launched back to back with no event markers
+between kernels.  `roofline` describes the dominant kernel (by name: for the
+MLP, gemm_mx_kernel, both GEMMs): its algorithmic flops (or bytes) per
+launch over its average launch duration, from HIP events on the launch
+stream around each of its launches in a second pass of K steps (a marker
+costs the GPU a few microseconds, so the `value` pass has none);
+`kernels` lists every op of the step; `cpu_baseline` times the CPU oracle
+on a bounded slice of the same step, single-threaded and on every host core.
 """
 from __future__ import annotations
 
@@ -47,7 +50,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="qkv",
+    ap.add_argument("--workload", default="mlp",
                     choices=["qkv", "mlp", "backward", "backward_dual", "dual_x", "nvfp4_global", "nvfp4_tile",
                              "nvfp4_chain", "nvfp4_chain_2pass", "nvfp4_wgrad", "mlp_chain", "mlp_chain_fused",
                              "mlp_swiglu", "mlp_swiglu_fused", "copy"],
@@ -481,32 +484,71 @@ def source_hash(paths):
     return h.hexdigest()[:16]
 
 
+def _oracle_quantize_rows(oracle, x, threads):
+    """oracle.quantize_mx of bf16 bits x along rows, the rows split over
+    `threads` host threads (the oracle's C releases the GIL; rows are
+    independent, so the result is the single-threaded one)."""
+    import concurrent.futures as cf
+
+    import numpy as np
+
+    if threads <= 1 or x.shape[0] < 2 * threads:
+        return oracle.quantize_mx(x)
+    parts = np.array_split(np.arange(x.shape[0]), threads)
+    with cf.ThreadPoolExecutor(max_workers=threads) as ex:
+        res = list(ex.map(lambda ix: oracle.quantize_mx(x[ix[0]:ix[-1] + 1]), [p for p in parts if p.size]))
+    return np.concatenate([r[0] for r in res]), np.concatenate([r[1] for r in res])
+
+
 def cpu_baseline(workload):
-    """The oracle, as it stands, on one full step of the qkv workload."""
-    if workload != "qkv":
+    """The oracle, as it stands, on a bounded slice of one step of the
+    workload (MXFP4 forward workloads): every operand cut to half of its
+    rows (tokens and output features alike), so each GEMM does 1/4 of its
+    flops, timed once on one thread and once on every host core; value = the
+    slice's GEMM flops / its time, in TFLOP/s."""
+    if workload not in ("qkv", "mlp"):
         return None
     import numpy as np
-    from threadpoolctl import threadpool_info
+    from threadpoolctl import threadpool_limits
 
     import oracle
     from fp4_block_scaled_quantizer_amd import synth
 
-    x = synth.bf16_bits(synth.config_tensor("qkv", "X"))
-    w = synth.bf16_bits(synth.config_tensor("qkv", "W"))
-    M, K = x.shape
-    N = w.shape[0]
-    t0 = time.perf_counter()
-    cx, sx = oracle.quantize_mx(x)
-    cw, sw = oracle.quantize_mx(w)
-    C, W = oracle.gemm_ref(oracle.dequant_mx(cx, sx), oracle.dequant_mx(cw, sw))
-    dt = time.perf_counter() - t0
-    del C, W
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    return {"value": 2.0 * M * N * K / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "seconds": round(dt, 3),
-            "sample": f"one full step: oracle.quantize_mx of X {M}x{K} and W {N}x{K} (single-threaded C), "
-                      f"dequantize, float64 numpy matmul for C and sum|ab| ({threads} BLAS threads)",
-            "host_cpu": platform.processor() or platform.machine(), "host_nproc": os.cpu_count()}
+    frac = 2
+    if workload == "qkv":
+        parts = [("qkv", "X", "qkv", "W")]
+    else:
+        parts = [("mlp_gate_up", "X", "mlp_gate_up", "W"), ("mlp_down", "H", "mlp_down", "W")]
+    slices = []
+    flops = 0.0
+    for ca, ra, cb, rb in parts:
+        a = synth.bf16_bits(synth.config_tensor(ca, ra))
+        b = synth.bf16_bits(synth.config_tensor(cb, rb))
+        a = np.ascontiguousarray(a[:a.shape[0] // frac])
+        b = np.ascontiguousarray(b[:b.shape[0] // frac])
+        slices.append((a, b))
+        flops += 2.0 * a.shape[0] * b.shape[0] * a.shape[1]
+    ncores = os.cpu_count() or 1
+
+    def run(threads):
+        with threadpool_limits(limits=threads):
+            t0 = time.perf_counter()
+            for a, b in slices:
+                qa = _oracle_quantize_rows(oracle, a, threads)
+                qb = _oracle_quantize_rows(oracle, b, threads)
+                oracle.gemm_ref(oracle.dequant_mx(*qa), oracle.dequant_mx(*qb), weights=False)
+            return time.perf_counter() - t0
+
+    t1 = run(1)
+    tn = run(ncores)
+    shapes = [[int(a.shape[0]), int(b.shape[0]), int(a.shape[1])] for a, b in slices]
+    return {"value": round(flops / tn / 1e12, 4), "unit": "TFLOP/s", "cores": ncores, "kind": "oracle",
+            "seconds": round(tn, 3), "single_thread": {"value": round(flops / t1 / 1e12, 4), "seconds": round(t1, 3),
+                                                         "cores": 1},
+            "sample": f"half of every operand's rows (GEMMs M x N x K = {shapes}, {flops / 1e9:.0f} GFLOP): "
+                      "oracle.quantize_mx of both operands (C, rows split over the threads), dequantize, float64 "
+                      "numpy matmul; value = the slice's GEMM flops / its time",
+            "host_cpu": platform.processor() or platform.machine(), "host_nproc": ncores}
 
 
 def main():
@@ -537,30 +579,31 @@ def main():
             torch.cuda.synchronize()
     torch.cuda.synchronize()
 
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+
     nops = len(ops)
-    # Per-kernel durations, measured in the step: for each op, K steps with a
-    # HIP event pair around that op's launch only (every event marker between
-    # two kernels costs the GPU a few microseconds, so one op is bracketed per
-    # pass and the step timing below has none).
+    # Per-op durations in the step: for each op, K steps with a HIP event pair
+    # around that op's launch only.
     op_ms = []
     for i in range(nops):
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        evs = [(ev(), ev()) for _ in range(args.steps)]
         for s in range(args.steps):
             for j, op in enumerate(ops):
                 if j == i:
-                    ev[s][0].record(stream)
+                    evs[s][0].record(stream)
                 op[2](s)
                 if j == i:
-                    ev[s][1].record(stream)
+                    evs[s][1].record(stream)
         torch.cuda.synchronize()
-        op_ms.append([e0.elapsed_time(e1) for e0, e1 in ev])
+        op_ms.append([e0.elapsed_time(e1) for e0, e1 in evs])
 
     # Each op also as a batch of back-to-back launches (no markers at all),
     # for the short producers where even two markers per step matter.
     batch = 20
     batched_ms = []
     for i, op in enumerate(ops):
-        b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        b0, b1 = ev(), ev()
         b0.record(stream)
         for r in range(batch):
             op[2](r)
@@ -568,9 +611,15 @@ def main():
         torch.cuda.synchronize()
         batched_ms.append(b0.elapsed_time(b1) / batch)
 
+    # The dominant kernel: the kernel name with the most time per step.
+    per_kernel = {}
+    for i, op in enumerate(ops):
+        per_kernel[op[1]] = per_kernel.get(op[1], 0.0) + sum(op_ms[i]) / len(op_ms[i])
+    dom_name = max(per_kernel, key=per_kernel.get)
+    dom_ops = [i for i, op in enumerate(ops) if op[1] == dom_name]
+
     # Timed region: K steps launched back to back.
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
+    t_start, t_end = ev(), ev()
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t_start.record(stream)
@@ -584,6 +633,26 @@ def main():
     gpu_ms = t_start.elapsed_time(t_end)
     ms_per_step = gpu_ms / args.steps
 
+    # Roofline pass: the same K steps with an event pair around every launch
+    # of the dominant kernel (on the stream it is launched on).
+    dom_ev = []
+    r_start, r_end = ev(), ev()
+    r_start.record(stream)
+    for s in range(args.steps):
+        for j, op in enumerate(ops):
+            if j in dom_ops:
+                e0, e1 = ev(), ev()
+                e0.record(stream)
+                op[2](s)
+                e1.record(stream)
+                dom_ev.append((j, e0, e1))
+            else:
+                op[2](s)
+    r_end.record(stream)
+    torch.cuda.synchronize()
+    dom_ms = [(j, e0.elapsed_time(e1)) for j, e0, e1 in dom_ev]
+    ms_per_step_marked = r_start.elapsed_time(r_end) / args.steps
+
     kernels = []
     for i, (label, kname, _, amount, unit, peak, bound) in enumerate(ops):
         durs = op_ms[i]
@@ -594,18 +663,26 @@ def main():
                         "avg_us_batched": round(batched_ms[i] * 1e3, 2), "min_us": round(min(durs) * 1e3, 2),
                         "achieved": round(achieved, 1), "unit": unit, "peak": peak,
                         "frac": round(achieved / peak, 4), "bound": bound, "algorithmic": amount})
-    dom = max(range(nops), key=lambda i: kernels[i]["avg_us"])
-    dk = kernels[dom]
-    roofline = {"bound": dk["bound"], "achieved": dk["achieved"], "peak": dk["peak"], "unit": dk["unit"],
-                "frac": dk["frac"], "traffic": read_traffic(dk["kernel"], args.workload), "kernel": dk["kernel"],
-                "op": dk["op"], "avg_us": dk["avg_us"]}
+    d0 = ops[dom_ops[0]]
+    unit, peak, bound = d0[4], d0[5], d0[6]
+    amount_per_launch = sum(ops[j][3] for j in dom_ops) / len(dom_ops)
+    avg_launch_ms = sum(t for _, t in dom_ms) / len(dom_ms)
+    achieved = amount_per_launch / (avg_launch_ms * 1e-3) / (1e9 if unit == "GB/s" else 1e12)
+    roofline = {"bound": bound, "achieved": round(achieved, 1), "peak": peak, "unit": unit,
+                "frac": round(achieved / peak, 4), "traffic": read_traffic(dom_name, args.workload),
+                "kernel": dom_name, "ops": [ops[j][0] for j in dom_ops],
+                "launches_per_step": len(dom_ops), "avg_launch_us": round(avg_launch_ms * 1e3, 2),
+                "algorithmic_per_launch": amount_per_launch,
+                "avg_launch_us_by_op": {ops[j][0]: round(1e3 * sum(t for jj, t in dom_ms if jj == j) /
+                                                         max(1, sum(1 for jj, _ in dom_ms if jj == j)), 2)
+                                        for j in dom_ops}}
     # workloads without a GEMM (a producer alone, the copy calibration) report
     # the dominant kernel's rate
-    value = step_flops / (ms_per_step * 1e-3) / 1e12 if step_flops else dk["achieved"]
+    value = step_flops / (ms_per_step * 1e-3) / 1e12 if step_flops else achieved
     out = {
-        "metric": "quantize+FP4 GEMM TFLOP/s (Llama-3-8B shapes)" if step_flops else f"{dk['op']} {dk['unit']}",
+        "metric": "quantize+FP4 GEMM TFLOP/s (Llama-3-8B shapes)" if step_flops else f"{d0[0]} {unit}",
         "value": round(value, 1),
-        "unit": "TFLOP/s" if step_flops else dk["unit"],
+        "unit": "TFLOP/s" if step_flops else unit,
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -620,6 +697,7 @@ def main():
         "config": cfg,
         "roofline": roofline,
         "kernels": kernels,
+        "ms_per_step_roofline_pass": round(ms_per_step_marked, 5),
         "wall_s_timed": round(wall, 4),
         "host_enqueue_us_per_step": round(enqueue / args.steps * 1e6, 1),
     }
