@@ -69,9 +69,11 @@ def lib() -> ctypes.CDLL:
     L.fp4_swiglu_bf16.argtypes = [vp, i64, i64, i64, i64, vp, i64, vp]
     L.fp4_gemm_nv_amax.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, i64, i64, f32, i32, vp, i32, i64, vp, vp]
     L.fp4_quantize_nv_amax.argtypes = [vp, i64, i64, i64, i32, u64, u32, vp, vp, vp, vp, vp]
+    L.fp4_quantize_nv_noalloc.argtypes = [vp, i64, i64, i64, i32, i32, u64, u32, i32, vp, vp, vp, i32, vp]
     L.fp4_hadamard32_quantize_nv.argtypes = [vp, i64, i64, i64, i32, u32, i32, u64, u32, i32, vp, vp, vp, vp,
                                              ctypes.c_size_t, i32, vp]
     for fn in ("fp4_quantize_mx", "fp4_hadamard32_quantize", "fp4_quantize_mx_dual", "fp4_quantize_nv",
+               "fp4_quantize_nv_noalloc",
                "fp4_quantize_nv_amax", "fp4_hadamard32_quantize_nv", "fp4_gemm_mx", "fp4_gemm_nv",
                "fp4_gemm_mx_amax", "fp4_gemm_nv_amax", "fp4_gemm_mx_quant"):
         getattr(L, fn).restype = i32
@@ -256,6 +258,30 @@ def fp4_quantize_nv(x: torch.Tensor, domain: int = NV_GLOBAL, *, cols: Optional[
            lib().fp4_quantize_nv(x.data_ptr(), rows, cols, ld, axis, round, seed, stream_id, domain,
                                  codes.data_ptr(), scales.data_ptr(), tensor_scale.data_ptr(), _ptr(workspace),
                                  wbytes, LAYOUT_LINEAR, _stream(stream)))
+    return codes, scales, tensor_scale
+
+
+def fp4_quantize_nv_noalloc(x: torch.Tensor, domain: int = NV_GLOBAL, *, cols: Optional[int] = None,
+                            axis: int = ALONG_ROWS, round: int = RNE, seed: int = 0, stream_id: int = 0,
+                            codes: Optional[torch.Tensor] = None, scales: Optional[torch.Tensor] = None,
+                            tensor_scale: Optional[torch.Tensor] = None, stream=None):
+    """fp4_quantize_nv with the library's own workspace: the call allocates
+    no device memory (pass every output to allocate none here either)."""
+    rows, cols, ld = _input(x, cols)
+    R, K = _logical(rows, cols, axis)
+    if codes is None:
+        codes = torch.empty((R, K // 2), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((R, K // 16), dtype=torch.uint8, device=x.device)
+    if tensor_scale is None:
+        tensor_scale = torch.empty(nv_tensor_scale_shape(R, K, domain), dtype=torch.float32, device=x.device)
+    _check_out(codes, "codes", torch.uint8, (R, K // 2), x.device)
+    _check_out(scales, "scales", torch.uint8, (R, K // 16), x.device)
+    _check_out(tensor_scale, "tensor_scale", torch.float32, nv_tensor_scale_shape(R, K, domain), x.device)
+    _check("fp4_quantize_nv_noalloc",
+           lib().fp4_quantize_nv_noalloc(x.data_ptr(), rows, cols, ld, axis, round, seed, stream_id, domain,
+                                         codes.data_ptr(), scales.data_ptr(), tensor_scale.data_ptr(), LAYOUT_LINEAR,
+                                         _stream(stream)))
     return codes, scales, tensor_scale
 
 

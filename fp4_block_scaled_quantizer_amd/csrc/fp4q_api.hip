@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/fp4q.h"
 #include "fp4q_internal.h"
 
@@ -248,10 +250,39 @@ fp4q_status run_gemm_nv(const void *a_codes, const void *a_scales, const float *
 }
 
 
+// The allocation-free variant's workspace: the global domain's partial
+// maxima (at most 1024 x 4 bytes, whatever the operand's size), in a
+// file-scope device array.  Each GPU holds its own copy until the process
+// ends; host code uses the address hipGetSymbolAddress returns for the
+// current device, never the array's name.
+constexpr size_t kScratchBytes = 4096;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch[kMaxDevices];
+
+// The current device's copy of `scratch` (looked up once per device).
+fp4q_status scratch_of_current_device(void **out)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return FP4Q_ELAUNCH;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return FP4Q_ELAUNCH;
+        g_scratch[dev] = p;
+    }
+    *out = g_scratch[dev];
+    return FP4Q_OK;
+}
+
+// use_scratch: the workspace is the library's `scratch` (workspace and
+// workspace_bytes are ignored); looked up after every argument check.
 fp4q_status run_quantize_nv(const void *x, int64_t rows, int64_t cols, int64_t ld_x, int axis, int round,
                             uint64_t seed, uint32_t stream_id, int domain, void *codes, void *scales,
                             float *tensor_scale, void *workspace, size_t workspace_bytes, int layout,
-                            const float *given_amax, bool hadamard, uint32_t sign_mask, void *stream)
+                            const float *given_amax, bool hadamard, uint32_t sign_mask, void *stream,
+                            bool use_scratch = false)
 {
     if ((axis != FP4Q_ALONG_ROWS && axis != FP4Q_ALONG_COLS) || (round != FP4Q_RNE && round != FP4Q_SR) ||
         (domain != FP4Q_NV_GLOBAL && domain != FP4Q_NV_TILE128) ||
@@ -272,12 +303,17 @@ fp4q_status run_quantize_nv(const void *x, int64_t rows, int64_t cols, int64_t l
     if (!empty && (!aligned(x, 16) || !aligned(codes, 16) || ld_x % 8 != 0)) return FP4Q_EALIGN;
     if (!aligned(tensor_scale, 4)) return FP4Q_EALIGN;
     const size_t need = given_amax ? 0 : fp4q_nv_workspace_bytes(rows, cols, axis, domain);
-    if (need > 0 && (!workspace || workspace_bytes < need)) return FP4Q_EINVAL;
-    if (need > 0 && !aligned(workspace, 4)) return FP4Q_EALIGN;
+    if (use_scratch) {
+        if (need > kScratchBytes) return FP4Q_EINVAL;  // the partial maxima never need more
+        workspace = nullptr;
+    } else {
+        if (need > 0 && (!workspace || workspace_bytes < need)) return FP4Q_EINVAL;
+        if (need > 0 && !aligned(workspace, 4)) return FP4Q_EALIGN;
+    }
     const uint64_t nts = domain == FP4Q_NV_GLOBAL ? 1 : (uint64_t)((R + 127) / 128) * (uint64_t)((K + 127) / 128);
     const Range rx = bytes(x, input_span(rows, cols, ld_x));
     const Range outs[4] = {bytes(codes, (uint64_t)R * K / 2), bytes(scales, (uint64_t)R * K / 16),
-                           bytes(tensor_scale, nts * 4), bytes(workspace, need)};
+                           bytes(tensor_scale, nts * 4), bytes(workspace, use_scratch ? 0 : need)};
     for (int i = 0; i < 4; ++i) {
         if (overlap(rx, outs[i])) return FP4Q_EINVAL;
         if (given_amax && overlap(bytes(given_amax, 4), outs[i])) return FP4Q_EINVAL;
@@ -297,6 +333,10 @@ fp4q_status run_quantize_nv(const void *x, int64_t rows, int64_t cols, int64_t l
     a.sign_mask = sign_mask;
     a.codes = codes;
     a.scales = scales;
+    if (use_scratch && need > 0) {
+        const fp4q_status st = scratch_of_current_device(&workspace);
+        if (st != FP4Q_OK) return st;
+    }
     (void)hipGetLastError();
     return launched(fp4q::launch_quant_nv(a, domain, tensor_scale, workspace, given_amax, as_stream(stream)));
 }
@@ -376,6 +416,14 @@ fp4q_status fp4_quantize_nv(const void *x, int64_t rows, int64_t cols, int64_t l
 {
     return run_quantize_nv(x, rows, cols, ld_x, axis, round, seed, stream_id, domain, codes, scales, tensor_scale,
                            workspace, workspace_bytes, layout, nullptr, false, 0u, stream);
+}
+
+fp4q_status fp4_quantize_nv_noalloc(const void *x, int64_t rows, int64_t cols, int64_t ld_x, int axis, int round,
+                                    uint64_t seed, uint32_t stream_id, int domain, void *codes, void *scales,
+                                    float *tensor_scale, int layout, void *stream)
+{
+    return run_quantize_nv(x, rows, cols, ld_x, axis, round, seed, stream_id, domain, codes, scales, tensor_scale,
+                           nullptr, 0, layout, nullptr, false, 0u, stream, true);
 }
 
 fp4q_status fp4_hadamard32_quantize_nv(const void *x, int64_t rows, int64_t cols, int64_t ld_x, int axis,

@@ -195,6 +195,26 @@ FP4Q_API fp4q_status fp4_quantize_nv(const void *x, int64_t rows, int64_t cols, 
                             float *tensor_scale, void *workspace, size_t workspace_bytes, int layout,
                             void *stream);
 
+/* fp4_quantize_nv without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  The global domain's partial maxima go
+ * to a 4 KiB buffer inside the library (a file-scope device array; every GPU
+ * the library runs on holds its own copy until the process ends), so the
+ * call allocates nothing; the tile domain needs none.  Every output byte
+ * equals fp4_quantize_nv's for the same arguments.  The work runs on the
+ * current device, which must be the one `stream` belongs to.  All calls on
+ * one GPU share its buffer: calls that overlap in time on one GPU (on
+ * different streams, or from several host threads without ordering) race
+ * and give unspecified outputs; calls ordered on one stream do not (each
+ * call writes every slot it reads before reading it, so nothing needs
+ * clearing).  The buffer holds at most 1024 partial maxima, enough for any
+ * operand size; FP4Q_EINVAL if a build ever needed more.  Errors as
+ * fp4_quantize_nv, plus FP4Q_ELAUNCH if the buffer's device address cannot
+ * be obtained. */
+FP4Q_API fp4q_status fp4_quantize_nv_noalloc(const void *x, int64_t rows, int64_t cols, int64_t ld_x, int axis,
+                                            int round, uint64_t seed, uint32_t stream_id, int domain, void *codes,
+                                            void *scales, float *tensor_scale, int layout, void *stream);
+
 /* Fixed-sign 32-point Hadamard along K, then NVFP4 ([Fusion] section "Two Key
  * Numerical Techniques" names it for the weight-gradient operands; here on
  * the NVFP4 path): as fp4_quantize_nv on the transformed values, which the
