@@ -333,8 +333,9 @@ def build_workload(name, dev, copies, layout_name="tiled"):
         D = B.NV_TILE128
 
         def nvbufs(R, Kc):
-            return (torch.empty((R, Kc // 2), dtype=torch.uint8, device=dev),
-                    torch.empty((R, Kc // 16), dtype=torch.uint8, device=dev),
+            cs, ss = B.nv_output_shapes(R, Kc, L)
+            return (torch.empty(cs, dtype=torch.uint8, device=dev),
+                    torch.empty(ss, dtype=torch.uint8, device=dev),
                     torch.empty(B.nv_tensor_scale_shape(R, Kc, D), dtype=torch.float32, device=dev))
 
         bd, bx = nvbufs(O, T), nvbufs(I, T)
@@ -343,18 +344,19 @@ def build_workload(name, dev, copies, layout_name="tiled"):
             ("Hadamard-quantize dY^T (NVFP4 tile, SR)", "nv_quant_cols_kernel",
              lambda s: B.fp4_quantize_nv(dY[s % copies], D, axis=B.ALONG_COLS, round=B.SR, seed=synth.SR_SEED,
                                          stream_id=1, hadamard_mask=mask, codes=bd[0], scales=bd[1],
-                                         tensor_scale=bd[2]),
+                                         tensor_scale=bd[2], layout=L),
              T * O * NV_TILE_BYTES_PER_ELEM, "GB/s", HBM_PEAK_GBS, "hbm"),
             ("Hadamard-quantize X^T (NVFP4 tile)", "nv_quant_cols_kernel",
              lambda s: B.fp4_quantize_nv(X[s % copies], D, axis=B.ALONG_COLS, hadamard_mask=mask, codes=bx[0],
-                                         scales=bx[1], tensor_scale=bx[2]),
+                                         scales=bx[1], tensor_scale=bx[2], layout=L),
              T * I * NV_TILE_BYTES_PER_ELEM, "GB/s", HBM_PEAK_GBS, "hbm"),
             ("GEMM NVFP4 wgrad dY^T X (alpha 1/32)", "gemm_nv_fp16_kernel",
-             lambda s: B.fp4_gemm_nv(*bd, *bx, D, alpha=1.0 / 32, c=dW), 2.0 * O * I * T, "TFLOP/s",
-             BF16_PEAK_TFLOPS, "mfma"),
+             lambda s: B.fp4_gemm_nv(*bd, *bx, D, alpha=1.0 / 32, c=dW, layout=L, m=O, n=I), 2.0 * O * I * T,
+             "TFLOP/s", BF16_PEAK_TFLOPS, "mfma"),
         ]
         cfg = {"workload": "Llama-3-8B o_proj weight gradient, NVFP4 per-128x128-tile domain, fixed-sign Hadamard-32 "
-                           "along tokens, SR on dY", "wgrad_mnk": [O, I, T], "input_copies": copies}
+                           "along tokens, SR on dY", "wgrad_mnk": [O, I, T], "layout": layout_name,
+               "input_copies": copies}
         return cfg, ops, 2.0 * O * I * T
     if name in ("nvfp4_chain", "nvfp4_chain_2pass"):
         # two NVFP4 GEMMs in a row (Llama-3-8B MLP up and down shapes, global
@@ -422,14 +424,15 @@ def build_workload(name, dev, copies, layout_name="tiled"):
 
     def qnv(tag, src, R):
         ts_shape = B.nv_tensor_scale_shape(R, K, domain)
-        bufs[tag] = (torch.empty((R, K // 2), dtype=torch.uint8, device=dev),
-                     torch.empty((R, K // 16), dtype=torch.uint8, device=dev),
+        cs, ss = B.nv_output_shapes(R, K, L)
+        bufs[tag] = (torch.empty(cs, dtype=torch.uint8, device=dev),
+                     torch.empty(ss, dtype=torch.uint8, device=dev),
                      torch.empty(ts_shape, dtype=torch.float32, device=dev),
                      torch.empty((max(1, B.fp4q_nv_workspace_bytes(R, K, 0, domain)),), dtype=torch.uint8,
                                  device=dev))
         b = bufs[tag]
         return lambda s: B.fp4_quantize_nv(src[s % copies], domain, codes=b[0], scales=b[1], tensor_scale=b[2],
-                                           workspace=b[3] if domain == B.NV_GLOBAL else None)
+                                           workspace=b[3] if domain == B.NV_GLOBAL else None, layout=L)
 
     C = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     bpe = NV_GLOBAL_BYTES_PER_ELEM if domain == B.NV_GLOBAL else NV_TILE_BYTES_PER_ELEM
@@ -439,10 +442,11 @@ def build_workload(name, dev, copies, layout_name="tiled"):
         ("quantize W (NVFP4)", kname, qnv("w", W, N), N * K * bpe, "GB/s", HBM_PEAK_GBS, "hbm"),
         ("GEMM NVFP4 (fp16 MFMA)", "gemm_nv_fp16_kernel",
          lambda s: B.fp4_gemm_nv(bufs["x"][0], bufs["x"][1], bufs["x"][2], bufs["w"][0], bufs["w"][1], bufs["w"][2],
-                                 domain, c=C), 2.0 * M * N * K, "TFLOP/s", BF16_PEAK_TFLOPS, "mfma"),
+                                 domain, c=C, layout=L, m=M, n=N), 2.0 * M * N * K, "TFLOP/s", BF16_PEAK_TFLOPS,
+         "mfma"),
     ]
     cfg = {"workload": f"NVFP4 {'global' if domain == B.NV_GLOBAL else 'per-128x128-tile'} tensor scale",
-           "gemm_mnk": [M, N, K], "out": "bf16", "input_copies": copies}
+           "gemm_mnk": [M, N, K], "out": "bf16", "layout": layout_name, "input_copies": copies}
     return cfg, ops, 2.0 * M * N * K
 
 

@@ -213,29 +213,39 @@ def nv_tensor_scale_shape(R: int, K: int, domain: int):
     return (1,) if domain == NV_GLOBAL else ((R + 127) // 128, (K + 127) // 128)
 
 
+def nv_output_shapes(R: int, K: int, layout: int = LAYOUT_LINEAR):
+    """(codes shape, scales shape) of an NV operand [R x K] in `layout`: the
+    tiled layout stores Rp = 32 ceil(R/32) rows (same bytes per row)."""
+    Rs = (R + 31) // 32 * 32 if layout == LAYOUT_TILED else R
+    return (Rs, K // 2), (Rs, K // 16)
+
+
 def fp4_quantize_nv(x: torch.Tensor, domain: int = NV_GLOBAL, *, cols: Optional[int] = None, axis: int = ALONG_ROWS,
                     round: int = RNE, seed: int = 0, stream_id: int = 0, codes: Optional[torch.Tensor] = None,
                     scales: Optional[torch.Tensor] = None, tensor_scale: Optional[torch.Tensor] = None,
                     workspace: Optional[torch.Tensor] = None, amax: Optional[torch.Tensor] = None,
-                    hadamard_mask: Optional[int] = None, stream=None):
+                    hadamard_mask: Optional[int] = None, layout: int = LAYOUT_LINEAR, stream=None):
     """NVFP4; with `amax` (a device float32 tensor holding max |x|, global
     domain only) the producer runs in one pass (fp4_quantize_nv_amax); with
     `hadamard_mask` the fixed-sign Hadamard-32 runs first
     (fp4_hadamard32_quantize_nv, along columns)."""
     rows, cols, ld = _input(x, cols)
     R, K = _logical(rows, cols, axis)
+    cshape, sshape = nv_output_shapes(R, K, layout)
     if codes is None:
-        codes = torch.empty((R, K // 2), dtype=torch.uint8, device=x.device)
+        codes = torch.empty(cshape, dtype=torch.uint8, device=x.device)
     if scales is None:
-        scales = torch.empty((R, K // 16), dtype=torch.uint8, device=x.device)
+        scales = torch.empty(sshape, dtype=torch.uint8, device=x.device)
     if tensor_scale is None:
         tensor_scale = torch.empty(nv_tensor_scale_shape(R, K, domain), dtype=torch.float32, device=x.device)
-    _check_out(codes, "codes", torch.uint8, (R, K // 2), x.device)
-    _check_out(scales, "scales", torch.uint8, (R, K // 16), x.device)
+    _check_out(codes, "codes", torch.uint8, cshape, x.device)
+    _check_out(scales, "scales", torch.uint8, sshape, x.device)
     _check_out(tensor_scale, "tensor_scale", torch.float32, nv_tensor_scale_shape(R, K, domain), x.device)
     if amax is not None:
-        if domain != NV_GLOBAL or axis != ALONG_ROWS or amax.dtype != torch.float32 or amax.device != x.device:
-            raise ValueError("a given amax is a float32 tensor on x's device, for the global domain along rows")
+        if (domain != NV_GLOBAL or axis != ALONG_ROWS or amax.dtype != torch.float32 or amax.device != x.device
+                or layout != LAYOUT_LINEAR):
+            raise ValueError("a given amax is a float32 tensor on x's device, for the global domain along rows, "
+                             "linear layout")
         _check("fp4_quantize_nv_amax",
                lib().fp4_quantize_nv_amax(x.data_ptr(), rows, cols, ld, round, seed, stream_id, amax.data_ptr(),
                                           codes.data_ptr(), scales.data_ptr(), tensor_scale.data_ptr(),
@@ -251,36 +261,37 @@ def fp4_quantize_nv(x: torch.Tensor, domain: int = NV_GLOBAL, *, cols: Optional[
         _check("fp4_hadamard32_quantize_nv",
                lib().fp4_hadamard32_quantize_nv(x.data_ptr(), rows, cols, ld, axis, hadamard_mask & 0xFFFFFFFF, round,
                                                 seed, stream_id, domain, codes.data_ptr(), scales.data_ptr(),
-                                                tensor_scale.data_ptr(), _ptr(workspace), wbytes, LAYOUT_LINEAR,
+                                                tensor_scale.data_ptr(), _ptr(workspace), wbytes, layout,
                                                 _stream(stream)))
         return codes, scales, tensor_scale
     _check("fp4_quantize_nv",
            lib().fp4_quantize_nv(x.data_ptr(), rows, cols, ld, axis, round, seed, stream_id, domain,
                                  codes.data_ptr(), scales.data_ptr(), tensor_scale.data_ptr(), _ptr(workspace),
-                                 wbytes, LAYOUT_LINEAR, _stream(stream)))
+                                 wbytes, layout, _stream(stream)))
     return codes, scales, tensor_scale
 
 
 def fp4_quantize_nv_noalloc(x: torch.Tensor, domain: int = NV_GLOBAL, *, cols: Optional[int] = None,
                             axis: int = ALONG_ROWS, round: int = RNE, seed: int = 0, stream_id: int = 0,
                             codes: Optional[torch.Tensor] = None, scales: Optional[torch.Tensor] = None,
-                            tensor_scale: Optional[torch.Tensor] = None, stream=None):
+                            tensor_scale: Optional[torch.Tensor] = None, layout: int = LAYOUT_LINEAR, stream=None):
     """fp4_quantize_nv with the library's own workspace: the call allocates
     no device memory (pass every output to allocate none here either)."""
     rows, cols, ld = _input(x, cols)
     R, K = _logical(rows, cols, axis)
+    cshape, sshape = nv_output_shapes(R, K, layout)
     if codes is None:
-        codes = torch.empty((R, K // 2), dtype=torch.uint8, device=x.device)
+        codes = torch.empty(cshape, dtype=torch.uint8, device=x.device)
     if scales is None:
-        scales = torch.empty((R, K // 16), dtype=torch.uint8, device=x.device)
+        scales = torch.empty(sshape, dtype=torch.uint8, device=x.device)
     if tensor_scale is None:
         tensor_scale = torch.empty(nv_tensor_scale_shape(R, K, domain), dtype=torch.float32, device=x.device)
-    _check_out(codes, "codes", torch.uint8, (R, K // 2), x.device)
-    _check_out(scales, "scales", torch.uint8, (R, K // 16), x.device)
+    _check_out(codes, "codes", torch.uint8, cshape, x.device)
+    _check_out(scales, "scales", torch.uint8, sshape, x.device)
     _check_out(tensor_scale, "tensor_scale", torch.float32, nv_tensor_scale_shape(R, K, domain), x.device)
     _check("fp4_quantize_nv_noalloc",
            lib().fp4_quantize_nv_noalloc(x.data_ptr(), rows, cols, ld, axis, round, seed, stream_id, domain,
-                                         codes.data_ptr(), scales.data_ptr(), tensor_scale.data_ptr(), LAYOUT_LINEAR,
+                                         codes.data_ptr(), scales.data_ptr(), tensor_scale.data_ptr(), layout,
                                          _stream(stream)))
     return codes, scales, tensor_scale
 
@@ -394,10 +405,14 @@ def pair_gate_up(w_gate: torch.Tensor, w_up: torch.Tensor, pair: int = 32) -> to
 def fp4_gemm_nv(a_codes: torch.Tensor, a_scales: torch.Tensor, a_tensor_scale: torch.Tensor, b_codes: torch.Tensor,
                 b_scales: torch.Tensor, b_tensor_scale: torch.Tensor, domain: int = NV_GLOBAL, *, alpha: float = 1.0,
                 out_dtype=torch.float32, c: Optional[torch.Tensor] = None, c_amax: Optional[torch.Tensor] = None,
+                layout: int = LAYOUT_LINEAR, m: Optional[int] = None, n: Optional[int] = None,
                 stream=None) -> torch.Tensor:
     """With `c_amax` (a device float32 tensor) max |C| is folded into it
-    (fp4_gemm_nv_amax)."""
-    M, N, K = a_codes.shape[0], b_codes.shape[0], a_codes.shape[1] * 2
+    (fp4_gemm_nv_amax).  In the tiled layout the code tensors carry rows
+    padded to a multiple of 32, so pass the logical m and n."""
+    M = a_codes.shape[0] if m is None else m
+    N = b_codes.shape[0] if n is None else n
+    K = a_codes.shape[1] * 2
     if b_codes.shape[1] * 2 != K:
         raise ValueError("A and B must have the same K")
     c, ctype, ldc = _gemm_out(M, N, out_dtype, a_codes.device, c)
@@ -405,11 +420,11 @@ def fp4_gemm_nv(a_codes: torch.Tensor, a_scales: torch.Tensor, a_tensor_scale: t
         _check("fp4_gemm_nv_amax",
                lib().fp4_gemm_nv_amax(a_codes.data_ptr(), a_scales.data_ptr(), a_tensor_scale.data_ptr(),
                                       b_codes.data_ptr(), b_scales.data_ptr(), b_tensor_scale.data_ptr(), domain, M, N,
-                                      K, float(alpha), LAYOUT_LINEAR, c.data_ptr(), ctype, ldc, _amax_ptr(c_amax, a_codes.device),
+                                      K, float(alpha), layout, c.data_ptr(), ctype, ldc, _amax_ptr(c_amax, a_codes.device),
                                       _stream(stream)))
         return c
     _check("fp4_gemm_nv", lib().fp4_gemm_nv(a_codes.data_ptr(), a_scales.data_ptr(), a_tensor_scale.data_ptr(),
                                             b_codes.data_ptr(), b_scales.data_ptr(), b_tensor_scale.data_ptr(),
-                                            domain, M, N, K, float(alpha), LAYOUT_LINEAR, c.data_ptr(), ctype, ldc,
+                                            domain, M, N, K, float(alpha), layout, c.data_ptr(), ctype, ldc,
                                             _stream(stream)))
     return c

@@ -4,10 +4,30 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
 #include <mutex>
 
 #include "../../include/fp4q.h"
 #include "fp4q_internal.h"
+
+namespace fp4q {
+
+int device_cu_count()
+{
+    static std::atomic<int> cached[64];
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return -1;
+    if (dev < 64) {
+        const int c = cached[dev].load(std::memory_order_relaxed);
+        if (c > 0) return c;
+    }
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) return -1;
+    if (dev < 64) cached[dev].store(cus, std::memory_order_relaxed);
+    return cus;
+}
+
+}  // namespace fp4q
 
 namespace {
 
@@ -212,7 +232,6 @@ fp4q_status run_gemm_nv(const void *a_codes, const void *a_scales, const float *
                         void *stream)
 {
     if (domain != FP4Q_NV_GLOBAL && domain != FP4Q_NV_TILE128) return FP4Q_EINVAL;
-    if (layout == FP4Q_LAYOUT_TILED) return FP4Q_EUNSUPPORTED;
     bool empty = false;
     const fp4q_status st =
         check_gemm_common(a_codes, a_scales, b_codes, b_scales, M, N, K, layout, c, c_type, ldc, 16, &empty);
@@ -245,6 +264,7 @@ fp4q_status run_gemm_nv(const void *a_codes, const void *a_scales, const float *
     g.c_bf16 = c_type == FP4Q_OUT_BF16;
     g.ldc = ldc;
     g.c_amax = reinterpret_cast<uint32_t *>(c_amax);
+    g.tiled = layout == FP4Q_LAYOUT_TILED;
     (void)hipGetLastError();
     return launched(fp4q::launch_gemm_nv(g, as_stream(stream)));
 }
@@ -288,19 +308,21 @@ fp4q_status run_quantize_nv(const void *x, int64_t rows, int64_t cols, int64_t l
         (domain != FP4Q_NV_GLOBAL && domain != FP4Q_NV_TILE128) ||
         (layout != FP4Q_LAYOUT_LINEAR && layout != FP4Q_LAYOUT_TILED))
         return FP4Q_EINVAL;
-    if (layout == FP4Q_LAYOUT_TILED) return FP4Q_EUNSUPPORTED;
+    const bool tiled = layout == FP4Q_LAYOUT_TILED;
     if (rows < 0 || cols < 0 || ld_x < cols || rows > kMaxDim || cols > kMaxDim || ld_x > kMaxDim)
         return FP4Q_ESHAPE;
     if (hadamard && axis == FP4Q_ALONG_ROWS) return FP4Q_EUNSUPPORTED;
     const int64_t R = axis == FP4Q_ALONG_ROWS ? rows : cols, K = axis == FP4Q_ALONG_ROWS ? cols : rows;
-    if (K % (hadamard ? 32 : 16) != 0) return FP4Q_ESHAPE;
+    if (K % (tiled ? 128 : hadamard ? 32 : 16) != 0) return FP4Q_ESHAPE;
     if (axis == FP4Q_ALONG_COLS && cols % 4 != 0) return FP4Q_ESHAPE;
-    if ((uint64_t)R * (uint64_t)(K / 8) >= (1ull << 32)) return FP4Q_ESHAPE;
+    const int64_t Rs = tiled ? (R + 31) / 32 * 32 : R;  // rows of the stored operand
+    if ((uint64_t)Rs * (uint64_t)(K / 8) >= (1ull << 32)) return FP4Q_ESHAPE;
     const bool empty = R == 0 || K == 0;
     if (empty && domain == FP4Q_NV_TILE128) return FP4Q_OK;  // no tiles, no tensor scales
     if (!tensor_scale) return FP4Q_EINVAL;
     if (!empty && (!x || !codes || !scales)) return FP4Q_EINVAL;
     if (!empty && (!aligned(x, 16) || !aligned(codes, 16) || ld_x % 8 != 0)) return FP4Q_EALIGN;
+    if (!empty && tiled && !aligned(scales, 16)) return FP4Q_EALIGN;
     if (!aligned(tensor_scale, 4)) return FP4Q_EALIGN;
     const size_t need = given_amax ? 0 : fp4q_nv_workspace_bytes(rows, cols, axis, domain);
     if (use_scratch) {
@@ -312,7 +334,7 @@ fp4q_status run_quantize_nv(const void *x, int64_t rows, int64_t cols, int64_t l
     }
     const uint64_t nts = domain == FP4Q_NV_GLOBAL ? 1 : (uint64_t)((R + 127) / 128) * (uint64_t)((K + 127) / 128);
     const Range rx = bytes(x, input_span(rows, cols, ld_x));
-    const Range outs[4] = {bytes(codes, (uint64_t)R * K / 2), bytes(scales, (uint64_t)R * K / 16),
+    const Range outs[4] = {bytes(codes, (uint64_t)Rs * K / 2), bytes(scales, (uint64_t)Rs * K / 16),
                            bytes(tensor_scale, nts * 4), bytes(workspace, use_scratch ? 0 : need)};
     for (int i = 0; i < 4; ++i) {
         if (overlap(rx, outs[i])) return FP4Q_EINVAL;
@@ -331,6 +353,7 @@ fp4q_status run_quantize_nv(const void *x, int64_t rows, int64_t cols, int64_t l
     a.stream_id = stream_id;
     a.hadamard = hadamard;
     a.sign_mask = sign_mask;
+    a.tiled = tiled;
     a.codes = codes;
     a.scales = scales;
     if (use_scratch && need > 0) {

@@ -213,6 +213,47 @@ FP4Q_HD void grid_stride_chunks(uint32_t start, uint32_t stride, uint32_t n, F4 
     for (; c < n; c += stride) visit1((uint32_t)c);
 }
 
+// Division of 32-bit numerators by a divisor d fixed for a launch, as a
+// multiply-high and shifts (Granlund and Montgomery, "Division by Invariant
+// Integers using Multiplication", PLDI 1994): with l = ceil(log2 d) and
+// m = floor(2^32 (2^l - d) / d) + 1, n / d = (t + ((n - t) >> 1)) >> (l - 1)
+// for t = mulhi(m, n) and l >= 1 (d = 1: n itself).  Exact for every
+// 32-bit n.
+struct FastDiv {
+    uint32_t m, l;
+};
+inline FastDiv fast_div_for(uint32_t d)
+{
+    uint32_t l = 0;
+    while ((1ull << l) < d) ++l;
+    const uint32_t m = (uint32_t)((((1ull << l) - d) << 32) / d + 1);
+    return FastDiv{m, l};
+}
+FP4Q_HD uint32_t fast_div(uint32_t n, FastDiv f)
+{
+    if (f.l == 0) return n;
+    const uint32_t t = (uint32_t)(((uint64_t)f.m * n) >> 32);
+    return (t + ((n - t) >> 1)) >> (f.l - 1);
+}
+
+// NVFP4 operand addresses (K % 16 == 0; tiled needs K % 128 == 0).  Linear:
+// codes [R][K/2], scales [R][K/16].  Tiled (the NV GEMM's consumer layout):
+// step-major row blocks, codes [Rp/32][K/128][32][64] and scales
+// [Rp/32][K/128][32][8] (Rp = R rounded up to 32), so that one 128-wide K
+// step of a 32-row group is 2 KiB of codes and 256 bytes of scales, each
+// contiguous.  Byte offset of the 4 code bytes of 8-element chunk c8 of row
+// r, and of the scale byte of 16-element block j of row r:
+FP4Q_HD uint64_t nv_code_off(uint32_t r, uint32_t c8, uint32_t K, bool tiled)
+{
+    if (!tiled) return (uint64_t)r * (K >> 1) + (uint64_t)c8 * 4u;
+    return (((uint64_t)(r >> 5) * (K >> 7) + (c8 >> 4)) * 32u + (r & 31u)) * 64u + (c8 & 15u) * 4u;
+}
+FP4Q_HD uint64_t nv_scale_off(uint32_t r, uint32_t j, uint32_t K, bool tiled)
+{
+    if (!tiled) return (uint64_t)r * (K >> 4) + j;
+    return (((uint64_t)(r >> 5) * (K >> 7) + (j >> 3)) * 32u + (r & 31u)) * 8u + (j & 7u);
+}
+
 // Device-only helpers shared by the producers and the GEMM epilogue that
 // quantizes its output.
 // 2^E as binary32 for E8M0 byte E + 127 (byte 0 -> the subnormal 2^-127).

@@ -14,7 +14,7 @@ struct QuantArgs {
     int axis;        // 0: along rows, 1: along columns (x^T)
     bool sr;
     bool hadamard;
-    bool tiled;      // FP4Q_LAYOUT_TILED outputs (MX only)
+    bool tiled;      // FP4Q_LAYOUT_TILED outputs
     uint64_t seed;
     uint32_t stream_id;
     uint32_t sign_mask;
@@ -32,7 +32,7 @@ struct GemmArgs {
     const void *a_codes, *a_scales, *b_codes, *b_scales;
     const float *a_ts, *b_ts;  // NV tensor scales (null for MX)
     int nv_domain;             // NV only: 0 global, 1 tile128
-    bool tiled;                // MX only: FP4Q_LAYOUT_TILED operands
+    bool tiled;                // FP4Q_LAYOUT_TILED operands
     int64_t M, N, K;
     float alpha;
     void *c;
@@ -46,6 +46,10 @@ struct GemmArgs {
     bool q_tiled;
     bool q_swiglu;
 };
+
+// Compute units of the current device (the persistent GEMMs' grid), looked
+// up once per device; <= 0 if the device cannot be queried.
+int device_cu_count();
 
 int launch_quant_mx(const QuantArgs &a, hipStream_t st);
 // given_amax: optional device pointer to the global domain's amax (skips the

@@ -403,10 +403,8 @@ int launch_gemm_mx(const GemmArgs &g, hipStream_t st)
     auto *bs = reinterpret_cast<const uint8_t *>(g.b_scales);
     // persistent grid: one workgroup per CU (the kernel's 136 KiB of LDS
     // allows no more), never more workgroups than tiles
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
-                                                 hipSuccess || cus <= 0)
-        return 1;
+    const int cus = device_cu_count();
+    if (cus <= 0) return 1;
     const int grid = min(tiles_m * tiles_n, cus);
 #define FP4Q_GEMM_MX(T, Q)                                                                                     \
     hipLaunchKernelGGL((gemm_mx_kernel<T, Q>), dim3(grid), dim3(256), 0, st, a, as, b, bs, M, N, K, g.alpha, g.c, \

@@ -102,7 +102,13 @@ __device__ __forceinline__ half2_t scale2(uint32_t w)
     return __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_pkrtz(f, f));
 }
 
-template <bool kTile>
+// kTiledIn: A and B in the tiled consumer layout (step-major 32-row blocks:
+// a step's 64 code bytes of local row f of group g at ((g * nk + s) * 32 + f)
+// * 64, its 8 scale bytes at ((g * nk + s) * 32 + f) * 8), so that each DMA
+// instruction copies 1 KiB of contiguous codes (16 rows of one step) and
+// each scale DMA 256 contiguous bytes; the chunk swizzle of the LDS image is
+// applied by the lane -> source mapping, as in the linear layout.
+template <bool kTile, bool kTiledIn>
 __global__ __launch_bounds__(256) void gemm_nv_fp16_kernel(
     const uint8_t *__restrict__ A, const uint8_t *__restrict__ As, const float *__restrict__ Ats,
     const uint8_t *__restrict__ B, const uint8_t *__restrict__ Bs, const float *__restrict__ Bts, int M, int N, int K,
@@ -124,6 +130,17 @@ __global__ __launch_bounds__(256) void gemm_nv_fp16_kernel(
     const uint32_t KB = (uint32_t)K >> 1;  // code bytes per row
     const uint32_t KS = (uint32_t)K >> 4;  // scale bytes per row
     const int nk = K >> 7;
+    const uint32_t Mp = ((uint32_t)M + 31) & ~31u, Np = ((uint32_t)N + 31) & ~31u;
+    constexpr uint32_t kCodeStep = kTiledIn ? 2048u : 64u;   // source advance per K step
+    constexpr uint32_t kScaleStep = kTiledIn ? 256u : 8u;
+    // source offset of the 64 code bytes (scale bytes) of stored row `row` in K step 0
+    auto code_row = [&](uint32_t row) -> uint32_t {
+        return kTiledIn ? ((row >> 5) * (uint32_t)nk * 32u + (row & 31u)) * 64u : row * KB;
+    };
+    auto scale_row = [&](uint32_t row) -> uint32_t {
+        return kTiledIn ? ((row >> 5) * (uint32_t)nk * 32u + (row & 31u)) * 8u : row * KS;
+    };
+    const uint32_t Mlast = kTiledIn ? Mp - 1 : (uint32_t)M - 1, Nlast = kTiledIn ? Np - 1 : (uint32_t)N - 1;
     const uint32_t lds_base = (uint32_t)(uintptr_t)lds;
     const int ntiles = tiles_m * tiles_n;
 
@@ -141,23 +158,23 @@ __global__ __launch_bounds__(256) void gemm_nv_fp16_kernel(
         for (int t = 0; t < 4; ++t) {
             const uint32_t r = 64 * wave + 16 * t + (lane >> 2);  // local row
             const uint32_t c = (uint32_t)(lane & 3) ^ ((r >> 1) & 3u);
-            a_goff[t] = (uint32_t)min(m0 + (int)r, M - 1) * KB + c * 16;
+            a_goff[t] = code_row(min((uint32_t)m0 + r, Mlast)) + c * 16;
         }
 #pragma unroll
         for (int t = 0; t < NJ; ++t) {
             const uint32_t r = kBRowsPerWave * wave + 16 * t + (lane >> 2);
             const uint32_t c = (uint32_t)(lane & 3) ^ ((r >> 1) & 3u);
-            b_goff[t] = (uint32_t)min(n0 + (int)r, N - 1) * KB + c * 16;
+            b_goff[t] = code_row(min((uint32_t)n0 + r, Nlast)) + c * 16;
         }
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
             const uint32_t r = 64 * wave + 32 * t + (lane >> 1);
-            as_goff[t] = (uint32_t)min(m0 + (int)r, M - 1) * KS + (lane & 1) * 4;
+            as_goff[t] = scale_row(min((uint32_t)m0 + r, Mlast)) + (lane & 1) * 4;
         }
 #pragma unroll
         for (int t = 0; t < NJ / 2; ++t) {
             const uint32_t r = kBRowsPerWave * wave + 32 * t + (lane >> 1);
-            bs_goff[t] = (uint32_t)min(n0 + (int)r, N - 1) * KS + (lane & 1) * 4;
+            bs_goff[t] = scale_row(min((uint32_t)n0 + r, Nlast)) + (lane & 1) * 4;
         }
         pa = A;
         pb = B;
@@ -179,10 +196,10 @@ __global__ __launch_bounds__(256) void gemm_nv_fp16_kernel(
     };
     auto advance = [&]() {
         const uint32_t more = dstep < nk - 1 ? 1u : 0u;
-        pa += more * 64u;
-        pb += more * 64u;
-        pas += more * 8u;
-        pbs += more * 8u;
+        pa += more * kCodeStep;
+        pb += more * kCodeStep;
+        pas += more * kScaleStep;
+        pbs += more * kScaleStep;
         dstep += (int)more;
     };
     auto prologue = [&]() {
@@ -310,10 +327,10 @@ __global__ __launch_bounds__(256) void gemm_nv_fp16_kernel(
                     }
                     // pointer updates after the step's last DMA
                     if constexpr (s == 6 && t < 4) {
-                        if (t == 0) { pa += more * 64u; asm volatile("" : "+s"(pa)); }
-                        if (t == 1) { pb += more * 64u; asm volatile("" : "+s"(pb)); }
-                        if (t == 2) { pas += more * 8u; asm volatile("" : "+s"(pas)); }
-                        if (t == 3) { pbs += more * 8u; asm volatile("" : "+s"(pbs)); }
+                        if (t == 0) { pa += more * kCodeStep; asm volatile("" : "+s"(pa)); }
+                        if (t == 1) { pb += more * kCodeStep; asm volatile("" : "+s"(pb)); }
+                        if (t == 2) { pas += more * kScaleStep; asm volatile("" : "+s"(pas)); }
+                        if (t == 3) { pbs += more * kScaleStep; asm volatile("" : "+s"(pbs)); }
                     }
                     // dequantize slice sn: fragment t/2 of A (even t) or B (odd t) in slots 0..7,
                     // block scales of a new slice pair first (slots 0..7 too)
@@ -397,17 +414,15 @@ int launch_gemm_nv(const GemmArgs &g, hipStream_t st)
     const int vec_ok = ((uintptr_t)g.c % 16 == 0) && (g.ldc % (16 / esize) == 0) && g.ldc <= (int64_t(1) << 26);
     const bool tile = g.nv_domain == 1;
     const int tiles_m = (M + 255) / 256, tiles_n = tile ? (N + 127) / 128 : (N + 255) / 256;
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-        return 1;
+    const int cus = device_cu_count();
+    if (cus <= 0) return 1;
     const int grid = min(tiles_m * tiles_n, cus);
-    if (tile)
-        hipLaunchKernelGGL(gemm_nv_fp16_kernel<true>, dim3(grid), dim3(256), 0, st, a, as, g.a_ts, b, bs, g.b_ts, M, N,
-                           K, g.alpha, g.c, g.ldc, (int)g.c_bf16, vec_ok, tiles_m, tiles_n, g.c_amax);
-    else
-        hipLaunchKernelGGL(gemm_nv_fp16_kernel<false>, dim3(grid), dim3(256), 0, st, a, as, g.a_ts, b, bs, g.b_ts, M, N,
-                           K, g.alpha, g.c, g.ldc, (int)g.c_bf16, vec_ok, tiles_m, tiles_n, g.c_amax);
+#define FP4Q_GEMM_NV(TILE, TIN)                                                                                 \
+    hipLaunchKernelGGL((gemm_nv_fp16_kernel<TILE, TIN>), dim3(grid), dim3(256), 0, st, a, as, g.a_ts, b, bs, g.b_ts, \
+                       M, N, K, g.alpha, g.c, g.ldc, (int)g.c_bf16, vec_ok, tiles_m, tiles_n, g.c_amax)
+    if (tile) { if (g.tiled) FP4Q_GEMM_NV(true, true); else FP4Q_GEMM_NV(true, false); }
+    else { if (g.tiled) FP4Q_GEMM_NV(false, true); else FP4Q_GEMM_NV(false, false); }
+#undef FP4Q_GEMM_NV
     return hipGetLastError() == hipSuccess ? 0 : 1;
 }
 

@@ -570,7 +570,16 @@ __device__ __forceinline__ uint32_t nv_encode8(const float f[8], float S, uint32
 // maxima while they are in flight; four scale bytes (lanes +0, +2, +4, +6:
 // consecutive chunks) are gathered by DPP row shifts into one 32-bit store
 // when the chunk count is a multiple of 8 and the scales are word-aligned.
-template <bool kSR, bool kFlat>
+// kTiled: the outputs go to the tiled consumer layout (K % 128 == 0) and the
+// chunks are walked in that layout's order: chunk c is 16 chunks (one row's
+// 128-element K step) of row (c >> 4) % 32 of 32-row block / K step c >> 9,
+// so the codes word of chunk c lands at word c and its scale bytes at byte
+// 2 c -- both output streams are written linearly, and a wave reads four
+// 256-byte row pieces.  The grid also covers the padding rows up to a
+// multiple of 32 (nchunks_out chunks), whose codes and scale bytes are
+// written as zeros.  `by` divides by K / 8 (row split of the linear order)
+// or, tiled, by K / 128 (the K steps per 32-row block).
+template <bool kSR, bool kFlat, bool kTiled>
 __global__ __launch_bounds__(kThreads) void nv_quant_global_kernel(const uint16_t *__restrict__ x, uint32_t K,
                                                                    uint32_t ld, uint32_t nchunks,
                                                                    const uint32_t *__restrict__ partial,
@@ -578,23 +587,33 @@ __global__ __launch_bounds__(kThreads) void nv_quant_global_kernel(const uint16_
                                                                    uint8_t *__restrict__ scales,
                                                                    float *__restrict__ tensor_scale,
                                                                    uint32_t seed_lo, uint32_t seed_hi,
-                                                                   uint32_t stream_id)
+                                                                   uint32_t stream_id, uint32_t nchunks_out,
+                                                                   FastDiv by)
 {
     __shared__ uint32_t sh[kThreads / 64];
     const uint32_t cpr = K >> 3;
     const uint32_t base = blockIdx.x * (kThreads * kChunksPerThread) + threadIdx.x;
     uint4 q[kChunksPerThread];
+    uint32_t rows[kChunksPerThread], cols[kChunksPerThread];  // (row, chunk in row) of each chunk
 #pragma unroll
     for (int i = 0; i < kChunksPerThread; ++i) {
         const uint32_t c = base + i * kThreads;
         q[i] = make_uint4(0u, 0u, 0u, 0u);
-        if (c < nchunks) {
-            if (kFlat) {
-                q[i] = load_nt16(x + (size_t)c * 8);
-            } else {
-                const uint32_t r = c / cpr;
-                q[i] = load_nt16(x + (size_t)r * ld + (size_t)(c - r * cpr) * 8);
+        if (kTiled) {
+            const uint32_t blk = c >> 9, rb = fast_div(blk, by);
+            rows[i] = rb * 32u + ((c >> 4) & 31u);
+            cols[i] = (blk - rb * (K >> 7)) * 16u + (c & 15u);
+            if (c < nchunks_out && (uint64_t)rows[i] * cpr < nchunks)
+                q[i] = load_nt16(x + (size_t)rows[i] * ld + (size_t)cols[i] * 8);
+        } else {
+            rows[i] = 0;
+            cols[i] = 0;
+            if (kSR || !kFlat) {
+                rows[i] = fast_div(c, by);
+                cols[i] = c - rows[i] * cpr;
             }
+            if (c < nchunks)
+                q[i] = load_nt16(kFlat ? x + (size_t)c * 8 : x + (size_t)rows[i] * ld + (size_t)cols[i] * 8);
         }
     }
     uint32_t a = 0;
@@ -602,23 +621,29 @@ __global__ __launch_bounds__(kThreads) void nv_quant_global_kernel(const uint16_
     a = block_max_u32(a, sh);
     const float S = nv_tensor_scale(u2f(a));
     if (blockIdx.x == 0 && threadIdx.x == 0) *tensor_scale = S;
-    const bool word_scales = (nchunks & 7u) == 0 && ((uintptr_t)scales & 3u) == 0;
+    const bool word_scales = kTiled || ((nchunks & 7u) == 0 && ((uintptr_t)scales & 3u) == 0);
 #pragma unroll
     for (int i = 0; i < kChunksPerThread; ++i) {
         const uint32_t c = base + i * kThreads;
-        uint32_t r = 0, col = 0;  // only stochastic rounding keys on them
-        if (kSR) {
-            r = c / cpr;
-            col = c - r * cpr;
-        }
+        const uint32_t r = rows[i], col = cols[i];  // stochastic rounding keys on them
         float f[8];
         unpack8(q[i], f);
         uint32_t sb;
-        const uint32_t packed = nv_encode8<kSR>(f, S, &sb, r, col, stream_id, seed_lo, seed_hi);
+        uint32_t packed = nv_encode8<kSR>(f, S, &sb, r, col, stream_id, seed_lo, seed_hi);
+        if (kTiled && (uint64_t)r * cpr >= nchunks) {  // a padding row
+            packed = 0;
+            sb = 0;
+        }
         const uint32_t s2 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)sb, 0x102, 0xF, 0xF, true);
         const uint32_t s4 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)sb, 0x104, 0xF, 0xF, true);
         const uint32_t s6 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)sb, 0x106, 0xF, 0xF, true);
-        if (c < nchunks) {
+        if (kTiled) {
+            if (c < nchunks_out) {  // tiled order: word c, scale bytes 2 c .. (nv_code_off / nv_scale_off)
+                __builtin_nontemporal_store(packed, codes + c);
+                if ((threadIdx.x & 7) == 0)  // chunks col .. col + 7: four blocks of one row and K step
+                    *reinterpret_cast<uint32_t *>(scales + (c >> 1)) = sb | s2 << 8 | s4 << 16 | s6 << 24;
+            }
+        } else if (c < nchunks) {
             __builtin_nontemporal_store(packed, codes + c);
             if (word_scales) {
                 if ((threadIdx.x & 7) == 0)  // c % 8 == 0 and c + 7 < nchunks
@@ -644,14 +669,16 @@ __global__ __launch_bounds__(kThreads) void nv_quant_global_kernel(const uint16_
 // ------------------------------------------------------------------
 constexpr int kTileThreads = 512, kTileRowsPerIter = kTileThreads / 32, kTileIters = 128 / kTileRowsPerIter;
 
-template <bool kSR>
+// kTiled: outputs in the tiled consumer layout (K % 128 == 0), padding rows
+// R .. Rp-1 (inside the last tile row) written as zeros.
+template <bool kSR, bool kTiled>
 __global__ __launch_bounds__(kTileThreads) void nv_quant_tile_kernel(const uint16_t *__restrict__ x, uint32_t R,
                                                                  uint32_t K, uint32_t ld,
                                                                  uint32_t *__restrict__ codes,
                                                                  uint8_t *__restrict__ scales,
                                                                  float *__restrict__ tensor_scale,
                                                                  uint32_t seed_lo, uint32_t seed_hi,
-                                                                 uint32_t stream_id)
+                                                                 uint32_t stream_id, uint32_t Rp)
 {
     __shared__ uint32_t sh[2 * (kTileThreads / 64)];
     const uint32_t TK = (K + 127) >> 7;
@@ -685,19 +712,31 @@ __global__ __launch_bounds__(kTileThreads) void nv_quant_tile_kernel(const uint1
     const float S = nv_tensor_scale(u2f(tm << 16));
     const uint32_t tk = tp * 2 + half;
     if ((t == 0 || t == 16) && tk < TK) tensor_scale[tr * TK + tk] = S;
-    const bool word_scales = (K & 63u) == 0 && ((uintptr_t)scales & 3u) == 0;
+    const bool word_scales = kTiled || ((K & 63u) == 0 && ((uintptr_t)scales & 3u) == 0);
 #pragma unroll
     for (int i = 0; i < kTileIters; ++i) {
         const uint32_t r = tr * 128 + (t >> 5) + kTileRowsPerIter * i;
         float f[8];
         unpack8(q[i], f);
         uint32_t sb;
-        const uint32_t packed = nv_encode8<kSR>(f, S, &sb, r, c8, stream_id, seed_lo, seed_hi);
+        uint32_t packed = nv_encode8<kSR>(f, S, &sb, r, c8, stream_id, seed_lo, seed_hi);
+        if (kTiled && r >= R) {  // a padding row
+            packed = 0;
+            sb = 0;
+        }
         // scale bytes of chunks cc, cc + 2, cc + 4, cc + 6 (one per 16-element block)
         const uint32_t s2 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)sb, 0x102, 0xF, 0xF, true);
         const uint32_t s4 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)sb, 0x104, 0xF, 0xF, true);
         const uint32_t s6 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)sb, 0x106, 0xF, 0xF, true);
-        if (r < R && cvalid) {
+        if (kTiled) {
+            if (r < Rp && cvalid) {
+                __builtin_nontemporal_store(packed, reinterpret_cast<uint32_t *>(reinterpret_cast<uint8_t *>(codes) +
+                                                                                 nv_code_off(r, c8, K, true)));
+                if ((cc & 7) == 0)  // four blocks of one row and K step
+                    *reinterpret_cast<uint32_t *>(scales + nv_scale_off(r, c8 >> 1, K, true)) =
+                        sb | s2 << 8 | s4 << 16 | s6 << 24;
+            }
+        } else if (r < R && cvalid) {
             const size_t c = (size_t)r * cpr + c8;
             __builtin_nontemporal_store(packed, codes + c);
             if (word_scales) {
@@ -725,7 +764,9 @@ __global__ __launch_bounds__(kTileThreads) void nv_quant_tile_kernel(const uint1
 //            partial[blockIdx.x].
 // Requires cols % 4 == 0 and rows % 16 == 0 (rows % 32 == 0 with Hadamard).
 // ------------------------------------------------------------------
-template <bool kSR, bool kHad, int kMode>
+// kTiled: outputs in the tiled consumer layout (rows % 128 == 0), output
+// rows cols .. Rp-1 (padding up to a multiple of 32) written as zeros.
+template <bool kSR, bool kHad, int kMode, bool kTiled = false>
 __global__ __launch_bounds__(kThreads) void nv_quant_cols_kernel(const uint16_t *__restrict__ x, uint32_t rows,
                                                                  uint32_t cols, uint32_t ld,
                                                                  uint8_t *__restrict__ codes,
@@ -733,7 +774,8 @@ __global__ __launch_bounds__(kThreads) void nv_quant_cols_kernel(const uint16_t 
                                                                  float *__restrict__ tensor_scale,
                                                                  uint32_t *__restrict__ partial, uint32_t npartial,
                                                                  uint32_t seed_lo, uint32_t seed_hi,
-                                                                 uint32_t stream_id, uint32_t sign_mask)
+                                                                 uint32_t stream_id, uint32_t sign_mask,
+                                                                 uint32_t Rp = 0)
 {
     __shared__ __attribute__((aligned(16))) uint8_t tile[kColTile * kColPitch];
     __shared__ uint32_t sh[kThreads / 64];
@@ -821,6 +863,14 @@ __global__ __launch_bounds__(kThreads) void nv_quant_cols_kernel(const uint16_t 
             S = nv_tensor_scale(u2f(a));
             if (t == 0) tensor_scale[(c0 / kColTile) * tiles_r + r0 / kColTile] = S;
         }
+        if (kTiled && kvalid != 0 && col >= cols && col < Rp) {
+            // padding output rows of the tiled layout: zero codes and scales
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                *reinterpret_cast<uint4 *>(codes + nv_code_off(col + h, k0 >> 3, rows, true)) = make_uint4(0u, 0u, 0u, 0u);
+                *reinterpret_cast<uint16_t *>(scales + nv_scale_off(col + h, k0 >> 4, rows, true)) = 0;
+            }
+        }
         if (kvalid == 0 || col >= cols) continue;
         const uint32_t K2 = rows >> 1, K16 = rows >> 4;
 #pragma unroll
@@ -848,6 +898,12 @@ __global__ __launch_bounds__(kThreads) void nv_quant_cols_kernel(const uint16_t 
                         out[g] = cvt8_f32(y, 1.0f);
                     }
                 }
+            }
+            if (kTiled) {  // 32 K of one row and K step: 16 contiguous code bytes, 2 scale bytes
+                *reinterpret_cast<uint4 *>(codes + nv_code_off(col + h, k0 >> 3, rows, true)) =
+                    make_uint4(out[0], out[1], out[2], out[3]);
+                *reinterpret_cast<uint16_t *>(scales + nv_scale_off(col + h, k0 >> 4, rows, true)) = (uint16_t)sbs;
+                continue;
             }
             uint8_t *crow = codes + (size_t)(col + h) * K2 + (k0 >> 1);
             uint8_t *srow = scales + (size_t)(col + h) * K16 + (k0 >> 4);
@@ -953,11 +1009,18 @@ int launch_quant_nv(const QuantArgs &a, int domain, float *tensor_scale, void *w
         const uint32_t rows = (uint32_t)a.rows, cols = (uint32_t)a.cols;
         const uint32_t ntile = ((cols + kColTile - 1) / kColTile) * ((rows + kColTile - 1) / kColTile);
         auto *c8 = reinterpret_cast<uint8_t *>(a.codes);
+        const uint32_t Rp = (cols + 31) / 32 * 32;  // output rows of the tiled layout
+#define FP4Q_NVC_T(SR, HAD, MODE, T, G, PART, NP)                                                                   \
+    hipLaunchKernelGGL((nv_quant_cols_kernel<SR, HAD, MODE, T>), dim3(G), dim3(kThreads), 0, st, x, rows, cols,     \
+                       (uint32_t)a.ld, c8, scales, tensor_scale, PART, NP, seed_lo, seed_hi, a.stream_id, a.sign_mask, \
+                       Rp)
+#define FP4Q_NVC(SR, HAD, MODE, G, PART, NP)                                      \
+    do {                                                                          \
+        if (a.tiled) FP4Q_NVC_T(SR, HAD, MODE, true, G, PART, NP);                \
+        else FP4Q_NVC_T(SR, HAD, MODE, false, G, PART, NP);                       \
+    } while (0)
         if (domain == 1) {
             if (ntile == 0) return 0;
-#define FP4Q_NVC(SR, HAD, MODE, G, PART, NP)                                                                       \
-    hipLaunchKernelGGL((nv_quant_cols_kernel<SR, HAD, MODE>), dim3(G), dim3(kThreads), 0, st, x, rows, cols,       \
-                       (uint32_t)a.ld, c8, scales, tensor_scale, PART, NP, seed_lo, seed_hi, a.stream_id, a.sign_mask)
             if (a.sr) { if (a.hadamard) FP4Q_NVC(true, true, 0, ntile, nullptr, 0u); else FP4Q_NVC(true, false, 0, ntile, nullptr, 0u); }
             else { if (a.hadamard) FP4Q_NVC(false, true, 0, ntile, nullptr, 0u); else FP4Q_NVC(false, false, 0, ntile, nullptr, 0u); }
         } else {
@@ -965,13 +1028,14 @@ int launch_quant_nv(const QuantArgs &a, int domain, float *tensor_scale, void *w
             // operand still gets S = 1 from pass 2
             auto *part = reinterpret_cast<uint32_t *>(workspace);
             const uint32_t np = ntile == 0 ? 1u : min(ntile, (uint32_t)kAmaxBlocks);
-            if (a.hadamard) FP4Q_NVC(false, true, 2, np, part, 0u);
-            else FP4Q_NVC(false, false, 2, np, part, 0u);
+            if (a.hadamard) FP4Q_NVC_T(false, true, 2, false, np, part, 0u);
+            else FP4Q_NVC_T(false, false, 2, false, np, part, 0u);
             const uint32_t g = ntile == 0 ? 1u : ntile;
             if (a.sr) { if (a.hadamard) FP4Q_NVC(true, true, 1, g, part, np); else FP4Q_NVC(true, false, 1, g, part, np); }
             else { if (a.hadamard) FP4Q_NVC(false, true, 1, g, part, np); else FP4Q_NVC(false, false, 1, g, part, np); }
-#undef FP4Q_NVC
         }
+#undef FP4Q_NVC
+#undef FP4Q_NVC_T
         return hipGetLastError() == hipSuccess ? 0 : 1;
     }
     if (domain == 0) {
@@ -997,27 +1061,35 @@ int launch_quant_nv(const QuantArgs &a, int domain, float *tensor_scale, void *w
                                    (uint32_t)a.ld, (uint32_t)nchunks, part);
             partial = part;
         }
-        const uint32_t grid = (uint32_t)((nchunks + kThreads * kChunksPerThread - 1) / (kThreads * kChunksPerThread));
+        // the tiled layout's padding rows (up to a multiple of 32) are written too
+        const uint64_t nchunks_out = a.tiled ? (uint64_t)((R + 31) / 32 * 32) * (K >> 3) : nchunks;
+        const uint32_t grid =
+            (uint32_t)((nchunks_out + kThreads * kChunksPerThread - 1) / (kThreads * kChunksPerThread));
         const uint32_t g = grid == 0 ? 1 : grid;
-#define FP4Q_NVG(SR, FLAT)                                                                                    \
-    hipLaunchKernelGGL((nv_quant_global_kernel<SR, FLAT>), dim3(g), dim3(kThreads), 0, st, x, K, (uint32_t)a.ld,      \
-                       (uint32_t)nchunks, partial, np, codes, scales, tensor_scale, seed_lo, seed_hi, a.stream_id)
+#define FP4Q_NVG(SR, FLAT, T)                                                                                  \
+    hipLaunchKernelGGL((nv_quant_global_kernel<SR, FLAT, T>), dim3(g), dim3(kThreads), 0, st, x, K, (uint32_t)a.ld,    \
+                       (uint32_t)nchunks, partial, np, codes, scales, tensor_scale, seed_lo, seed_hi, a.stream_id, \
+                       (uint32_t)nchunks_out, by)
         const bool flat = a.ld == (int64_t)K;
-        if (a.sr) {
-            if (flat) FP4Q_NVG(true, true); else FP4Q_NVG(true, false);
+        const uint32_t div = a.tiled ? K >> 7 : K >> 3;
+        const FastDiv by = fast_div_for(div ? div : 1);
+        if (a.tiled) {  // the tiled walk computes each chunk's row itself: one form for any ld
+            if (a.sr) FP4Q_NVG(true, false, true); else FP4Q_NVG(false, false, true);
         } else {
-            if (flat) FP4Q_NVG(false, true); else FP4Q_NVG(false, false);
+            if (a.sr) { if (flat) FP4Q_NVG(true, true, false); else FP4Q_NVG(true, false, false); }
+            else { if (flat) FP4Q_NVG(false, true, false); else FP4Q_NVG(false, false, false); }
         }
 #undef FP4Q_NVG
     } else {
         if (R == 0 || K == 0) return 0;
         dim3 grid(((K + 127) / 128 + 1) / 2, (R + 127) / 128);  // pairs of tiles
-        if (a.sr)
-            hipLaunchKernelGGL(nv_quant_tile_kernel<true>, grid, dim3(kTileThreads), 0, st, x, R, K, (uint32_t)a.ld,
-                               codes, scales, tensor_scale, seed_lo, seed_hi, a.stream_id);
-        else
-            hipLaunchKernelGGL(nv_quant_tile_kernel<false>, grid, dim3(kTileThreads), 0, st, x, R, K, (uint32_t)a.ld,
-                               codes, scales, tensor_scale, seed_lo, seed_hi, a.stream_id);
+        const uint32_t Rp = (R + 31) / 32 * 32;
+#define FP4Q_NVT(SR, T)                                                                                            \
+    hipLaunchKernelGGL((nv_quant_tile_kernel<SR, T>), grid, dim3(kTileThreads), 0, st, x, R, K, (uint32_t)a.ld, codes, \
+                       scales, tensor_scale, seed_lo, seed_hi, a.stream_id, Rp)
+        if (a.tiled) { if (a.sr) FP4Q_NVT(true, true); else FP4Q_NVT(false, true); }
+        else { if (a.sr) FP4Q_NVT(true, false); else FP4Q_NVT(false, false); }
+#undef FP4Q_NVT
     }
     return hipGetLastError() == hipSuccess ? 0 : 1;
 }

@@ -58,10 +58,10 @@
  *   scales  MX: [R x K/32] E8M0 bytes; NV: [R x K/16] E4M3 bytes, row-major;
  *   tensor_scale  NV global: 1 float; NV tile128: [ceil(R/128) x ceil(K/128)]
  *           floats, row-major, one per 128 x 128 tile of the logical operand.
- * Tiled layout (FP4Q_LAYOUT_TILED; MX operands only; K % 128 == 0): the
- * consumer layout of the MX GEMM ([Fusion], section "The Design Philosophy
- * of Format-Aware Fusion": the producer writes what the consumer loads).
- * With Rp = 32 * ceil(R/32):
+ * Tiled layout (FP4Q_LAYOUT_TILED; K % 128 == 0): the consumer layout of
+ * the GEMMs ([Fusion], section "The Design Philosophy of Format-Aware
+ * Fusion": the producer writes what the consumer loads).  With
+ * Rp = 32 * ceil(R/32), for MX operands:
  *   codes   [Rp/32][K/64][64][16] bytes.  The 16 bytes at (g, kb, l) hold row
  *           32 g + (l mod 32), K elements 64 kb + 32 (l / 32) .. +31, element
  *           2j in the low nibble of byte j: one 1 KiB block is exactly the
@@ -72,6 +72,16 @@
  *           Rows R .. Rp-1 hold 0.
  *   Sizes: codes Rp * K / 2 bytes, scales Rp * K / 32 bytes, both 16-byte
  *   aligned.  Producers write every byte, padding included.
+ * For NV operands (step-major 32-row blocks):
+ *   codes   [Rp/32][K/128][32][64] bytes: the 64 bytes at (g, s, f) are the
+ *           codes of row 32 g + f, K elements 128 s .. 128 s + 127, in the
+ *           order of the linear layout (element 2j of the step in the low
+ *           nibble of byte j); a K step of a 32-row group is 2 KiB.
+ *   scales  [Rp/32][K/128][32][8] bytes: the eight E4M3 bytes of row 32 g + f,
+ *           K blocks 8 s .. 8 s + 7.
+ *   tensor_scale as in the linear layout.  Rows R .. Rp-1 hold zero codes
+ *   and zero scale bytes.  Sizes: codes Rp * K / 2, scales Rp * K / 16
+ *   bytes, both 16-byte aligned.
  *
  * GEMM.  C[M x N] = alpha * A * B^T, A the logical [M x K] operand and B the
  * logical [N x K] operand, both quantized along K; fp32 accumulation; C is
@@ -188,8 +198,8 @@ FP4Q_API size_t fp4q_nv_workspace_bytes(int64_t rows, int64_t cols, int axis, in
  * than a 4-bit value").  Writes codes [R x K/2], E4M3 scales [R x K/16] and
  * tensor_scale.  Both axes: along columns (the transpose a wgrad operand
  * needs) a 128 x 128 tile of x is one tile domain of x^T.  Requires
- * K % 16 == 0, and cols % 4 == 0 along columns.  FP4Q_EUNSUPPORTED: layout
- * FP4Q_LAYOUT_TILED. */
+ * K % 16 == 0 (linear) or K % 128 == 0 (tiled), and cols % 4 == 0 along
+ * columns.  Both layouts, axes and domains, RNE and SR. */
 FP4Q_API fp4q_status fp4_quantize_nv(const void *x, int64_t rows, int64_t cols, int64_t ld_x, int axis, int round,
                             uint64_t seed, uint32_t stream_id, int domain, void *codes, void *scales,
                             float *tensor_scale, void *workspace, size_t workspace_bytes, int layout,
@@ -219,9 +229,9 @@ FP4Q_API fp4q_status fp4_quantize_nv_noalloc(const void *x, int64_t rows, int64_
  * Numerical Techniques" names it for the weight-gradient operands; here on
  * the NVFP4 path): as fp4_quantize_nv on the transformed values, which the
  * domain amax, the block amax and the codes all see.  Along columns only
- * (the wgrad operands, quantized along tokens); requires K % 32 == 0 and
- * cols % 4 == 0.  FP4Q_EUNSUPPORTED: FP4Q_ALONG_ROWS, layout
- * FP4Q_LAYOUT_TILED. */
+ * (the wgrad operands, quantized along tokens); requires K % 32 == 0
+ * (linear) or K % 128 == 0 (tiled) and cols % 4 == 0.  FP4Q_EUNSUPPORTED:
+ * FP4Q_ALONG_ROWS. */
 FP4Q_API fp4q_status fp4_hadamard32_quantize_nv(const void *x, int64_t rows, int64_t cols, int64_t ld_x, int axis,
                                        uint32_t sign_mask, int round, uint64_t seed, uint32_t stream_id, int domain,
                                        void *codes, void *scales, float *tensor_scale, void *workspace,
@@ -242,8 +252,8 @@ FP4Q_API fp4q_status fp4_gemm_mx(const void *a_codes, const void *a_scales, cons
  * partial sums (once in the epilogue for the global domain, per 128-wide K
  * slice for tile128).
  * a_tensor_scale / b_tensor_scale as written by fp4_quantize_nv with the same
- * domain.  Requires K % 128 == 0.  FP4Q_EUNSUPPORTED: layout
- * FP4Q_LAYOUT_TILED. */
+ * domain; A and B both in `layout` (the tiled layout's 2 KiB step blocks
+ * are what the GEMM's LDS DMA copies, whole).  Requires K % 128 == 0. */
 FP4Q_API fp4q_status fp4_gemm_nv(const void *a_codes, const void *a_scales, const float *a_tensor_scale,
                         const void *b_codes, const void *b_scales, const float *b_tensor_scale, int domain,
                         int64_t M, int64_t N, int64_t K, float alpha, int layout, void *c, int c_type,

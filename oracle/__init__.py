@@ -256,6 +256,30 @@ def tile_mx(codes, scales):
     return np.ascontiguousarray(tiled), np.ascontiguousarray(ts)
 
 
+def tile_nv(codes, scales):
+    """The tiled consumer layout of an NV operand (K % 128 == 0), as a pure
+    index map of the linear one (definition in the library header): with
+    Rp = 32 * ceil(R/32) and S = K/128 steps, codes become [Rp/32][S][32][64]
+    (the 64 code bytes of row 32 g + f for K elements 128 s .. 128 s + 127 at
+    (g, s, f)) and scales [Rp/32][S][32][8] (the eight E4M3 bytes of the same
+    row and step).  Padding rows are zero.  Returns (codes [Rp, K/2], scales
+    [Rp, K/16]) as uint8 arrays holding those bytes in order."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    scales = np.asarray(scales, dtype=np.uint8)
+    R, K2 = codes.shape
+    K = 2 * K2
+    assert K % 128 == 0 and scales.shape == (R, K // 16)
+    Rp = (R + 31) // 32 * 32
+    c = np.zeros((Rp, K2), dtype=np.uint8)
+    c[:R] = codes
+    s = np.zeros((Rp, K // 16), dtype=np.uint8)
+    s[:R] = scales
+    # [g, f, step, bytes] -> [g, step, f, bytes]
+    tc = c.reshape(Rp // 32, 32, K // 128, 64).transpose(0, 2, 1, 3).reshape(Rp, K2)
+    tsc = s.reshape(Rp // 32, 32, K // 128, 8).transpose(0, 2, 1, 3).reshape(Rp, K // 16)
+    return np.ascontiguousarray(tc), np.ascontiguousarray(tsc)
+
+
 def dequant_mx(codes, scales):
     codes = np.ascontiguousarray(codes, dtype=np.uint8)
     scales = np.ascontiguousarray(scales, dtype=np.uint8)

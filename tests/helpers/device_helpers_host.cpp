@@ -32,6 +32,12 @@ void h_swiglu_batch(const uint16_t *g, const uint16_t *u, uint16_t *out, size_t 
     for (size_t i = 0; i < n; ++i)
         out[i] = (uint16_t)fp4q::f32_to_bf16_rne(fp4q::silu_f32(fp4q::bf16_lo(g[i])) * fp4q::bf16_lo(u[i]));
 }
+// fast_div against the divisor d for n values
+void h_fast_div(uint32_t d, const uint32_t *n, uint32_t *out, size_t count)
+{
+    const fp4q::FastDiv f = fp4q::fast_div_for(d);
+    for (size_t i = 0; i < count; ++i) out[i] = fp4q::fast_div(n[i], f);
+}
 // chunks visited by one thread of the partial-maximum pass: count, index sum
 // and the largest index (visit4 counts its four chunks)
 void h_grid_stride(uint32_t start, uint32_t stride, uint32_t n, uint64_t *out)

@@ -137,7 +137,10 @@ def test_tiled_layout_status_codes():
     assert q_mx(layout=1, cols=96, ld=96) == B.ESHAPE             # tiled needs K % 128
     assert q_mx(layout=1, cols=128, ld=128, scales=SCALES + 4) == B.EALIGN
     assert q_mx(layout=2) == B.EINVAL
-    assert L.fp4_quantize_nv(X, 64, 64, 64, 0, 0, 0, 0, 0, CODES, SCALES, TS, WS, 4096, 1, None) == B.EUNSUPPORTED
+    # NVFP4 tiled: K % 128 (the 64-column operand has K = 64), 16-byte aligned scales
+    assert L.fp4_quantize_nv(X, 64, 64, 64, 0, 0, 0, 0, 0, CODES, SCALES, TS, WS, 4096, 1, None) == B.ESHAPE
+    assert L.fp4_quantize_nv(X, 32, 128, 128, 0, 0, 0, 0, 0, CODES, SCALES + 4, TS, WS, 4096, 1, None) == B.EALIGN
+    assert L.fp4_quantize_nv_noalloc(X, 64, 64, 64, 0, 0, 0, 0, 0, CODES, SCALES, TS, 1, None) == B.ESHAPE
     assert g_mx(layout=1, K=96) == B.ESHAPE
     assert g_mx(layout=3) == B.EINVAL
 

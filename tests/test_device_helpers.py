@@ -41,6 +41,7 @@ def H(tmp_path_factory):
     L.h_e2m1_sr_batch.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t]
     L.h_silu_batch.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t]
     L.h_swiglu_batch.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_size_t]
+    L.h_fast_div.argtypes = [u32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t]
     L.h_grid_stride.argtypes = [u32, u32, u32, ctypes.POINTER(ctypes.c_uint64)]
     return L
 
@@ -235,3 +236,19 @@ def test_swiglu_kernel_arithmetic_against_oracle_rule(H):
         want, hv = oracle.swiglu_bf16(np.stack([normal_g, u], axis=1), 1, 1, with_f64=True)
         lo, hi = allowed_range(want[:, 0], hv[:, 0], np.full(normal_g.size, float(sf.bf16_to_f32(u[:1])[0])))
         assert np.all(hi - lo <= 1)
+
+
+def test_fast_div_exact(H):
+    # the row split of the tiled NV producers: n / d for divisors of every
+    # size, against integer division, on random and boundary numerators
+    rng = np.random.default_rng(13)
+    divisors = [1, 2, 3, 7, 16, 496, 512, 1792, 1795, 4096, 65536, 0x7FFFFFFF, 0xFFFFFFFF] + \
+        list(rng.integers(1, 2 ** 32, 40, dtype=np.uint64))
+    for d in divisors:
+        d = int(d)
+        n = np.concatenate([rng.integers(0, 2 ** 32, 20000, dtype=np.uint64),
+                            np.array([0, 1, d - 1, d, d + 1, 2 ** 32 - 1, 2 ** 32 - 2, (2 ** 32 - 1) // d * d,
+                                      (2 ** 32 - 1) // d * d - 1], dtype=np.uint64) % 2 ** 32]).astype(np.uint32)
+        out = np.zeros_like(n)
+        H.h_fast_div(d, n.ctypes.data, out.ctypes.data, n.size)
+        assert np.array_equal(out, (n.astype(np.uint64) // d).astype(np.uint32)), d

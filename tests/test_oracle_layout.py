@@ -60,3 +60,33 @@ def test_untile_inverts_tile(R, K):
     c, s, cpad, spad = untile_mx(tc, ts, R, K)
     assert np.array_equal(c, codes) and np.array_equal(s, scales)
     assert not cpad.any() and not spad.any()
+
+
+def brute_tile_nv(codes, scales):
+    # element by element from the definition: code nibble of (r, k) goes to
+    # block (g = r / 32, step s = k / 128), row f = r mod 32, byte (k mod 128) / 2
+    R, K2 = codes.shape
+    K = 2 * K2
+    Rp = (R + 31) // 32 * 32
+    S = K // 128
+    out = np.zeros(Rp * K2, dtype=np.uint8)
+    sout = np.zeros(Rp * K // 16, dtype=np.uint8)
+    for r in range(R):
+        g, f = r // 32, r % 32
+        for k in range(K):
+            nib = (codes[r, k // 2] >> (4 * (k & 1))) & 0xF
+            byte = ((g * S + k // 128) * 32 + f) * 64 + (k % 128) // 2
+            out[byte] |= nib << (4 * (k & 1))
+        for j in range(K // 16):
+            sout[((g * S + j // 8) * 32 + f) * 8 + j % 8] = scales[r, j]
+    return out.reshape(Rp, K2), sout.reshape(Rp, K // 16)
+
+
+@pytest.mark.parametrize("R,K", [(1, 128), (33, 256), (64, 384), (70, 512)])
+def test_tile_nv_against_bruteforce(R, K):
+    rng = np.random.default_rng(R + K)
+    codes = rng.integers(0, 256, (R, K // 2), dtype=np.uint8)
+    scales = rng.integers(0, 256, (R, K // 16), dtype=np.uint8)
+    tc, ts = oracle.tile_nv(codes, scales)
+    bc, bs = brute_tile_nv(codes, scales)
+    assert np.array_equal(tc, bc) and np.array_equal(ts, bs)
