@@ -93,13 +93,19 @@ __device__ __forceinline__ half8_t dequant8(uint32_t w, half2_t s2)
     return (half8_t){p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 
-// E4M3 byte b of word w as two equal fp16 (exact: every E4M3 value is an
-// fp16 normal).
-template <int b>
-__device__ __forceinline__ half2_t scale2(uint32_t w)
+// E4M3 bytes 0, 1 (kHi: 2, 3) of word w as two fp16 (exact: every E4M3 value
+// is an fp16 normal); a fragment's block scale is then one half of the pair,
+// broadcast by bcast<h> into the op_sel of the packed multiply.
+template <bool kHi>
+__device__ __forceinline__ half2_t scale_pair(uint32_t w)
 {
-    const float f = __builtin_amdgcn_cvt_f32_fp8((int)w, b);
-    return __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_pkrtz(f, f));
+    return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, kHi);
+}
+
+template <int h>
+__device__ __forceinline__ half2_t bcast(half2_t p)
+{
+    return __builtin_shufflevector(p, p, h, h);
 }
 
 // kTiledIn: A and B in the tiled consumer layout (step-major 32-row blocks:
@@ -227,7 +233,7 @@ __global__ __launch_bounds__(256) void gemm_nv_fp16_kernel(
     uint4 rawA[4][2], rawB[NJ][2];  // code chunks of the step (q = 0, 1)
     uint32_t swA[4], swB[NJ];       // scale words of the step
     uint32_t nswA[4], nswB[NJ];     // scale words of the next step
-    half2_t sA2[4], sB2[NJ];        // block scales of the current slice pair
+    half2_t sAp[4], sBp[NJ];        // block scales of the current two slice pairs
     half8_t fa[4], fb[NJ];          // fragments of the slice on the matrix cores
     half8_t na[4], nb[NJ];          // fragments of the next slice
 
@@ -256,13 +262,13 @@ __global__ __launch_bounds__(256) void gemm_nv_fp16_kernel(
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            sA2[i] = scale2<0>(swA[i]);
-            fa[i] = dequant8(rawA[i][0].x, sA2[i]);
+            sAp[i] = scale_pair<false>(swA[i]);
+            fa[i] = dequant8(rawA[i][0].x, bcast<0>(sAp[i]));
         }
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
-            sB2[j] = scale2<0>(swB[j]);
-            fb[j] = dequant8(rawB[j][0].x, sB2[j]);
+            sBp[j] = scale_pair<false>(swB[j]);
+            fb[j] = dequant8(rawB[j][0].x, bcast<0>(sBp[j]));
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -336,13 +342,14 @@ __global__ __launch_bounds__(256) void gemm_nv_fp16_kernel(
                     // block scales of a new slice pair first (slots 0..7 too)
                     if constexpr (t < 8 && ((t & 1) == 0 || (t >> 1) < NJ)) {
                         constexpr int f = t >> 1;
-                        constexpr int ss = sn & 7, q = ss >> 2, d = ss & 3, b = ss >> 1;
+                        // block scale byte ss / 2: half (ss / 2) % 2 of the pair of bytes ss / 4
+                        constexpr int ss = sn & 7, q = ss >> 2, d = ss & 3, h = (ss >> 1) & 1;
                         if constexpr ((t & 1) == 0) {
-                            if constexpr ((ss & 1) == 0) sA2[f] = scale2<b>(sn == 8 ? nswA[f] : swA[f]);
-                            na[f] = dequant8(word_of(rawA[f][q], d), sA2[f]);
+                            if constexpr ((ss & 3) == 0) sAp[f] = scale_pair<(ss >= 4)>(sn == 8 ? nswA[f] : swA[f]);
+                            na[f] = dequant8(word_of(rawA[f][q], d), bcast<h>(sAp[f]));
                         } else {
-                            if constexpr ((ss & 1) == 0) sB2[f] = scale2<b>(sn == 8 ? nswB[f] : swB[f]);
-                            nb[f] = dequant8(word_of(rawB[f][q], d), sB2[f]);
+                            if constexpr ((ss & 3) == 0) sBp[f] = scale_pair<(ss >= 4)>(sn == 8 ? nswB[f] : swB[f]);
+                            nb[f] = dequant8(word_of(rawB[f][q], d), bcast<h>(sBp[f]));
                         }
                     }
                     __builtin_amdgcn_sched_barrier(0);
@@ -353,14 +360,15 @@ __global__ __launch_bounds__(256) void gemm_nv_fp16_kernel(
                 for (int f = 0; f < NJ; ++f) fb[f] = nb[f];
             });
             if constexpr (kTile) {
-                // fold this K tile's partial sum with its factor
+                // fold this K tile's partial sum with its factor (one rounding)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
 #pragma unroll
                     for (int j = 0; j < NJ; ++j)
 #pragma unroll
                         for (int r = 0; r < 16; ++r)
-                            tot[kTile ? i : 0][kTile ? j : 0][r] += fold * acc[i][j][r];
+                            tot[kTile ? i : 0][kTile ? j : 0][r] =
+                                __builtin_fmaf(fold, acc[i][j][r], tot[kTile ? i : 0][kTile ? j : 0][r]);
             }
             dstep += (int)more;
 #pragma unroll
