@@ -72,6 +72,20 @@ __device__ __forceinline__ void wait_and_barrier()
     asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kAhead) : "memory");
 }
 
+// wait_and_barrier<kAhead + kExtra> when `extra` (a wave-uniform scalar:
+// kExtra more vector-memory instructions were issued, in order, before the
+// DMA being waited for is younger than them), else wait_and_barrier<kAhead>.
+// Each path meets the workgroup exactly once.
+template <int kAhead, int kExtra>
+__device__ __forceinline__ void wait_and_barrier_if(int extra)
+{
+    static_assert(kAhead + kExtra <= 63, "vmcnt holds at most 63");
+    if (extra)
+        wait_and_barrier<kAhead + kExtra>();
+    else
+        wait_and_barrier<kAhead>();
+}
+
 // f(integral_constant<int, 0>) ... f(integral_constant<int, N-1>)
 template <int N, int I = 0, typename F>
 __device__ __forceinline__ void static_for(F &&f)
@@ -103,6 +117,11 @@ __device__ __forceinline__ void static_for(F &&f)
 // wave (the bits of non-negative floats order like the values).  The maximum
 // is taken over the fp32 values and rounded to bf16 once at the end: round
 // to nearest even is monotonic, so that is the maximum of the rounded values.
+
+// Vector-memory instructions store_wave_block issues for a full bf16 block
+// without amax: one 16-byte store per piece, four pieces per 32 x 64 chunk.
+template <int kNJ>
+constexpr int kEpiStoresBf16Full = 2 * kNJ * 4;
 
 template <int kNJ, bool kScale, bool kBf16>
 __device__ __forceinline__ void store_wave_block(const v16f_t (&acc)[4][kNJ], uint8_t *ep, int el, int row_base,

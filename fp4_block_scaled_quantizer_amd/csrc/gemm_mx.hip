@@ -217,15 +217,23 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(const uint8_t *__restrict_
     v8i_t fa0[4], fb0[4], fa1[4], fb1[4];
     uint32_t sa[4], sb[4], nsa[4], nsb[4];
 
+    // The previous tile's bf16 epilogue issued exactly kEpiStores stores after
+    // this tile's prologue (full block, no amax; wave-uniform): the waits of
+    // this tile's first two K steps then allow that many more outstanding
+    // vector-memory instructions, so the stores drain while the matrix cores
+    // run instead of before the first step (the counter completes in issue
+    // order; from step 2 on the stores are older than the awaited DMA).
+    constexpr int kEpiStores = kEpiStoresBf16Full<4>;
+    int stores_pending = 0;
     int tile = blockIdx.x;
     setup(tile);
     prologue();
     for (;;) {
         // stage 0 of this tile has landed: loads complete in issue order, so
-        // once at most (kStages-2) stages' DMA instructions are outstanding
-        // (the previous tile's output stores share the counter and only
-        // make this wait longer) the oldest stage is in LDS
-        wait_and_barrier<(kStages - 2) * kDmaPerStage>();
+        // once at most (kStages-2) stages' DMA instructions (plus the
+        // previous tile's pending stores) are outstanding the oldest stage is
+        // in LDS
+        wait_and_barrier_if<(kStages - 2) * kDmaPerStage, kEpiStores>(stores_pending);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             fa0[i] = frag(lds, 0, i, 0);
@@ -281,7 +289,7 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(const uint8_t *__restrict_
             // step ks+1's DMA was issued two steps ago; after it only step
             // ks+2's DMA and this step's first kDmaA instructions may
             // still be in flight
-            wait_and_barrier<(kStages - 3) * kDmaPerStage + kDmaA>();
+            wait_and_barrier_if<(kStages - 3) * kDmaPerStage + kDmaA, kEpiStores>(ks < 2 ? stores_pending : 0);
             const uint32_t more = dstep < nk - 1 ? 1u : 0u;
             static_for<16>([&](auto t_tag) {
                 constexpr int t = decltype(t_tag)::value;
@@ -365,6 +373,9 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(const uint8_t *__restrict_
         else
             store_wave_block_any(acc, ep, el, row_base, col_base, M, N, alpha, C, ldc, c_bf16 != 0, vec_ok != 0,
                                  c_amax);
+        // the full-block condition of store_wave_block_any, as a scalar
+        stores_pending = __builtin_amdgcn_readfirstlane(
+            (kOut == 0 && c_bf16 && !c_amax && vec_ok && row_base + 128 <= M && col_base + 128 <= N) ? 1 : 0);
         if (next >= ntiles) break;
         tile = next;
     }
