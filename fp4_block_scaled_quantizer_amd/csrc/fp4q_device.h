@@ -77,34 +77,74 @@ FP4Q_HD float silu_f32(float x)
 }
 
 // E2M1 stochastic rounding ([Fusion] section "Two Key Numerical Techniques":
-// up or down with probability proportional to the distance).  The grid step
-// is g = 0.5 below 2, 1 in [2, 4), 2 in [4, 6); with t = |y| / g, f its
-// fractional part (the distance to the lower neighbour in steps), the value
-// rounds up iff f * 2^16 > r16.  |y| >= 6 saturates.  r16 is uniform on
-// [0, 65535].  Evaluated branch-free and exactly, on the code axis in fixed
-// point (X = code * 2^22 + 2^22 f, codes 0..7 for 0, 0.5, 1, 1.5, 2, 3, 4, 6):
-//  - |y| >= 1: X = bits(|y|) - bits(0.5) (one binade holds two codes);
-//  - |y| < 1: the grid is linear, X = 2^23 |y| (exact); for integer m,
-//    f 2^22 > m iff ceil(f 2^22) > m, so X = ceil(2^23 |y|) serves;
-//  - both at once: X = max(bits(|y|) - bits(0.5) saturated at 0,
-//    ceil(2^23 min(|y|, 1))); below 1 the second term is the larger (equal
-//    or above within [0.5, 1), the first is 0 below 0.5), from 1 on the first;
+// up or down with probability proportional to the distance), eight values at
+// a time: the codes of y[0..7] packed into one word (code j in bits 4j..4j+3),
+// value j drawing r16 = r16_of(w, j).  The grid step is g = 0.5 below 2, 1 in
+// [2, 4), 2 in [4, 6); with t = |y| / g and f its fractional part (the
+// distance to the lower neighbour in steps), a value rounds up iff
+// f * 2^16 > r16; |y| >= 6 saturates.  r16 is uniform on [0, 65535].
+// Evaluated branch-free and exactly, on the code axis in fixed point
+// (X = code * 2^22 + 2^22 f, codes 0..7 for 0, 0.5, 1, 1.5, 2, 3, 4, 6):
+//  - a = min(|y|, 6) first (Inf and NaN give 6): saturation happens before
+//    the rounding, and every X below stays at most 7 * 2^22;
+//  - a >= 1: X = bits(a) - bits(0.5) (one binade holds two codes);
+//  - a < 1: the grid is linear, X = 2^23 a (exact); for integer m,
+//    f 2^22 > m iff ceil(f 2^22) > m, so X = ceil(2^23 a) serves.  It is
+//    read off the bits of 0.5 a + 0.5 rounded toward +infinity (on [0.5, 1]
+//    binary32 steps are 2^-24, so those bits are bits(0.5) + ceil(2^23 a));
+//  - both at once: X + bits(0.5) = max(that, bits(a), bits(0.5)): below 1
+//    the first term is the larger, from 1 on the second (0.5 a + 0.5 <= a);
 // then adding 2^22 - 1 - 64 r16 carries into the code iff 2^22 f > 64 r16
 // (64 r16 < 2^22 - 1, so a ceiling that reaches the next code still rounds
-// up).  Saturation is min(code, 7): the code is at least 7 for every
-// |y| >= 6 (Inf and NaN included, no 32-bit wrap) and at most 7 below.  The
-// selects stay selects: no divergent branch per element.
-FP4Q_HD uint32_t e2m1_sr(float y, uint32_t r16)
+// up).  The sign bit is kept for values that round to zero.  On the GPU the
+// eight rounded-up FMAs run in one inline-assembly block that switches the
+// wave's binary32 rounding mode (MODE bits 1:0) to +infinity and back, so no
+// other floating-point instruction can be scheduled inside it; on the host
+// the rounding up is done exactly through binary64.
+FP4Q_HD uint32_t e2m1_sr8(const float y[8], const uint32_t w[4])
 {
-    const uint32_t b = f2u(y);
-    const uint32_t u = b & 0x7FFFFFFFu;
-    const uint32_t s = (b >> 28) & 8u;
-    const uint32_t ul = u < 0x3F800000u ? u : 0x3F800000u;  // |y| clamped to 1: in range of the conversion
-    const uint32_t xl = (uint32_t)__builtin_ceilf(u2f(ul) * 8388608.0f);
-    const uint32_t xh = u > 0x3F000000u ? u - 0x3F000000u : 0u;
-    const uint32_t X = xh > xl ? xh : xl;
-    const uint32_t c = (X + 0x3FFFFFu - (r16 << 6)) >> 22;
-    return s | (c < 7u ? c : 7u);
+    float a[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) a[j] = __builtin_fminf(__builtin_fabsf(y[j]), 6.0f);
+    uint32_t h[8];
+#if defined(__HIP_DEVICE_COMPILE__)
+    float r[8];
+    asm volatile(
+        "s_setreg_imm32_b32 hwreg(HW_REG_MODE, 0, 2), 1\n\t"
+        "s_nop 1\n\t"
+        "v_fma_f32 %0, %8, 0.5, 0.5\n\t"
+        "v_fma_f32 %1, %9, 0.5, 0.5\n\t"
+        "v_fma_f32 %2, %10, 0.5, 0.5\n\t"
+        "v_fma_f32 %3, %11, 0.5, 0.5\n\t"
+        "v_fma_f32 %4, %12, 0.5, 0.5\n\t"
+        "v_fma_f32 %5, %13, 0.5, 0.5\n\t"
+        "v_fma_f32 %6, %14, 0.5, 0.5\n\t"
+        "v_fma_f32 %7, %15, 0.5, 0.5\n\t"
+        "s_setreg_imm32_b32 hwreg(HW_REG_MODE, 0, 2), 0\n\t"
+        "s_nop 1"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]));
+#pragma unroll
+    for (int j = 0; j < 8; ++j) h[j] = f2u(r[j]);
+#else
+    for (int j = 0; j < 8; ++j) {
+        // the smallest binary32 f >= 0.5 a + 0.5, i.e. with 2 f - 1 >= a
+        // (exact in binary64: f lies in [0.5, 3.5])
+        float f = (float)(0.5 * (double)a[j] + 0.5);
+        while (2.0 * (double)f - 1.0 < (double)a[j]) f = u2f(f2u(f) + 1u);
+        h[j] = f2u(f);
+    }
+#endif
+    uint32_t out = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const uint32_t m = h[j] > f2u(a[j]) ? h[j] : f2u(a[j]);
+        const uint32_t x = m > 0x3F000000u ? m : 0x3F000000u;  // X + bits(0.5)
+        const uint32_t r16 = (j & 1) ? (w[j >> 1] >> 16) : (w[j >> 1] & 0xFFFFu);
+        const uint32_t t = x - ((r16 << 6) + 0x3EC00001u);  // X + 2^22 - 1 - 64 r16
+        out |= ((t >> 22) | ((f2u(y[j]) >> 28) & 8u)) << (4 * j);
+    }
+    return out;
 }
 
 // OCP MX shared exponent byte (E8M0) of a block whose amax has binary32 bits

@@ -90,12 +90,16 @@ __device__ __forceinline__ uint32_t cvt8_bf16(const uint4 &q, float scale)
 }
 
 
-// Largest |bf16| bit pattern (15 bits) among the 8 values of a chunk.
+// Largest |bf16| bit pattern (15 bits) among the 8 values of a chunk: the
+// sign bits cleared in each word, then packed 16-bit maxima (v_pk_max_u16,
+// two values per instruction) and one max of the two halves.
 __device__ __forceinline__ uint32_t amax8_bf16(const uint4 &q)
 {
-    uint32_t m = max(max(q.x & 0x7FFFu, (q.x >> 16) & 0x7FFFu), max(q.y & 0x7FFFu, (q.y >> 16) & 0x7FFFu));
-    m = max(m, max(max(q.z & 0x7FFFu, (q.z >> 16) & 0x7FFFu), max(q.w & 0x7FFFu, (q.w >> 16) & 0x7FFFu)));
-    return m;
+    typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+    const u16x2_t a = __builtin_bit_cast(u16x2_t, q.x & 0x7FFF7FFFu), b = __builtin_bit_cast(u16x2_t, q.y & 0x7FFF7FFFu);
+    const u16x2_t c = __builtin_bit_cast(u16x2_t, q.z & 0x7FFF7FFFu), d = __builtin_bit_cast(u16x2_t, q.w & 0x7FFF7FFFu);
+    const u16x2_t m = __builtin_elementwise_max(__builtin_elementwise_max(a, b), __builtin_elementwise_max(c, d));
+    return max((uint32_t)m.x, (uint32_t)m.y);
 }
 
 // The 8 bf16 of a chunk as binary32.
@@ -194,8 +198,10 @@ __global__ __launch_bounds__(kThreads) void quant_mx_rows_kernel(const uint16_t 
                 const uint32_t c8 = c - r * cpr;
                 uint32_t w[4];
                 philox4x32_10(c8, r, stream_id, 0u, seed_lo, seed_hi, w);
+                float y[8];
 #pragma unroll
-                for (int j = 0; j < 8; ++j) packed |= e2m1_sr(f[j] * inv, r16_of(w, j)) << (4 * j);
+                for (int j = 0; j < 8; ++j) y[j] = f[j] * inv;
+                packed |= e2m1_sr8(y, w);
             } else {
                 packed = cvt8_f32(f, mx_scale_f32(sbyte));
             }
@@ -235,10 +241,10 @@ __device__ __forceinline__ uint32_t encode_row_chunk(const uint4 &q, uint32_t ro
     const float inv = mx_inv_scale(sbyte);
     uint32_t w[4];
     philox4x32_10(chunk, row, stream_id, 0u, seed_lo, seed_hi, w);
-    uint32_t packed = 0;
+    float y[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) packed |= e2m1_sr(f[j] * inv, r16_of(w, j)) << (4 * j);
-    return packed;
+    for (int j = 0; j < 8; ++j) y[j] = f[j] * inv;
+    return e2m1_sr8(y, w);
 }
 
 // ------------------------------------------------------------------
@@ -363,10 +369,10 @@ __global__ __launch_bounds__(kThreads) void quant_mx_cols_kernel(const uint16_t 
                 for (int g = 0; g < 4; ++g) {
                     uint32_t w[4];
                     philox4x32_10(4 * j + g, col + h, stream_id, 0u, seed_lo, seed_hi, w);
-                    uint32_t packed = 0;
+                    float y[8];
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) packed |= e2m1_sr(v[h][8 * g + e] * inv, r16_of(w, e)) << (4 * e);
-                    out[g] = packed;
+                    for (int e = 0; e < 8; ++e) y[e] = v[h][8 * g + e] * inv;
+                    out[g] = e2m1_sr8(y, w);
                 }
             } else {
                 const float scale = mx_scale_f32(sbyte);
@@ -467,8 +473,10 @@ __global__ __launch_bounds__(kThreads) void quant_mx_rows_tiled_kernel(
                 const float inv = mx_inv_scale(sbyte);
                 uint32_t w[4];
                 philox4x32_10((k0 >> 3) + c8, row, stream_id, 0u, seed_lo, seed_hi, w);
+                float y[8];
 #pragma unroll
-                for (int j = 0; j < 8; ++j) packed |= e2m1_sr(f[j] * inv, r16_of(w, j)) << (4 * j);
+                for (int j = 0; j < 8; ++j) y[j] = f[j] * inv;
+                packed |= e2m1_sr8(y, w);
             } else {
                 packed = cvt8_f32(f, mx_scale_f32(sbyte));
             }
@@ -556,8 +564,7 @@ __device__ __forceinline__ uint32_t nv_encode8(const float f[8], float S, uint32
     if (kSR) {
         uint32_t w[4];
         philox4x32_10(c8, r, stream_id, 0u, seed_lo, seed_hi, w);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) packed |= e2m1_sr(y[j], r16_of(w, j)) << (4 * j);
+        packed = e2m1_sr8(y, w);
     } else {
         packed = cvt8_f32(y, 1.0f);  // scale 2^0: plain RNE of y, saturating
     }
@@ -890,10 +897,7 @@ __global__ __launch_bounds__(kThreads) void nv_quant_cols_kernel(const uint16_t 
                     if (kSR) {
                         uint32_t w[4];
                         philox4x32_10((k0 >> 3) + g, col + h, stream_id, 0u, seed_lo, seed_hi, w);
-                        uint32_t packed = 0;
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) packed |= e2m1_sr(y[e], r16_of(w, e)) << (4 * e);
-                        out[g] = packed;
+                        out[g] = e2m1_sr8(y, w);
                     } else {
                         out[g] = cvt8_f32(y, 1.0f);
                     }

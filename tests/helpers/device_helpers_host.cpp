@@ -4,7 +4,17 @@
 #include "fp4q_device.h"
 
 extern "C" {
-uint32_t h_e2m1_sr(float y, uint32_t r16) { return fp4q::e2m1_sr(y, r16); }
+// one value through slot `slot` (0..7) of the eight-value SR encode, the
+// other slots holding zeros
+uint32_t h_e2m1_sr_slot(float y, uint32_t r16, int slot)
+{
+    float v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    uint32_t w[4] = {0, 0, 0, 0};
+    v[slot] = y;
+    w[slot >> 1] = (slot & 1) ? r16 << 16 : r16;
+    return (fp4q::e2m1_sr8(v, w) >> (4 * slot)) & 15u;
+}
+uint32_t h_e2m1_sr(float y, uint32_t r16) { return h_e2m1_sr_slot(y, r16, 0); }
 uint32_t h_e4m3_rne_satfinite(float z) { return fp4q::e4m3_rne_satfinite(z); }
 float h_e4m3_value(uint32_t c) { return fp4q::e4m3_value(c); }
 uint32_t h_nv_block_scale(float b, float S) { return fp4q::nv_block_scale(b, S); }
@@ -60,6 +70,16 @@ void h_grid_stride(uint32_t start, uint32_t stride, uint32_t n, uint64_t *out)
 }
 void h_e2m1_sr_batch(const float *y, const uint32_t *r, uint8_t *out, size_t n)
 {
-    for (size_t i = 0; i < n; ++i) out[i] = (uint8_t)fp4q::e2m1_sr(y[i], r[i]);
+    // consecutive values share one eight-value encode: value i sits in slot i % 8
+    for (size_t i = 0; i < n; i += 8) {
+        float v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        uint32_t w[4] = {0, 0, 0, 0};
+        for (size_t j = 0; j < 8 && i + j < n; ++j) {
+            v[j] = y[i + j];
+            w[j >> 1] |= (j & 1) ? r[i + j] << 16 : r[i + j];
+        }
+        const uint32_t p = fp4q::e2m1_sr8(v, w);
+        for (size_t j = 0; j < 8 && i + j < n; ++j) out[i + j] = (uint8_t)((p >> (4 * j)) & 15u);
+    }
 }
 }

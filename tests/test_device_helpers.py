@@ -252,3 +252,10 @@ def test_fast_div_exact(H):
         out = np.zeros_like(n)
         H.h_fast_div(d, n.ctypes.data, out.ctypes.data, n.size)
         assert np.array_equal(out, (n.astype(np.uint64) // d).astype(np.uint32)), d
+    # every numerator below 2^24 (the tiled walk divides chunk index / 512 by
+    # the K steps per row)
+    n = np.arange(2 ** 24, dtype=np.uint32)
+    out = np.zeros_like(n)
+    for d in [3, 7, 32, 112, 127, 4097]:
+        H.h_fast_div(d, n.ctypes.data, out.ctypes.data, n.size)
+        assert np.array_equal(out, n // np.uint32(d)), d

@@ -162,6 +162,45 @@ def test_outputs_written_exactly_guard_bytes():
     assert np.all(np_u8(cbuf[nbytes_c:]) == 0xA5) and np.all(np_u8(sbuf[nbytes_s:]) == 0xA5)
 
 
+def tiny_and_wide_blocks(rows, cols, seed):
+    """bf16 [rows x cols]: every 32-element block holds one value of magnitude
+    2^e (e in -100, 0, 60, 126; random sign) and 31 random bf16 patterns no
+    larger than it, so that after the block scale y spans zero, subnormal and
+    tiny binary32, full mantissas and exact grid points."""
+    rng = np.random.default_rng(seed)
+    nb = rows * cols // 32
+    e = rng.choice(np.array([-100, 0, 60, 126]), nb)
+    top = ((e + 127) << 7).astype(np.uint16)
+    body = rng.integers(0, 0x8000, (nb, 31)).astype(np.uint32)
+    body = np.minimum(body, top[:, None].astype(np.uint32)).astype(np.uint16)
+    blk = np.concatenate([top[:, None], body], axis=1)
+    blk |= (rng.integers(0, 2, blk.shape) << 15).astype(np.uint16)
+    rot = rng.integers(0, 32, nb)  # the large value anywhere in the block
+    idx = (np.arange(32)[None, :] + rot[:, None]) % 32
+    blk = np.take_along_axis(blk, idx, axis=1)
+    return blk.reshape(rows, cols)
+
+
+@pytest.mark.parametrize("axis", ["rows", "cols"])
+def test_sr_tiny_and_wide_blocks(axis):
+    # stochastic rounding where r16 = 0 meets tiny nonzero y (it must round
+    # up) and y from zero to the saturation range: byte for byte
+    dev = device()
+    announce(f"SR tiny and wide blocks along {axis}")
+    xb = tiny_and_wide_blocks(2048, 4096, 5)
+    x = synth.from_bf16_bits(xb).to(dev)
+    if axis == "rows":
+        codes, scales = B.fp4_quantize_mx(x, round=B.SR, seed=11, stream_id=4)
+        oc, os_ = oracle.quantize_mx(xb, sr=True, seed=11, stream=4)
+    else:
+        xt = x.t().contiguous()
+        codes, scales = B.fp4_quantize_mx(xt, axis=B.ALONG_COLS, round=B.SR, seed=11, stream_id=4)
+        oc, os_ = oracle.quantize_mx(xb, sr=True, seed=11, stream=4)
+    torch.cuda.synchronize()
+    assert_bytes_equal(np_u8(scales), os_, "scales")
+    assert_bytes_equal(np_u8(codes), oc, "codes")
+
+
 def test_repeat_is_deterministic():
     dev = device()
     announce("determinism")
