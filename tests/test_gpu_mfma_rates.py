@@ -1,0 +1,52 @@
+"""Would an NVFP4 GEMM on gfx950's 8-bit matrix cores beat the fp16 path?
+
+An E2M1 value times its E4M3 block scale has up to 6 significant bits
+(tests/test_nv_fp8_split.py); E4M3 holds 4, so an exact product on fp8
+matrix cores takes each operand in two E4M3 parts: four fp8 products for
+every fp16 one.  libfp4q's NV GEMM runs v_mfma_f32_32x32x16_f16 on the
+exact fp16 dequantization instead.  This measures, on the GPU, the cycles
+per instruction of the fp16, bf16, fp8 and fp4 32x32 instructions (8
+independent accumulators per wave, one wave per SIMD on every CU, cycles by
+s_memtime) and checks the cost of one 128-wide K step of a 32x32 output
+block both ways: fp16 = 8 instructions of K 16; two-part fp8 = 4 x 2
+instructions of K 64."""
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+from tests.gpu_common import announce, device
+from tests.helpers import build as helpers
+
+pytestmark = pytest.mark.gpu
+
+KINDS = {"fp16": (0, 16), "bf16": (1, 16), "fp8": (2, 64), "fp4": (3, 64)}  # kind id, K per instruction
+
+
+def cycles_per_instruction(kind, blocks=256, iters=2000):
+    lib = ctypes.CDLL(helpers.path("libmfma_rates.so"))
+    lib.mfma_rate_launch.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                     ctypes.c_void_p]
+    dev = device()
+    cyc = torch.zeros(blocks * 4, dtype=torch.int64, device=dev)
+    sink = torch.zeros(blocks * 256, dtype=torch.float32, device=dev)
+    st = torch.cuda.current_stream(dev).cuda_stream
+    for _ in range(2):  # the second launch is the one read
+        assert lib.mfma_rate_launch(kind, blocks, iters, cyc.data_ptr(), sink.data_ptr(), st) == 0
+    torch.cuda.synchronize()
+    return float(cyc.cpu().numpy().astype(np.float64).mean()) / (iters * 8)
+
+
+def test_fp8_split_does_not_beat_fp16():
+    announce("matrix-core instruction rates")
+    c = {name: cycles_per_instruction(kid) for name, (kid, _) in KINDS.items()}
+    for name, (_, k) in KINDS.items():
+        print(f"{name}: {c[name]:.1f} cycles per 32x32x{k} instruction, {k / c[name]:.3f} K per cycle")
+    step_fp16 = (128 // 16) * c["fp16"]
+    step_fp8_split = 4 * (128 // 64) * c["fp8"]
+    step_fp8_one_side = 2 * (128 // 64) * c["fp8"]
+    print(f"one 128-wide K step of a 32x32 block: fp16 {step_fp16:.0f} cycles, two-part fp8 "
+          f"{step_fp8_split:.0f} ({step_fp8_split / step_fp16:.2f}x), one operand split {step_fp8_one_side:.0f}")
+    assert step_fp8_split >= step_fp16, "fp8 matrix cores would win: revisit the NVFP4 GEMM"
+    assert c["fp4"] <= c["fp8"]
