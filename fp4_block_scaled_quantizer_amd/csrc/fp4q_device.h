@@ -165,21 +165,19 @@ FP4Q_HD float e4m3_value(uint32_t c)
     return u2f(((e + 120u) << 23) | (m << 20));
 }
 
-// E4M3 round-to-nearest-even with saturation to 448 (0x7E), z >= 0 finite.
+// E4M3 round-to-nearest-even with saturation to 448 (0x7E), z >= 0.
 // Below 2^-6 the E4M3 step is 2^-9, so the code is rint(z * 512) (this also
 // yields 0x08 when z rounds up to 2^-6); above, the 23-bit mantissa is
-// rounded to 3 bits at bit 20 with the carry flowing into the exponent.
+// rounded to 3 bits at bit 20 with the carry flowing into the exponent, and
+// every z >= 448 (Inf and NaN included) comes out at least 0x7E, so one min
+// saturates.  Both forms are computed and one is selected (no branch).
 FP4Q_HD uint32_t e4m3_rne_satfinite(float z)
 {
-    if (z >= 448.0f) return 0x7Eu;
     const uint32_t b = f2u(z);
-    if (b < 0x3C800000u) {  // z < 2^-6
-        return (uint32_t)rintf(z * 512.0f);
-    }
+    const uint32_t sub = (uint32_t)rintf(fminf(z * 512.0f, 8.0f));  // z < 2^-6 (the min keeps the cast defined)
     const uint32_t r = b + 0x7FFFFu + ((b >> 20) & 1u);
-    const uint32_t eb = (r >> 23) - 120u;  // E4M3 biased exponent (fp32 bias 127, E4M3 bias 7)
-    const uint32_t code = (eb << 3) | ((r >> 20) & 7u);
-    return code < 0x7Eu ? code : 0x7Eu;
+    const uint32_t code = (((r >> 23) - 120u) << 3) | ((r >> 20) & 7u);  // E4M3 bias 7, binary32 bias 127
+    return b < 0x3C800000u ? sub : (code < 0x7Eu ? code : 0x7Eu);
 }
 
 // NVFP4 block scale byte and its reciprocal decode scale for block amax b in
@@ -194,6 +192,55 @@ FP4Q_HD uint32_t nv_block_scale(float b, float S)
     return sb == 0u ? 1u : sb;
 }
 FP4Q_HD float nv_inv_decode(uint32_t sb, float S) { return 1.0f / (e4m3_value(sb) * S); }
+
+// a / d rounded to nearest from y = RN(1/d) by one correction step
+// (P. Markstein, "Computation of elementary functions on the IBM RISC
+// System/6000 processor", IBM J. Res. Dev. 34(1), 1990): q0 = RN(a y) lies
+// within one ulp of a / d, r = a - d q0 is exact (one FMA), and
+// RN(q0 + r y) = RN(a / d), provided nothing overflows and neither q0 nor r
+// leaves the normal range.
+FP4Q_HD float div_by_recip(float a, float d, float y)
+{
+    const float q0 = a * y;
+    const float r = __builtin_fmaf(-q0, d, a);
+    return __builtin_fmaf(r, y, q0);
+}
+
+// A scale domain's constants for nv_block_scale_fast: S, RN(1/S), and
+// whether the correction-step form is exact for every block of the domain.
+// With 2^-92 <= S <= 2^116 (S = A / 2688 for a finite amax A of at least
+// about 2^-80.6) both quotients b / 6 and (b / 6) / S, and their remainders,
+// stay normal wherever the E4M3 code depends on them: a block scale below
+// 2^-10 gives code 1 in either case (0 is clamped to 1), and that needs
+// b / 6 >= 2^-102.  Outside the range (tiny, Inf or NaN S) the plain
+// divisions run.
+struct NvDomain {
+    float S, rS;
+    bool fast;
+};
+FP4Q_HD NvDomain nv_domain(float S)
+{
+    NvDomain t;
+    t.S = S;
+    t.rS = 1.0f / S;
+    t.fast = S >= 0x1p-92f && S <= 0x1p116f;
+    return t;
+}
+
+// nv_block_scale(b, S) with the two divisions done by correction steps
+// from RN(1/6) and RN(1/S): the same value of (b / 6) / S, bit for bit,
+// in a domain whose `fast` holds (checked on the host against the
+// divisions for every bf16 block amax b <= A and every bf16 domain amax A).
+FP4Q_HD uint32_t nv_block_scale_fast(float b, const NvDomain &t)
+{
+    float sbf;
+    if (t.fast)
+        sbf = div_by_recip(div_by_recip(b, 6.0f, 0x1.555556p-3f), t.S, t.rS);
+    else
+        sbf = (b / 6.0f) / t.S;
+    const uint32_t sb = e4m3_rne_satfinite(sbf);
+    return sb == 0u ? 1u : sb;
+}
 
 // FP32 tensor-level scale of a domain with amax A (A = 0 gives 1): the
 // domain's largest block then maps onto E4M3 448 x E2M1 6 = 2688.

@@ -546,18 +546,21 @@ __global__ __launch_bounds__(kThreads) void nv_amax_partial_kernel(const uint16_
     if (threadIdx.x == 0) partial[blockIdx.x] = m << 16;  // binary32 bits of the partial amax
 }
 
+// One lane's 8 bf16 values (q) of a 16-element NV block shared with lane ^ 1:
+// block amax (packed 16-bit maxima, then across the lane pair), E4M3 block
+// scale by correction steps (nv_block_scale_fast), its decode reciprocal
+// 1 / (e4m3(sb) S) from the workgroup's table inv_tab (filled with the
+// correctly rounded divisions), y = x * inv and the E2M1 codes.
 template <bool kSR>
-__device__ __forceinline__ uint32_t nv_encode8(const float f[8], float S, uint32_t *sb_out, uint32_t r,
-                                               uint32_t c8, uint32_t stream_id, uint32_t seed_lo,
-                                               uint32_t seed_hi)
+__device__ __forceinline__ uint32_t nv_encode8(const uint4 &q, const NvDomain &dom, const float *inv_tab,
+                                               uint32_t *sb_out, uint32_t r, uint32_t c8, uint32_t stream_id,
+                                               uint32_t seed_lo, uint32_t seed_hi)
 {
-    uint32_t bmax = 0;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) bmax = max(bmax, f2u(f[j]) & 0x7FFFFFFFu);
-    bmax = xor_max<1>(bmax);  // the two lanes of a 16-element block
-    const uint32_t sb = nv_block_scale(u2f(bmax), S);
-    const float inv = nv_inv_decode(sb, S);
-    float y[8];
+    const uint32_t bmax = xor_max<1>(amax8_bf16(q) << 16);  // binary32 bits of the block amax
+    const uint32_t sb = nv_block_scale_fast(u2f(bmax), dom);
+    const float inv = inv_tab[sb];
+    float f[8], y[8];
+    unpack8(q, f);
 #pragma unroll
     for (int j = 0; j < 8; ++j) y[j] = f[j] * inv;
     uint32_t packed = 0;
@@ -570,6 +573,13 @@ __device__ __forceinline__ uint32_t nv_encode8(const float f[8], float S, uint32
     }
     *sb_out = sb;
     return packed;
+}
+
+// The decode reciprocals 1 / (e4m3(k) S) of a scale domain, k = 1 .. 126,
+// correctly rounded (entry 0 is unused: block scales are at least 1).
+__device__ __forceinline__ void nv_fill_inv_table(float *inv_tab, float S, int i)
+{
+    if (i >= 1 && i < 127) inv_tab[i] = nv_inv_decode((uint32_t)i, S);
 }
 
 // kFlat: contiguous rows (ld == K), chunk c starts at element 8 c.  The
@@ -623,20 +633,22 @@ __global__ __launch_bounds__(kThreads) void nv_quant_global_kernel(const uint16_
                 q[i] = load_nt16(kFlat ? x + (size_t)c * 8 : x + (size_t)rows[i] * ld + (size_t)cols[i] * 8);
         }
     }
+    __shared__ float inv_tab[128];
     uint32_t a = 0;
     for (uint32_t i = threadIdx.x; i < npartial; i += kThreads) a = max(a, partial[i]);
     a = block_max_u32(a, sh);
     const float S = nv_tensor_scale(u2f(a));
     if (blockIdx.x == 0 && threadIdx.x == 0) *tensor_scale = S;
+    const NvDomain dom = nv_domain(S);
+    nv_fill_inv_table(inv_tab, S, threadIdx.x);
+    __syncthreads();
     const bool word_scales = kTiled || ((nchunks & 7u) == 0 && ((uintptr_t)scales & 3u) == 0);
 #pragma unroll
     for (int i = 0; i < kChunksPerThread; ++i) {
         const uint32_t c = base + i * kThreads;
         const uint32_t r = rows[i], col = cols[i];  // stochastic rounding keys on them
-        float f[8];
-        unpack8(q[i], f);
         uint32_t sb;
-        uint32_t packed = nv_encode8<kSR>(f, S, &sb, r, col, stream_id, seed_lo, seed_hi);
+        uint32_t packed = nv_encode8<kSR>(q[i], dom, inv_tab, &sb, r, col, stream_id, seed_lo, seed_hi);
         if (kTiled && (uint64_t)r * cpr >= nchunks) {  // a padding row
             packed = 0;
             sb = 0;
@@ -719,14 +731,23 @@ __global__ __launch_bounds__(kTileThreads) void nv_quant_tile_kernel(const uint1
     const float S = nv_tensor_scale(u2f(tm << 16));
     const uint32_t tk = tp * 2 + half;
     if ((t == 0 || t == 16) && tk < TK) tensor_scale[tr * TK + tk] = S;
+    // decode tables of the two tiles: threads 0..127 fill tile 0's, 128..255 tile 1's
+    __shared__ float inv_tab[2][128];
+    if (t < 256) {
+        const uint32_t h = (uint32_t)t >> 7;
+        uint32_t th = sh[h];
+#pragma unroll
+        for (int w = 1; w < kTileThreads / 64; ++w) th = max(th, sh[2 * w + h]);
+        nv_fill_inv_table(inv_tab[h], nv_tensor_scale(u2f(th << 16)), t & 127);
+    }
+    __syncthreads();
+    const NvDomain dom = nv_domain(S);
     const bool word_scales = kTiled || ((K & 63u) == 0 && ((uintptr_t)scales & 3u) == 0);
 #pragma unroll
     for (int i = 0; i < kTileIters; ++i) {
         const uint32_t r = tr * 128 + (t >> 5) + kTileRowsPerIter * i;
-        float f[8];
-        unpack8(q[i], f);
         uint32_t sb;
-        uint32_t packed = nv_encode8<kSR>(f, S, &sb, r, c8, stream_id, seed_lo, seed_hi);
+        uint32_t packed = nv_encode8<kSR>(q[i], dom, inv_tab[half], &sb, r, c8, stream_id, seed_lo, seed_hi);
         if (kTiled && r >= R) {  // a padding row
             packed = 0;
             sb = 0;
@@ -879,13 +900,14 @@ __global__ __launch_bounds__(kThreads) void nv_quant_cols_kernel(const uint16_t 
             }
         }
         if (kvalid == 0 || col >= cols) continue;
+        const NvDomain dom = nv_domain(S);
         const uint32_t K2 = rows >> 1, K16 = rows >> 4;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             uint32_t out[4], sbs = 0;
 #pragma unroll
             for (int b = 0; b < 2; ++b) {
-                const uint32_t sb = nv_block_scale(u2f(bmax[h][b]), S);
+                const uint32_t sb = nv_block_scale_fast(u2f(bmax[h][b]), dom);
                 const float inv = nv_inv_decode(sb, S);
                 sbs |= sb << (8 * b);
 #pragma unroll

@@ -82,4 +82,34 @@ void h_e2m1_sr_batch(const float *y, const uint32_t *r, uint8_t *out, size_t n)
         for (size_t j = 0; j < 8 && i + j < n; ++j) out[i + j] = (uint8_t)((p >> (4 * j)) & 15u);
     }
 }
+
+// NV block scales for every bf16 domain amax A (step `astep` through the
+// positive finite patterns) and every bf16 block amax b <= A: counts the
+// pairs where the correction-step form differs from the two divisions in
+// the code byte, and (where the block scale is at least 2^-10) in the
+// binary32 block scale itself; also checks the decode table entries.
+void h_nv_fast_sweep(uint32_t astep, uint64_t *out)
+{
+    uint64_t pairs = 0, code_diff = 0, value_diff = 0, fast_domains = 0;
+    for (uint32_t a = 1; a < 0x7F80u; a += astep) {
+        const float A = fp4q::u2f(a << 16);
+        const float S = fp4q::nv_tensor_scale(A);
+        const fp4q::NvDomain t = fp4q::nv_domain(S);
+        fast_domains += t.fast ? 1 : 0;
+        for (uint32_t b = 0; b <= a; ++b) {
+            const float B = fp4q::u2f(b << 16);
+            ++pairs;
+            if (fp4q::nv_block_scale_fast(B, t) != fp4q::nv_block_scale(B, S)) ++code_diff;
+            if (t.fast) {
+                const float exact = (B / 6.0f) / S;
+                const float fast = fp4q::div_by_recip(fp4q::div_by_recip(B, 6.0f, 0x1.555556p-3f), t.S, t.rS);
+                if (exact >= 0x1p-10f && fp4q::f2u(exact) != fp4q::f2u(fast)) ++value_diff;
+            }
+        }
+    }
+    out[0] = pairs;
+    out[1] = code_diff;
+    out[2] = value_diff;
+    out[3] = fast_domains;
+}
 }
