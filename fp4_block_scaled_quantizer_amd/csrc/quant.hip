@@ -34,6 +34,10 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kChunksPerThread = 4;  // 16-byte chunks per lane per launch slot
+// The global-domain NVFP4 quantize pass: chunks per lane.  Each workgroup
+// first folds every partial maximum and fills its decode table, so it is
+// given more input to amortize that over.
+constexpr int kNvgChunks = 8;
 
 // Cross-lane exchange inside a quad of lanes (DPP quad_perm): mask 1 swaps
 // lanes 0<->1 and 2<->3, mask 2 swaps 0<->2 and 1<->3.
@@ -187,8 +191,12 @@ __global__ __launch_bounds__(kThreads) void quant_mx_rows_kernel(const uint16_t 
             unpack8(q[i], f);
             if (kHad) hadamard32_quad(f, (sign_mask >> (8 * quad_lane)) & 0xFFu, quad_lane);
             uint32_t amax = 0;
+            if (kHad) {
 #pragma unroll
-            for (int j = 0; j < 8; ++j) amax = max(amax, f2u(f[j]) & 0x7FFFFFFFu);
+                for (int j = 0; j < 8; ++j) amax = max(amax, f2u(f[j]) & 0x7FFFFFFFu);
+            } else {
+                amax = amax8_bf16(q[i]) << 16;  // the values are still the bf16 inputs
+            }
             amax = xor_max<1>(amax);
             amax = xor_max<2>(amax);
             sbyte = mx_scale_byte(amax);
@@ -464,8 +472,12 @@ __global__ __launch_bounds__(kThreads) void quant_mx_rows_tiled_kernel(
             unpack8(q[i], f);
             if (kHad) hadamard32_quad(f, (sign_mask >> (8 * quad_lane)) & 0xFFu, quad_lane);
             uint32_t amax = 0;
+            if (kHad) {
 #pragma unroll
-            for (int j = 0; j < 8; ++j) amax = max(amax, f2u(f[j]) & 0x7FFFFFFFu);
+                for (int j = 0; j < 8; ++j) amax = max(amax, f2u(f[j]) & 0x7FFFFFFFu);
+            } else {
+                amax = amax8_bf16(q[i]) << 16;  // the values are still the bf16 inputs
+            }
             amax = xor_max<1>(amax);
             amax = xor_max<2>(amax);
             sbyte = mx_scale_byte(amax);
@@ -609,11 +621,11 @@ __global__ __launch_bounds__(kThreads) void nv_quant_global_kernel(const uint16_
 {
     __shared__ uint32_t sh[kThreads / 64];
     const uint32_t cpr = K >> 3;
-    const uint32_t base = blockIdx.x * (kThreads * kChunksPerThread) + threadIdx.x;
-    uint4 q[kChunksPerThread];
-    uint32_t rows[kChunksPerThread], cols[kChunksPerThread];  // (row, chunk in row) of each chunk
+    const uint32_t base = blockIdx.x * (kThreads * kNvgChunks) + threadIdx.x;
+    uint4 q[kNvgChunks];
+    uint32_t rows[kNvgChunks], cols[kNvgChunks];  // (row, chunk in row) of each chunk
 #pragma unroll
-    for (int i = 0; i < kChunksPerThread; ++i) {
+    for (int i = 0; i < kNvgChunks; ++i) {
         const uint32_t c = base + i * kThreads;
         q[i] = make_uint4(0u, 0u, 0u, 0u);
         if (kTiled) {
@@ -644,7 +656,7 @@ __global__ __launch_bounds__(kThreads) void nv_quant_global_kernel(const uint16_
     __syncthreads();
     const bool word_scales = kTiled || ((nchunks & 7u) == 0 && ((uintptr_t)scales & 3u) == 0);
 #pragma unroll
-    for (int i = 0; i < kChunksPerThread; ++i) {
+    for (int i = 0; i < kNvgChunks; ++i) {
         const uint32_t c = base + i * kThreads;
         const uint32_t r = rows[i], col = cols[i];  // stochastic rounding keys on them
         uint32_t sb;
@@ -1090,7 +1102,7 @@ int launch_quant_nv(const QuantArgs &a, int domain, float *tensor_scale, void *w
         // the tiled layout's padding rows (up to a multiple of 32) are written too
         const uint64_t nchunks_out = a.tiled ? (uint64_t)((R + 31) / 32 * 32) * (K >> 3) : nchunks;
         const uint32_t grid =
-            (uint32_t)((nchunks_out + kThreads * kChunksPerThread - 1) / (kThreads * kChunksPerThread));
+            (uint32_t)((nchunks_out + kThreads * kNvgChunks - 1) / (kThreads * kNvgChunks));
         const uint32_t g = grid == 0 ? 1 : grid;
 #define FP4Q_NVG(SR, FLAT, T)                                                                                  \
     hipLaunchKernelGGL((nv_quant_global_kernel<SR, FLAT, T>), dim3(g), dim3(kThreads), 0, st, x, K, (uint32_t)a.ld,    \
