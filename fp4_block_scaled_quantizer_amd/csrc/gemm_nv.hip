@@ -93,6 +93,19 @@ __device__ __forceinline__ half8_t dequant8(uint32_t w, half2_t s2)
     return (half8_t){p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 
+// Half of dequant8: elements 4 p .. 4 p + 3 of the fragment (codes of nibble
+// pairs 2 p and 2 p + 1 of w), written into their two registers of out.
+template <int p>
+__device__ __forceinline__ void dequant4(half8_t &out, uint32_t w, half2_t s2)
+{
+    const half2_t lo = __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2 * p)) * s2;
+    const half2_t hi = __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2 * p + 1)) * s2;
+    out[4 * p] = lo[0];
+    out[4 * p + 1] = lo[1];
+    out[4 * p + 2] = hi[0];
+    out[4 * p + 3] = hi[1];
+}
+
 // E4M3 bytes 0, 1 (kHi: 2, 3) of word w as two fp16 (exact: every E4M3 value
 // is an fp16 normal); a fragment's block scale is then one half of the pair,
 // broadcast by bcast<h> into the op_sel of the packed multiply.
@@ -338,9 +351,24 @@ __global__ __launch_bounds__(256) void gemm_nv_fp16_kernel(
                         if (t == 2) { pas += more * kScaleStep; asm volatile("" : "+s"(pas)); }
                         if (t == 3) { pbs += more * kScaleStep; asm volatile("" : "+s"(pbs)); }
                     }
-                    // dequantize slice sn: fragment t/2 of A (even t) or B (odd t) in slots 0..7,
-                    // block scales of a new slice pair first (slots 0..7 too)
-                    if constexpr (t < 8 && ((t & 1) == 0 || (t >> 1) < NJ)) {
+                    // dequantize slice sn.  Global domain (16 slots): fragment F = t / 2 (A F / 2 for
+                    // even F, B F / 2 for odd F), half t % 2 of it per slot, so that every slot's
+                    // VALU work (4 instructions) fits under its MFMA; block scales of a new slice
+                    // pair before a fragment's first half.  Per-tile domain (8 slots, VALU-bound
+                    // either way): fragment t / 2 of A (even t) or B (odd t) in slots 0..7.
+                    if constexpr (!kTile) {
+                        constexpr int F = t >> 1, part = t & 1, f = F >> 1;
+                        constexpr int ss = sn & 7, q = ss >> 2, d = ss & 3, h = (ss >> 1) & 1;
+                        if constexpr ((F & 1) == 0) {
+                            if constexpr (part == 0 && (ss & 3) == 0)
+                                sAp[f] = scale_pair<(ss >= 4)>(sn == 8 ? nswA[f] : swA[f]);
+                            dequant4<part>(na[f], word_of(rawA[f][q], d), bcast<h>(sAp[f]));
+                        } else {
+                            if constexpr (part == 0 && (ss & 3) == 0)
+                                sBp[f] = scale_pair<(ss >= 4)>(sn == 8 ? nswB[f] : swB[f]);
+                            dequant4<part>(nb[f], word_of(rawB[f][q], d), bcast<h>(sBp[f]));
+                        }
+                    } else if constexpr (t < 8 && ((t & 1) == 0 || (t >> 1) < NJ)) {
                         constexpr int f = t >> 1;
                         // block scale byte ss / 2: half (ss / 2) % 2 of the pair of bytes ss / 4
                         constexpr int ss = sn & 7, q = ss >> 2, d = ss & 3, h = (ss >> 1) & 1;
