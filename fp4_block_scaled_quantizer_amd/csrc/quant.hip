@@ -608,6 +608,9 @@ __device__ __forceinline__ void nv_fill_inv_table(float *inv_tab, float S, int i
 // multiple of 32 (nchunks_out chunks), whose codes and scale bytes are
 // written as zeros.  `by` divides by K / 8 (row split of the linear order)
 // or, tiled, by K / 128 (the K steps per 32-row block).
+// a readable 16-byte chunk for loads that an empty operand cannot serve
+__device__ __align__(16) uint32_t kZeroChunk[4] = {0u, 0u, 0u, 0u};  // never written
+
 template <bool kSR, bool kFlat, bool kTiled>
 __global__ __launch_bounds__(kThreads) void nv_quant_global_kernel(const uint16_t *__restrict__ x, uint32_t K,
                                                                    uint32_t ld, uint32_t nchunks,
@@ -622,18 +625,34 @@ __global__ __launch_bounds__(kThreads) void nv_quant_global_kernel(const uint16_
     __shared__ uint32_t sh[kThreads / 64];
     const uint32_t cpr = K >> 3;
     const uint32_t base = blockIdx.x * (kThreads * kNvgChunks) + threadIdx.x;
+    // The partial maxima are loaded before the data: loads complete in issue
+    // order, so the domain amax, the barriers and the decode table proceed
+    // while the data is in flight, and chunk i's encode waits for its own load.
+    static_assert(kAmaxBlocks % kThreads == 0, "partial maxima per lane");
+    // (Unconditional loads from a clamped index, npartial >= 1: a repeated
+    // element does not change a maximum, and a guarded load would be waited
+    // for inside its branch.)
+    uint32_t pm[kAmaxBlocks / kThreads];
+#pragma unroll
+    for (int j = 0; j < kAmaxBlocks / kThreads; ++j) pm[j] = partial[min(threadIdx.x + j * kThreads, npartial - 1)];
+    asm volatile("" ::: "memory");  // keep the data loads after these
+    const uint16_t *fallback = nchunks != 0 ? x : reinterpret_cast<const uint16_t *>(kZeroChunk);
     uint4 q[kNvgChunks];
     uint32_t rows[kNvgChunks], cols[kNvgChunks];  // (row, chunk in row) of each chunk
 #pragma unroll
     for (int i = 0; i < kNvgChunks; ++i) {
         const uint32_t c = base + i * kThreads;
-        q[i] = make_uint4(0u, 0u, 0u, 0u);
+        // every load is issued (an invalid chunk reads the operand's first
+        // chunk, or a zero chunk when the operand is empty, and is zeroed
+        // below), so the loads' completion count is exact
+        bool valid;
+        const uint16_t *src;
         if (kTiled) {
             const uint32_t blk = c >> 9, rb = fast_div(blk, by);
             rows[i] = rb * 32u + ((c >> 4) & 31u);
             cols[i] = (blk - rb * (K >> 7)) * 16u + (c & 15u);
-            if (c < nchunks_out && (uint64_t)rows[i] * cpr < nchunks)
-                q[i] = load_nt16(x + (size_t)rows[i] * ld + (size_t)cols[i] * 8);
+            valid = c < nchunks_out && (uint64_t)rows[i] * cpr < nchunks;
+            src = x + (size_t)rows[i] * ld + (size_t)cols[i] * 8;
         } else {
             rows[i] = 0;
             cols[i] = 0;
@@ -641,13 +660,17 @@ __global__ __launch_bounds__(kThreads) void nv_quant_global_kernel(const uint16_
                 rows[i] = fast_div(c, by);
                 cols[i] = c - rows[i] * cpr;
             }
-            if (c < nchunks)
-                q[i] = load_nt16(kFlat ? x + (size_t)c * 8 : x + (size_t)rows[i] * ld + (size_t)cols[i] * 8);
+            valid = c < nchunks;
+            src = kFlat ? x + (size_t)c * 8 : x + (size_t)rows[i] * ld + (size_t)cols[i] * 8;
         }
+        const uint4 v = load_nt16(valid ? src : fallback);
+        const uint32_t keep = valid ? ~0u : 0u;
+        q[i] = make_uint4(v.x & keep, v.y & keep, v.z & keep, v.w & keep);
     }
     __shared__ float inv_tab[128];
     uint32_t a = 0;
-    for (uint32_t i = threadIdx.x; i < npartial; i += kThreads) a = max(a, partial[i]);
+#pragma unroll
+    for (int j = 0; j < kAmaxBlocks / kThreads; ++j) a = max(a, pm[j]);
     a = block_max_u32(a, sh);
     const float S = nv_tensor_scale(u2f(a));
     if (blockIdx.x == 0 && threadIdx.x == 0) *tensor_scale = S;
