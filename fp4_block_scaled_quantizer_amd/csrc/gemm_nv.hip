@@ -292,8 +292,9 @@ __global__ __launch_bounds__(256) void gemm_nv_fp16_kernel(
                 else
                     acc[i][j] = (v16f_t){};
             }
-        // per-tile domain: the 128-row tiles of A and B this wave's block lies in
-        const int mt = (m0 >> 7) + wm, nt = n0 >> 7;
+        // per-tile domain: the 128-row tiles of A and B this wave's block lies
+        // in (a block wholly past row M, never stored, reads the last tile row)
+        const int mt = min((m0 >> 7) + wm, (M - 1) >> 7), nt = n0 >> 7;
 
         uint32_t off_cur = 0, off_nxt = gStageBytes, off_n2 = 2 * gStageBytes, off_dma = 3 * gStageBytes;
         for (int ks = 0; ks < nk; ++ks) {
