@@ -710,9 +710,9 @@ __global__ __launch_bounds__(kThreads) void nv_quant_global_kernel(const uint16_
 }
 
 // ------------------------------------------------------------------
-// NVFP4, per-128x128-tile domain ("CTA-local"): a 512-thread workgroup owns
-// two horizontally adjacent tiles (128 rows x 256 K), takes each tile's
-// amax, writes its S, then quantizes from registers.  No grid-wide
+// NVFP4, per-128x128-tile domain ("CTA-local"): a 512-thread workgroup
+// owns two horizontally adjacent tiles (128 rows x 256 K): each tile's
+// amax, its S, then the codes from registers.  No grid-wide
 // dependency.  Thread t handles chunk t mod 32 (tile (t mod 32) / 16) of
 // rows t / 32 + 16 i (i < 8), so a row's 32 codes words are one full
 // 128-byte line and the two tiles' maxima reduce over lane bits 0-3 and 5
@@ -723,34 +723,27 @@ __global__ __launch_bounds__(kThreads) void nv_quant_global_kernel(const uint16_
 // ------------------------------------------------------------------
 constexpr int kTileThreads = 512, kTileRowsPerIter = kTileThreads / 32, kTileIters = 128 / kTileRowsPerIter;
 
+// The quantization of tile pair (tr, tp) from this thread's 8 chunks q[i]
+// (zero outside the operand).  sh: 2 * 8 words, inv_tab: two 128-entry
+// tables, both in LDS; the function meets the workgroup twice.
 // kTiled: outputs in the tiled consumer layout (K % 128 == 0), padding rows
 // R .. Rp-1 (inside the last tile row) written as zeros.
 template <bool kSR, bool kTiled>
-__global__ __launch_bounds__(kTileThreads) void nv_quant_tile_kernel(const uint16_t *__restrict__ x, uint32_t R,
-                                                                 uint32_t K, uint32_t ld,
-                                                                 uint32_t *__restrict__ codes,
-                                                                 uint8_t *__restrict__ scales,
-                                                                 float *__restrict__ tensor_scale,
-                                                                 uint32_t seed_lo, uint32_t seed_hi,
-                                                                 uint32_t stream_id, uint32_t Rp)
+__device__ __forceinline__ void nv_tile_pair_encode(const uint4 (&q)[kTileIters], uint32_t tr, uint32_t tp, uint32_t R,
+                                                    uint32_t K, uint32_t *__restrict__ codes,
+                                                    uint8_t *__restrict__ scales, float *__restrict__ tensor_scale,
+                                                    uint32_t seed_lo, uint32_t seed_hi, uint32_t stream_id,
+                                                    uint32_t Rp, uint32_t *sh, float (*inv_tab)[128])
 {
-    __shared__ uint32_t sh[2 * (kTileThreads / 64)];
     const uint32_t TK = (K + 127) >> 7;
-    const uint32_t tr = blockIdx.y, tp = blockIdx.x;  // tile row, tile pair
     const uint32_t cpr = K >> 3;
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-    const uint32_t cc = t & 31, half = cc >> 4;        // chunk within the pair, its tile
+    const uint32_t cc = t & 31, half = cc >> 4;  // chunk within the pair, its tile
     const uint32_t c8 = tp * 32 + cc;
     const bool cvalid = c8 < cpr;
-    uint4 q[kTileIters];
     uint32_t m = 0;
 #pragma unroll
-    for (int i = 0; i < kTileIters; ++i) {
-        const uint32_t r = tr * 128 + (t >> 5) + kTileRowsPerIter * i;
-        q[i] = make_uint4(0u, 0u, 0u, 0u);
-        if (r < R && cvalid) q[i] = load_nt16(x + (size_t)r * ld + (size_t)c8 * 8);
-        m = max(m, amax8_bf16(q[i]));
-    }
+    for (int i = 0; i < kTileIters; ++i) m = max(m, amax8_bf16(q[i]));
     // per tile: lanes with the same bit 4 (and any bits 0-3, 5) share it
     m = max(m, (uint32_t)__shfl_xor((int)m, 1, 64));
     m = max(m, (uint32_t)__shfl_xor((int)m, 2, 64));
@@ -767,7 +760,6 @@ __global__ __launch_bounds__(kTileThreads) void nv_quant_tile_kernel(const uint1
     const uint32_t tk = tp * 2 + half;
     if ((t == 0 || t == 16) && tk < TK) tensor_scale[tr * TK + tk] = S;
     // decode tables of the two tiles: threads 0..127 fill tile 0's, 128..255 tile 1's
-    __shared__ float inv_tab[2][128];
     if (t < 256) {
         const uint32_t h = (uint32_t)t >> 7;
         uint32_t th = sh[h];
@@ -810,6 +802,41 @@ __global__ __launch_bounds__(kTileThreads) void nv_quant_tile_kernel(const uint1
             }
         }
     }
+}
+
+// One tile pair per workgroup (grid: pairs x tile rows), the chunks loaded
+// into registers.  Unconditional loads from clamped in-bounds addresses (row
+// R - 1, the row's first chunk), zeroed afterwards: a load under a branch
+// lets the compiler wait for it inside the branch.
+template <bool kSR, bool kTiled>
+__global__ __launch_bounds__(kTileThreads) void nv_quant_tile_kernel(const uint16_t *__restrict__ x, uint32_t R,
+                                                                 uint32_t K, uint32_t ld,
+                                                                 uint32_t *__restrict__ codes,
+                                                                 uint8_t *__restrict__ scales,
+                                                                 float *__restrict__ tensor_scale,
+                                                                 uint32_t seed_lo, uint32_t seed_hi,
+                                                                 uint32_t stream_id, uint32_t Rp)
+{
+    __shared__ uint32_t sh[2 * (kTileThreads / 64)];
+    __shared__ float inv_tab[2][128];
+    const uint32_t tr = blockIdx.y, tp = blockIdx.x;  // tile row, tile pair
+    const int t = threadIdx.x;
+    const uint32_t c8 = tp * 32 + (t & 31);
+    const bool cvalid = c8 < (K >> 3);
+    uint4 q[kTileIters];
+#pragma unroll
+    for (int i = 0; i < kTileIters; ++i) {
+        const uint32_t r = tr * 128 + (t >> 5) + kTileRowsPerIter * i;
+        q[i] = load_nt16(x + (size_t)min(r, R - 1) * ld + (size_t)(cvalid ? c8 : 0u) * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < kTileIters; ++i) {
+        const uint32_t r = tr * 128 + (t >> 5) + kTileRowsPerIter * i;
+        const uint32_t keep = r < R && cvalid ? ~0u : 0u;
+        q[i] = make_uint4(q[i].x & keep, q[i].y & keep, q[i].z & keep, q[i].w & keep);
+    }
+    nv_tile_pair_encode<kSR, kTiled>(q, tr, tp, R, K, codes, scales, tensor_scale, seed_lo, seed_hi, stream_id, Rp,
+                                     sh, inv_tab);
 }
 
 // ------------------------------------------------------------------
