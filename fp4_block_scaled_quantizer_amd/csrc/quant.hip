@@ -271,6 +271,47 @@ __device__ __forceinline__ uint32_t encode_row_chunk(const uint4 &q, uint32_t ro
 constexpr int kColTile = 128;            // rows and columns of a workgroup tile
 constexpr int kColPitch = kColTile * 2;  // bytes per staged row
 
+// Thread t's share of the 128 x 128 tile at (r0, c0) of x (rows >= 1,
+// cols % 4 == 0): 8 passes of 16 rows, thread = (row t / 16, 16-byte chunk
+// t mod 16); zeros outside the operand.  With cols % 8 == 0 a chunk is full
+// or empty, and the eight loads are issued unconditionally from clamped
+// in-bounds addresses (row rows - 1, the row's first chunk) and masked
+// afterwards: a load under a branch is waited for inside the branch, which
+// serialized them.  Otherwise a row's last chunk may be half full and the
+// guarded loads are kept.
+__device__ __forceinline__ void load_col_tile(const uint16_t *__restrict__ x, uint32_t rows, uint32_t cols,
+                                              uint32_t ld, uint32_t r0, uint32_t c0, uint4 (&q)[8])
+{
+    const int t = threadIdx.x;
+    const uint32_t rr = t >> 4, c = c0 + (t & 15) * 8;
+    if ((cols & 7u) == 0) {
+        const bool cv = c < cols;
+#pragma unroll
+        for (int p = 0; p < 8; ++p)
+            q[p] = load_nt16(x + (size_t)min(r0 + p * 16 + rr, rows - 1) * ld + (cv ? c : 0u));
+#pragma unroll
+        for (int p = 0; p < 8; ++p) {
+            const uint32_t keep = r0 + p * 16 + rr < rows && cv ? ~0u : 0u;
+            q[p] = make_uint4(q[p].x & keep, q[p].y & keep, q[p].z & keep, q[p].w & keep);
+        }
+    } else {
+#pragma unroll
+        for (int p = 0; p < 8; ++p) {
+            const uint32_t r = r0 + p * 16 + rr;
+            q[p] = make_uint4(0u, 0u, 0u, 0u);
+            if (r < rows) {
+                const uint16_t *src = x + (size_t)r * ld + c;
+                if (c + 8 <= cols) {
+                    q[p] = load_nt16(src);
+                } else if (c + 4 <= cols) {  // cols % 4 == 0: a chunk is full, half or empty
+                    const uint2 h = load_nt8(src);
+                    q[p] = make_uint4(h.x, h.y, 0u, 0u);
+                }
+            }
+        }
+    }
+}
+
 // Dual output (kRowsOut = 1: RNE, 2: SR): while the tile is in registers
 // the kernel also writes x along rows ([rows x cols], no Hadamard) to
 // codes_r / scales_r, bit-identical to the row producers, so one read of x
@@ -297,20 +338,7 @@ __global__ __launch_bounds__(kThreads) void quant_mx_cols_kernel(const uint16_t 
         // 8 passes of 16 rows; thread = (row t / 16, 16-byte chunk t mod 16)
         const uint32_t ch = t & 15, rr = t >> 4, c = c0 + ch * 8;
         uint4 q[8];
-#pragma unroll
-        for (int p = 0; p < 8; ++p) {
-            const uint32_t r = r0 + p * 16 + rr;
-            q[p] = make_uint4(0u, 0u, 0u, 0u);
-            if (r < rows) {
-                const uint16_t *src = x + (size_t)r * ld + c;
-                if (c + 8 <= cols) {
-                    q[p] = load_nt16(src);
-                } else if (c + 4 <= cols) {  // cols % 4 == 0: a chunk is full, half or empty
-                    const uint2 h = load_nt8(src);
-                    q[p] = make_uint4(h.x, h.y, 0u, 0u);
-                }
-            }
-        }
+        load_col_tile(x, rows, cols, ld, r0, c0, q);
 #pragma unroll
         for (int p = 0; p < 8; ++p) *reinterpret_cast<uint4 *>(tile + (p * 16 + rr) * kColPitch + ch * 16) = q[p];
         if constexpr (kRowsOut != 0) {
@@ -877,22 +905,9 @@ __global__ __launch_bounds__(kThreads) void nv_quant_cols_kernel(const uint16_t 
         const uint32_t c0 = (tt % tiles_c) * kColTile, r0 = (tt / tiles_c) * kColTile;
         if (kMode == 2 && tt != blockIdx.x) __syncthreads();  // the previous tile's LDS reads are done
         {
-            const uint32_t ch = t & 15, rr = t >> 4, c = c0 + ch * 8;
+            const uint32_t ch = t & 15, rr = t >> 4;
             uint4 q[8];
-#pragma unroll
-            for (int p = 0; p < 8; ++p) {
-                const uint32_t r = r0 + p * 16 + rr;
-                q[p] = make_uint4(0u, 0u, 0u, 0u);
-                if (r < rows) {
-                    const uint16_t *src = x + (size_t)r * ld + c;
-                    if (c + 8 <= cols) {
-                        q[p] = load_nt16(src);
-                    } else if (c + 4 <= cols) {
-                        const uint2 h = load_nt8(src);
-                        q[p] = make_uint4(h.x, h.y, 0u, 0u);
-                    }
-                }
-            }
+            load_col_tile(x, rows, cols, ld, r0, c0, q);
 #pragma unroll
             for (int p = 0; p < 8; ++p) *reinterpret_cast<uint4 *>(tile + (p * 16 + rr) * kColPitch + ch * 16) = q[p];
         }
