@@ -141,7 +141,21 @@ FP4Q_HD uint32_t e2m1_sr8(const float y[8], const uint32_t w[4])
         const uint32_t m = h[j] > f2u(a[j]) ? h[j] : f2u(a[j]);
         const uint32_t x = m > 0x3F000000u ? m : 0x3F000000u;  // X + bits(0.5)
         const uint32_t r16 = (j & 1) ? (w[j >> 1] >> 16) : (w[j >> 1] & 0xFFFFu);
-        const uint32_t t = x - ((r16 << 6) + 0x3EC00001u);  // X + 2^22 - 1 - 64 r16
+        // t = X + 2^22 - 1 - 64 r16 = x - 64 r16 - 0x3EC00001 (mod 2^32): on the
+        // GPU -64 r16 is one 24-bit multiply that reads its half of the random
+        // word directly, and the sum one three-operand add
+#if defined(__HIP_DEVICE_COMPILE__)
+        uint32_t n64;  // -64 times half (j & 1) of w[j >> 1], zero-extended
+        if (j & 1)
+            asm("v_mul_i32_i24_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:WORD_1"
+                : "=v"(n64) : "v"(-64), "v"(w[j >> 1]));
+        else
+            asm("v_mul_i32_i24_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:WORD_0"
+                : "=v"(n64) : "v"(-64), "v"(w[j >> 1]));
+#else
+        const uint32_t n64 = 0u - (r16 << 6);
+#endif
+        const uint32_t t = x + n64 + (0u - 0x3EC00001u);
         out |= ((t >> 22) | ((f2u(y[j]) >> 28) & 8u)) << (4 * j);
     }
     return out;
