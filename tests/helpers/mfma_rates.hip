@@ -25,7 +25,7 @@ typedef int v8i_t __attribute__((ext_vector_type(8)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 
-enum { kF16 = 0, kBF16 = 1, kFP8 = 2, kFP4 = 3 };
+enum { kF16 = 0, kBF16 = 1, kFP8 = 2, kFP4 = 3, kFP4Data = 4 };
 
 template <int kKind>
 __device__ __forceinline__ v16f_t one(const v8i_t &a, const v8i_t &b, const v16f_t &c)
@@ -55,6 +55,20 @@ __global__ __launch_bounds__(256) void rate_kernel(int iters, unsigned long long
         a[i] = 0x38383838 ^ (tid * 0x01010101 + i);  // small finite codes in every format
         b[i] = 0x30303030 ^ (tid * 0x00010001 + 3 * i);
     }
+    // kFP4Data: four random operand pairs per lane (xorshift32), rotated
+    // every instruction, so that the matrix core sees changing data as in a
+    // GEMM (every 4-bit pattern is an E2M1 value)
+    v8i_t av[4], bv[4];
+    uint32_t x = 0x9E3779B9u * (uint32_t)(blockIdx.x * 256 + tid + 1);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            x ^= x << 13; x ^= x >> 17; x ^= x << 5;
+            av[j][i] = (int)x;
+            x ^= x << 13; x ^= x >> 17; x ^= x << 5;
+            bv[j][i] = (int)x;
+        }
     v16f_t acc[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) acc[k] = (v16f_t){};
@@ -62,7 +76,12 @@ __global__ __launch_bounds__(256) void rate_kernel(int iters, unsigned long long
     const unsigned long long t0 = __builtin_amdgcn_s_memtime();
     for (int it = 0; it < iters; ++it) {
 #pragma unroll
-        for (int k = 0; k < 8; ++k) acc[k] = one<kKind>(a, b, acc[k]);
+        for (int k = 0; k < 8; ++k) {
+            if constexpr (kKind == kFP4Data)
+                acc[k] = one<kFP4>(av[k & 3], bv[(k + 1) & 3], acc[k]);
+            else
+                acc[k] = one<kKind>(a, b, acc[k]);
+        }
     }
     const unsigned long long t1 = __builtin_amdgcn_s_memtime();
     float s = 0.0f;
@@ -74,7 +93,8 @@ __global__ __launch_bounds__(256) void rate_kernel(int iters, unsigned long long
     if ((tid & 63) == 0) cycles[blockIdx.x * 4 + (tid >> 6)] = t1 - t0;
 }
 
-// Launches the kernel of `kind` (0 fp16, 1 bf16, 2 fp8, 3 fp4) on `stream`;
+// Launches the kernel of `kind` (0 fp16, 1 bf16, 2 fp8, 3 fp4, 4 fp4 on
+// changing random operands) on `stream`;
 // 0 on success, 1 for an unknown kind or a launch error.
 extern "C" int mfma_rate_launch(int kind, int blocks, int iters, unsigned long long *cycles, float *sink,
                                 void *stream)
@@ -85,6 +105,9 @@ extern "C" int mfma_rate_launch(int kind, int blocks, int iters, unsigned long l
     case kBF16: hipLaunchKernelGGL(rate_kernel<kBF16>, dim3(blocks), dim3(256), 0, st, iters, cycles, sink); break;
     case kFP8: hipLaunchKernelGGL(rate_kernel<kFP8>, dim3(blocks), dim3(256), 0, st, iters, cycles, sink); break;
     case kFP4: hipLaunchKernelGGL(rate_kernel<kFP4>, dim3(blocks), dim3(256), 0, st, iters, cycles, sink); break;
+    case kFP4Data:
+        hipLaunchKernelGGL(rate_kernel<kFP4Data>, dim3(blocks), dim3(256), 0, st, iters, cycles, sink);
+        break;
     default: return 1;
     }
     return hipGetLastError() == hipSuccess ? 0 : 1;

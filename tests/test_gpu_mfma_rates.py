@@ -50,3 +50,48 @@ def test_fp8_split_does_not_beat_fp16():
           f"{step_fp8_split:.0f} ({step_fp8_split / step_fp16:.2f}x), one operand split {step_fp8_one_side:.0f}")
     assert step_fp8_split >= step_fp16, "fp8 matrix cores would win: revisit the NVFP4 GEMM"
     assert c["fp4"] <= c["fp8"]
+
+
+def test_fp4_sustained_rate_on_changing_operands():
+    # The FP4 instruction at full issue (one wave per SIMD, eight independent
+    # accumulators) on random operands that change every instruction, held
+    # for about 2.7 s: after the first second the chip runs at its sustained,
+    # power-limited clock.  The rate over the last 1.5 s is the practical
+    # ceiling a GEMM's matrix cores could reach on this chip (no memory
+    # traffic at all), next to the 10.1 PFLOP/s nominal dense peak.
+    import time
+    announce("sustained FP4 matrix-core rate")
+    lib = ctypes.CDLL(helpers.path("libmfma_rates.so"))
+    lib.mfma_rate_launch.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                     ctypes.c_void_p]
+    dev = device()
+    blocks, iters = 256, 20000
+    cyc = torch.zeros(blocks * 4, dtype=torch.int64, device=dev)
+    sink = torch.zeros(blocks * 256, dtype=torch.float32, device=dev)
+    st = torch.cuda.current_stream(dev).cuda_stream
+    launch = lambda: lib.mfma_rate_launch(4, blocks, iters, cyc.data_ptr(), sink.data_ptr(), st)
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < 1.2:
+        for _ in range(16):
+            assert launch() == 0
+        torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n = 0
+    e0.record()
+    t1 = time.perf_counter()
+    while time.perf_counter() - t1 < 1.5:
+        for _ in range(16):
+            assert launch() == 0
+        n += 16
+        e1.record()
+        e1.synchronize()
+    ms = e0.elapsed_time(e1)
+    flops = n * blocks * 4 * iters * 8 * (32 * 32 * 64 * 2)
+    cycles_per_instr = float(cyc.cpu().numpy().astype(np.float64).mean()) / (iters * 8)
+    rate = flops / (ms * 1e-3) / 1e12
+    ghz = cycles_per_instr * iters * 8 / (ms * 1e-3 / n) / 1e9  # s_memtime counts core clock cycles
+    print(f"FP4 32x32x64 on changing operands: {rate:.0f} TFLOP/s sustained over {ms / 1e3:.2f} s "
+          f"({rate / 10100:.3f} of the 10.1 PFLOP/s nominal peak), {cycles_per_instr:.1f} cycles per instruction, "
+          f"{ghz:.2f} GHz implied")
+    assert 0 < rate <= 10200 and np.isfinite(sink.cpu().numpy()).all()
+
