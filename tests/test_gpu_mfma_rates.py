@@ -9,7 +9,9 @@ per instruction of the fp16, bf16, fp8 and fp4 32x32 instructions (8
 independent accumulators per wave, one wave per SIMD on every CU, cycles by
 s_memtime) and checks the cost of one 128-wide K step of a 32x32 output
 block both ways: fp16 = 8 instructions of K 16; two-part fp8 = 4 x 2
-instructions of K 64."""
+instructions of K 64.  A second test holds the FP4 instruction on changing
+operands for a few seconds and reports the sustained rate: the practical
+ceiling of the MXFP4 GEMM on this chip."""
 import ctypes
 
 import numpy as np
