@@ -157,14 +157,16 @@ __global__ __launch_bounds__(kThreads) void quant_mx_rows_kernel(const uint16_t 
                                                                  uint32_t sign_mask)
 {
     const uint32_t cpr = K >> 3;  // 16-byte chunks per row
-    const uint32_t base = blockIdx.x * (kThreads * kChunksPerThread) + threadIdx.x;
+    // chunk indices in 64 bits for the bounds test: nchunks may lie within a
+    // workgroup's span of 2^32, where a 32-bit index would wrap below it
+    const uint64_t base = (uint64_t)blockIdx.x * (kThreads * kChunksPerThread) + threadIdx.x;
     const int quad_lane = threadIdx.x & 3;
     uint4 q[kChunksPerThread];
 #pragma unroll
     for (int i = 0; i < kChunksPerThread; ++i) {
-        const uint32_t c = base + i * kThreads;
+        const uint32_t c = (uint32_t)(base + i * kThreads);
         q[i] = make_uint4(0u, 0u, 0u, 0u);
-        if (c < nchunks) {
+        if (base + i * kThreads < nchunks) {
             size_t off;
             if (kContig) {
                 off = (size_t)c * 8;
@@ -177,7 +179,8 @@ __global__ __launch_bounds__(kThreads) void quant_mx_rows_kernel(const uint16_t 
     }
 #pragma unroll
     for (int i = 0; i < kChunksPerThread; ++i) {
-        const uint32_t c = base + i * kThreads;
+        const uint32_t c = (uint32_t)(base + i * kThreads);
+        const bool valid = base + i * kThreads < nchunks;
         uint32_t packed = 0, sbyte;
         if (!kHad && !kSR) {
             // bf16 straight into the scaled convert: no binary32 unpack
@@ -214,7 +217,7 @@ __global__ __launch_bounds__(kThreads) void quant_mx_rows_kernel(const uint16_t 
                 packed = cvt8_f32(f, mx_scale_f32(sbyte));
             }
         }
-        if (c < nchunks) {
+        if (valid) {
             __builtin_nontemporal_store(packed, codes + c);
             if (quad_lane == 0) scales[c >> 2] = (uint8_t)sbyte;
         }
@@ -652,7 +655,10 @@ __global__ __launch_bounds__(kThreads) void nv_quant_global_kernel(const uint16_
 {
     __shared__ uint32_t sh[kThreads / 64];
     const uint32_t cpr = K >> 3;
-    const uint32_t base = blockIdx.x * (kThreads * kNvgChunks) + threadIdx.x;
+    // chunk indices in 64 bits for the bounds tests: the chunk count may lie
+    // within a workgroup's span of 2^32, where a 32-bit index would wrap
+    const uint64_t base = (uint64_t)blockIdx.x * (kThreads * kNvgChunks) + threadIdx.x;
+    const uint64_t cend = kTiled ? nchunks_out : nchunks;
     // The partial maxima are loaded before the data: loads complete in issue
     // order, so the domain amax, the barriers and the decode table proceed
     // while the data is in flight, and chunk i's encode waits for its own load.
@@ -669,7 +675,8 @@ __global__ __launch_bounds__(kThreads) void nv_quant_global_kernel(const uint16_
     uint32_t rows[kNvgChunks], cols[kNvgChunks];  // (row, chunk in row) of each chunk
 #pragma unroll
     for (int i = 0; i < kNvgChunks; ++i) {
-        const uint32_t c = base + i * kThreads;
+        const uint32_t c = (uint32_t)(base + i * kThreads);
+        const bool in = base + i * kThreads < cend;
         // every load is issued (an invalid chunk reads the operand's first
         // chunk, or a zero chunk when the operand is empty, and is zeroed
         // below), so the loads' completion count is exact
@@ -679,7 +686,7 @@ __global__ __launch_bounds__(kThreads) void nv_quant_global_kernel(const uint16_
             const uint32_t blk = c >> 9, rb = fast_div(blk, by);
             rows[i] = rb * 32u + ((c >> 4) & 31u);
             cols[i] = (blk - rb * (K >> 7)) * 16u + (c & 15u);
-            valid = c < nchunks_out && (uint64_t)rows[i] * cpr < nchunks;
+            valid = in && (uint64_t)rows[i] * cpr < nchunks;
             src = x + (size_t)rows[i] * ld + (size_t)cols[i] * 8;
         } else {
             rows[i] = 0;
@@ -688,7 +695,7 @@ __global__ __launch_bounds__(kThreads) void nv_quant_global_kernel(const uint16_
                 rows[i] = fast_div(c, by);
                 cols[i] = c - rows[i] * cpr;
             }
-            valid = c < nchunks;
+            valid = in;
             src = kFlat ? x + (size_t)c * 8 : x + (size_t)rows[i] * ld + (size_t)cols[i] * 8;
         }
         const uint4 v = load_nt16(valid ? src : fallback);
@@ -708,7 +715,8 @@ __global__ __launch_bounds__(kThreads) void nv_quant_global_kernel(const uint16_
     const bool word_scales = kTiled || ((nchunks & 7u) == 0 && ((uintptr_t)scales & 3u) == 0);
 #pragma unroll
     for (int i = 0; i < kNvgChunks; ++i) {
-        const uint32_t c = base + i * kThreads;
+        const uint32_t c = (uint32_t)(base + i * kThreads);
+        const bool in = base + i * kThreads < cend;
         const uint32_t r = rows[i], col = cols[i];  // stochastic rounding keys on them
         uint32_t sb;
         uint32_t packed = nv_encode8<kSR>(q[i], dom, inv_tab, &sb, r, col, stream_id, seed_lo, seed_hi);
@@ -720,12 +728,12 @@ __global__ __launch_bounds__(kThreads) void nv_quant_global_kernel(const uint16_
         const uint32_t s4 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)sb, 0x104, 0xF, 0xF, true);
         const uint32_t s6 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)sb, 0x106, 0xF, 0xF, true);
         if (kTiled) {
-            if (c < nchunks_out) {  // tiled order: word c, scale bytes 2 c .. (nv_code_off / nv_scale_off)
+            if (in) {  // tiled order: word c, scale bytes 2 c .. (nv_code_off / nv_scale_off)
                 __builtin_nontemporal_store(packed, codes + c);
                 if ((threadIdx.x & 7) == 0)  // chunks col .. col + 7: four blocks of one row and K step
                     *reinterpret_cast<uint32_t *>(scales + (c >> 1)) = sb | s2 << 8 | s4 << 16 | s6 << 24;
             }
-        } else if (c < nchunks) {
+        } else if (in) {
             __builtin_nontemporal_store(packed, codes + c);
             if (word_scales) {
                 if ((threadIdx.x & 7) == 0)  // c % 8 == 0 and c + 7 < nchunks
