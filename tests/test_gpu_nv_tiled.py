@@ -123,3 +123,31 @@ def test_nv_tiled_full_size(domain):
     cref, w = oracle.gemm_ref(oracle.dequant_nv(*oa, domain), oracle.dequant_nv(*ob, domain))
     worst = gemm_check(c.cpu().numpy(), cref, w, f"nv tiled full d{domain}")
     print(f"nv tiled domain {domain}: worst |err| / sum|ab| = {worst:.3e}")
+
+
+_SR_ORACLE = {}
+
+
+@pytest.mark.parametrize("domain", [0, 1])
+@pytest.mark.parametrize("layout", ["linear", "tiled"])
+def test_nv_sr_rows_full_size(domain, layout):
+    # the backward workload's dY (8192 x 4096, Student-t with 3 degrees of
+    # freedom, scaled 1e-3) along rows with stochastic rounding, in both
+    # scale domains and both layouts: every code, block scale and tensor
+    # scale against the oracle (the workgroups past the first wave included)
+    dev = device()
+    announce(f"nv SR rows full backward.dY domain={domain} {layout}")
+    xt = synth.config_tensor("backward", "dY")
+    codes, scales, ts = B.fp4_quantize_nv(xt.to(dev), domain, round=B.SR, seed=7, stream_id=3,
+                                          layout=T if layout == "tiled" else B.LAYOUT_LINEAR)
+    if domain not in _SR_ORACLE:
+        _SR_ORACLE[domain] = oracle.quantize_nv(synth.bf16_bits(xt), sr=True, seed=7, stream=3, domain=domain)
+    oc, os_, ots = _SR_ORACLE[domain]
+    torch.cuda.synchronize()
+    if layout == "tiled":
+        check_tiled(codes, scales, ts, oc, os_, ots, "dY")
+    else:
+        assert np.array_equal(ts.cpu().numpy().view(np.uint32), ots.view(np.uint32)), "tensor scales"
+        assert_bytes_equal(np_u8(scales), os_, "block scales")
+        assert_bytes_equal(np_u8(codes), oc, "codes")
+
