@@ -109,6 +109,26 @@ def test_quantize_nv_one_pass_matches_oracle(rows, cols, sr):
     assert_bytes_equal(np_u8(codes), oc, "codes")
 
 
+@pytest.mark.parametrize("role", ["X", "W"])
+@pytest.mark.parametrize("sr", [False, True])
+def test_quantize_nv_one_pass_full_size(role, sr):
+    # the NVFP4 configuration's operands (8192 x 4096 and 14336 x 4096) in one
+    # pass from a host-computed amax, against the oracle's two-pass definition
+    dev = device()
+    announce(f"nv one pass full nvfp4.{role} sr={sr}")
+    xt = synth.config_tensor("nvfp4", role)
+    xb = synth.bf16_bits(xt)
+    amax_host = np.float32(np.abs(xt.float().numpy()).max())
+    amax = torch.tensor([amax_host], dtype=torch.float32, device=dev)
+    codes, scales, ts = B.fp4_quantize_nv(xt.to(dev), B.NV_GLOBAL, round=B.SR if sr else B.RNE, seed=5,
+                                          stream_id=2, amax=amax)
+    oc, os_, ots = oracle.quantize_nv(xb, sr=sr, seed=5, stream=2, domain=oracle.NV_GLOBAL)
+    torch.cuda.synchronize()
+    assert_bytes_equal(ts.cpu().numpy().view(np.uint32), ots.view(np.uint32), "tensor scale")
+    assert_bytes_equal(np_u8(scales), os_, "block scales")
+    assert_bytes_equal(np_u8(codes), oc, "codes")
+
+
 def test_quantize_nv_one_pass_zero_amax():
     # an all-zero operand: amax 0 gives S = 1, zero codes, as the two-pass producer
     dev = device()
